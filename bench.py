@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X flash-attention forward path; prints one JSON line.
+
+Headline (value): long-context GQA decode, bf16, B=1 Hq=32 Hkv=4 Sq=1
+Sk=32768 d=128 -- KV bytes read per second over whole steps (forward kernel
+plus log-sum-exp combine), with the KV cache rotated over enough copies that
+every step reads HBM rather than the 256 MB last-level cache.
+Secondary (prefill): causal prefill, bf16, B=1 H=32 S=8192 d=128 -- TFLOP/s
+over visible (query, key) pairs only.
+
+A step is one call of the library on one batch of synthetic inputs already
+resident in GPU memory. Per-kernel durations come from HIP events the library
+records around each launch (on the launch stream) in a separate pass.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+LLC_BYTES = 256 << 20       # MI355X Infinity Cache
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "tiled_prefill_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run one leg only (for profiling)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """Counter-derived HBM bytes per launch, if recorded for the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = rec.get(f"{kernel}:{workload}")
+    if not e or e.get("kernel_sha") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every workload fits one MI355X); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_prefill_amd as tpa
+    from workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tpa.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    out = {}
+
+    # ------------------------------------------------------------------ decode
+    w = WORKLOADS["gqa_decode_bf16"]
+    esz = 2
+    kv_bytes = 2 * w.B * w.Sk * w.Hkv * w.d * esz            # K and V, every row visible
+    q_bytes = w.B * w.Sq * w.Hq * w.d * esz
+    o_bytes = q_bytes + w.B * w.Hq * w.Sq * 4                 # O plus lse
+    plan = tpa.plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, dtype=w.dtype)
+    if args.only in (None, "decode"):
+        q, k, v, _ = make_inputs(w, seed=0, device=dev)
+        n_rot = max(2, math.ceil(2 * LLC_BYTES / kv_bytes))
+        ks = [k] + [k.clone() for _ in range(n_rot - 1)]
+        vs = [v] + [v.clone() for _ in range(n_rot - 1)]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+
+        def step(i):
+            tpa.fwd(q, ks[i % n_rot], vs[i % n_rot], causal=False, out=o, lse=lse)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        ms = dt * 1e3 / args.steps
+        value = kv_bytes / (dt / args.steps) / 1e9
+        # per-kernel durations (events around each launch, on the launch stream)
+        tpa.profile_begin(2 * args.steps + 8)
+        for i in range(args.steps):
+            step(i)
+        prof = tpa.profile_end()
+        fwd_ms = prof["fwd_ms"] / max(1, prof["fwd_launches"])
+        comb_ms = prof["combine_ms"] / max(1, prof["combine_launches"])
+        achieved = (kv_bytes + q_bytes) / (fwd_ms * 1e-3) / 1e9
+        traffic = traffic_for("attn_fwd_kernel", w.name)
+        out["decode"] = dict(value=value, ms_per_step=ms, fwd_ms=fwd_ms, combine_ms=comb_ms,
+                             achieved=achieved, traffic=traffic, n_rot=n_rot)
+        del ks, vs, q, k, v
+
+    # ----------------------------------------------------------------- prefill
+    wp = WORKLOADS["causal_prefill_bf16"]
+    pairs = wp.B * wp.Hq * sum(min(i + 1 + wp.Sk - wp.Sq, wp.Sk) for i in range(wp.Sq))
+    flops = 4.0 * wp.d * pairs
+    if not args.no_prefill and args.only in (None, "prefill"):
+        q, k, v, _ = make_inputs(wp, seed=0, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((wp.B, wp.Hq, wp.Sq), dtype=torch.float32, device=dev)
+
+        def pstep():
+            tpa.fwd(q, k, v, causal=True, out=o, lse=lse)
+
+        for _ in range(3):
+            pstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.prefill_steps):
+            pstep()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        pms = dt * 1e3 / args.prefill_steps
+        tpa.profile_begin(args.prefill_steps + 4)
+        for _ in range(args.prefill_steps):
+            pstep()
+        prof = tpa.profile_end()
+        pf_ms = prof["fwd_ms"] / max(1, prof["fwd_launches"])
+        out["prefill"] = dict(value=flops / (pms * 1e-3) / 1e12, ms_per_step=pms, fwd_ms=pf_ms,
+                              achieved=flops / (pf_ms * 1e-3) / 1e12)
+        del q, k, v
+
+    # ------------------------------------------------------------ cpu baseline
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        q, k, v, _ = make_inputs(w, seed=0)
+        oracle.attn_ref(q, k, v, False, -1, w.scale, n_threads=threads)  # warm (build, pages)
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.attn_ref(q, k, v, False, -1, w.scale, n_threads=threads)
+            runs += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": kv_bytes * runs / dt / 1e9, "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole decode workload (all 32 query heads, 32768 keys), "
+                         f"{runs} oracle runs in {dt:.1f} s, fp64"}
+        # prefill: 16 query rows spread over the sequence, all heads, oracle fp64
+        qp, kp, vp, _ = make_inputs(wp, seed=0)
+        rows = [int(x) for x in torch.linspace(0, wp.Sq - 1, 16).round()]
+        t0 = time.perf_counter()
+        pf = 0.0
+        for i in rows:
+            kl = i + 1
+            oracle.attn_ref(qp[:, i:i + 1], kp[:, :kl], vp[:, :kl], True, -1, wp.scale,
+                            n_threads=threads)
+            pf += 4.0 * wp.d * kl * wp.Hq
+        dtp = time.perf_counter() - t0
+        cpu["prefill"] = {"value": pf / dtp / 1e12, "unit": "TFLOP/s",
+                          "sample": f"{len(rows)} causal query rows x 32 heads, {dtp:.1f} s"}
+
+    dec = out.get("decode")
+    pre = out.get("prefill")
+    line = {
+        "metric": "decode KV GB/s (% of HBM peak); causal prefill TFLOP/s (% MFMA peak), 1 GPU",
+        "value": round(dec["value"], 2) if dec else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5) if dec else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tensors; KV rotated over copies to defeat the LLC)",
+        "config": {"workload": "gqa_decode_bf16: B=1 Hq=32 Hkv=4 Sq=1 Sk=32768 d=128, "
+                               "non-causal, split-KV + LSE combine",
+                   "num_splits": plan["num_splits"], "pack_gqa": plan["pack_gqa"],
+                   "grid": [plan["grid_x"], plan["grid_y"], plan["grid_z"]],
+                   "kv_copies": dec["n_rot"] if dec else None},
+    }
+    if dec:
+        line["pct_of_hbm_peak"] = round(100 * dec["value"] / HBM_PEAK_GBS, 2)
+        line["roofline"] = {"bound": "hbm", "kernel": "attn_fwd_kernel (decode tile)",
+                            "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+                            "traffic": dec["traffic"],
+                            "avg_launch_ms": round(dec["fwd_ms"], 5),
+                            "combine_avg_launch_ms": round(dec["combine_ms"], 5)}
+    if pre:
+        line["prefill"] = {
+            "metric": "causal prefill TFLOP/s", "value": round(pre["value"], 2),
+            "unit": "TFLOP/s", "ms_per_step": round(pre["ms_per_step"], 4),
+            "pct_of_mfma_peak": round(100 * pre["value"] / BF16_PEAK_TFLOPS, 2),
+            "config": {"workload": "causal_prefill_bf16: B=1 H=32 S=8192 d=128, causal, "
+                                   "visible pairs only", "flops_per_step": flops},
+            "roofline": {"bound": "mfma", "achieved": round(pre["achieved"], 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre["achieved"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_for("attn_fwd_kernel", wp.name),
+                         "avg_launch_ms": round(pre["fwd_ms"], 4)},
+        }
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

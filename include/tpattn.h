@@ -1,0 +1,168 @@
+/*
+ * tpattn.h -- C-ABI of the MI355X (gfx950) tiled flash-attention forward library
+ * (libtpattn.so).
+ *
+ * The library computes exact softmax attention
+ *     O = softmax(scale * Q K^T + mask) V,     lse = log sum_j exp(scale q.k_j)
+ * as a tiled flash-attention forward pass with online softmax, block skipping
+ * for causal / sliding-window masks, GQA packing and split-KV with a separate
+ * log-sum-exp combine kernel.
+ *
+ * Sources (page title, section):
+ *   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling):
+ *                §2 tile sizes, §3 block-range skipping, §4 tile scheduling,
+ *                §5 split-K and num_splits, §6 PackGQA.
+ *   [Occupancy]  "The Occupancy Awakening: Rewriting a Flash Attention Kernel for
+ *                Blackwell's 188 SMs": KV-split partials and their merge.
+ *   [llama.cpp]  llama.cpp pull request 21086 review thread: at least two blocks
+ *                per SM, then more only while each keeps a minimum KV chunk.
+ *
+ * Conventions shared by every entry point
+ *   Layouts (row-major, contiguous, device memory):
+ *     q, o   [B][Sq][Hq][d]      element type `dtype`
+ *     k, v   [B][Sk][Hkv][d]     element type `dtype`
+ *     lse    [B][Hq][Sq]         fp32, natural log; may be NULL (not written)
+ *   dtype: TPATTN_FP32 (0) or TPATTN_BF16 (1). o has q's dtype; softmax and
+ *     accumulation are fp32 in both cases; bf16 outputs are rounded to nearest
+ *     even.
+ *   Heads: query head h reads key/value head h / (Hq / Hkv).
+ *   Mask ([FA-tiling] §3.1, aligned to the bottom right, delta = Sk_b - Sq):
+ *     key j is visible to query row i iff j < Sk_b, and, if causal,
+ *     j <= i + delta, and, if window_left >= 0, j >= i + delta - window_left.
+ *     window_left = -1 means no left bound. A row with no visible key gets
+ *     o = 0 and lse = -inf.
+ *   num_splits: <= 0 picks the split count with the occupancy rule
+ *     ([llama.cpp]); 1 runs one pass with no combine; 2..256 forces that many
+ *     key splits (splits beyond the key blocks are empty and legal).
+ *   stream: a hipStream_t, or NULL for the default stream. Calls are
+ *     asynchronous on the stream and never synchronise the device, except
+ *     that growing the internal split workspace synchronises once.
+ *   Ownership: all tensors belong to the caller; the library never frees
+ *     them. Split partials go to a library-owned device workspace (one per
+ *     device, grown on demand, released at unload); calls that use it on the
+ *     same device are serialised by a lock, so the library is thread-safe.
+ *   Errors: a negative status code; nothing is launched and the message is
+ *     available from tpattn_last_error() (thread-local). Argument checks never
+ *     touch the GPU.
+ */
+#ifndef TPATTN_H
+#define TPATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPATTN_OK 0
+#define TPATTN_EINVAL (-1)       /* bad argument (null pointer, shape, range)   */
+#define TPATTN_EUNSUPPORTED (-2) /* valid but not built: d not in {64,128}, dtype */
+#define TPATTN_EHIP (-3)         /* a HIP runtime call or launch failed          */
+#define TPATTN_ENOMEM (-4)       /* the split workspace could not be allocated   */
+
+#define TPATTN_FP32 0
+#define TPATTN_BF16 1
+
+#define TPATTN_MAX_SPLITS 256
+
+/* Execution plan of one call: what the host planner chose. */
+typedef struct tpattn_plan {
+    int pack_gqa;        /* 1: the G query heads of a KV head share a tile ([FA-tiling] §6) */
+    int block_m;         /* query rows per tile (packed rows when pack_gqa)                 */
+    int block_n;         /* key rows per tile                                              */
+    int waves_m;         /* waves along query rows                                          */
+    int waves_n;         /* waves along keys inside a tile                                  */
+    int num_m_blocks;    /* query blocks per (batch, grid head)                             */
+    int grid_heads;      /* Hkv when packed, Hq otherwise                                   */
+    int num_splits;      /* key splits; 1 = no combine kernel                               */
+    int chunk_blocks;    /* > 0: variable-length per-sequence split chunk, in key blocks    */
+    int grid_x, grid_y, grid_z;  /* forward-kernel grid                                    */
+    int threads;         /* threads per workgroup                                           */
+    int lds_bytes;       /* LDS per workgroup                                               */
+    int num_cus;         /* compute units the split rule assumed                            */
+    int lpt;             /* 1: query blocks launched heaviest first ([FA-tiling] §4.4)      */
+    long long visited_blocks;  /* key blocks all tiles visit (fixed-length problems)        */
+    size_t workspace_bytes;    /* split partials needed (0 when num_splits == 1)           */
+} tpattn_plan;
+
+/* Forward attention ([FA-tiling] §1-§6; [Occupancy] for the split path).
+ * q, k, v, o: device pointers in the layouts above; lse: device fp32 or NULL.
+ * B >= 0, Sq >= 0, Sk >= 0 (zero sizes are a no-op or give masked rows),
+ * Hq, Hkv >= 1 with Hq % Hkv == 0, d in {64, 128}, scale finite and > 0,
+ * window_left >= -1, num_splits <= 256. */
+int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Sq, int Sk, int d,
+               int causal, int window_left, float scale, int num_splits,
+               int dtype, void* stream);
+
+/* Variable key lengths ([FA-tiling] §5.3: the split count may differ per
+ * sequence). k and v are padded to [B][Sk][Hkv][d]; sequence b uses its first
+ * seqlens_k[b] rows (device int32[B], each clamped to [0, Sk]). The split
+ * count of each sequence is ceil(its key blocks / chunk); the chunk follows the
+ * occupancy rule from sum_seqlens_k (host: the sum of seqlens_k, or <= 0 if
+ * unknown, then B * Sk is assumed). num_splits > 0 forces the maximum split
+ * count instead. Other arguments as tpattn_fwd. */
+int tpattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                      int causal, int window_left, float scale, int num_splits,
+                      int dtype, const int* seqlens_k, long long sum_seqlens_k,
+                      void* stream);
+
+/* The plan tpattn_fwd / tpattn_fwd_varlen would use (varlen != 0 selects the
+ * latter). num_cus <= 0 reads the current device (256 when no device is
+ * present). Pure host code: never touches the GPU beyond that query. */
+int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
+                    tpattn_plan* out);
+
+/* Split workspace bytes for B*Sq*Hq rows of head dim d and num_splits splits
+ * (fp32 partial outputs plus fp32 partial lse). */
+size_t tpattn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits);
+
+/* Log-sum-exp combine of split partials ([FA-tiling] §5.1; [Occupancy]):
+ *   lse[r] = log sum_s exp(lse_part[s][r]),  o[r] = sum_s exp(lse_part[s][r] - lse[r]) o_part[s][r]
+ * over rows r = (b, i, h) in o's order (B*Sq*Hq rows). o_part [S][rows][d] fp32,
+ * lse_part [S][rows] fp32 (-inf marks an empty split, whose o_part is not
+ * read), o in `dtype`, lse [B][Hq][Sq] fp32 or NULL. 1 <= num_splits <= 256. */
+int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                       int B, int Sq, int Hq, int d, int num_splits, int dtype, void* stream);
+
+/* Host mirrors of the planner's integer rules, for tests and tooling. */
+/* Key-block range of query block m_block, then of split `split` of
+ * `num_splits` ([FA-tiling] §3.2, §5.3); pack folds G heads into rows. */
+int tpattn_n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
+                         int block_m, int block_n, int m_block, int split, int num_splits,
+                         int* n_min, int* n_max);
+/* [FA-tiling] §6.2: pack iff varlen, or row efficiency without packing is
+ * below 0.9 of the efficiency with packing. Returns 0 or 1. */
+int tpattn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int block_m);
+/* [FA-tiling] §5.2 split heuristic (kept as an ablation of the default rule):
+ * 1 split if tiles >= 0.8 * SMs (or ceil(KV/L2) splits for a long non-causal
+ * KV), 1 if there are at most 4 key blocks, else the smallest split count
+ * whose wave efficiency reaches 0.85 of the best. */
+int tpattn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
+                          long long size_one_kv_head, int is_causal_or_local, int max_splits);
+/* Default split rule, a reading of [llama.cpp] for 256 CUs: 1 split when
+ * tiles >= wg_per_cu * num_cus or there are fewer than 2 key blocks; else
+ * max(s_occ, s_chunk) with s_occ = min(ceil(wg_per_cu * num_cus / tiles),
+ * n_blocks) (reach wg_per_cu workgroups per CU) and s_chunk = n_blocks /
+ * ceil(min_chunk_rows / block_n) (more splits only while each keeps
+ * min_chunk_rows keys), at most 256. */
+int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
+                                int min_chunk_rows, int wg_per_cu);
+
+/* Kernel timing for measurement tools: while enabled, every launch of the
+ * forward and combine kernels is bracketed by HIP events on its stream.
+ * tpattn_profile_end synchronises those events and returns the summed
+ * durations (ms) and launch counts, then disables recording. */
+int tpattn_profile_begin(int max_launches);
+int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
+                       int* combine_launches);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* tpattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

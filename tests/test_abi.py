@@ -1,0 +1,94 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol its
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import re
+
+import pytest
+
+import tiled_prefill_amd as tpa
+
+FAKE = 0x1000  # never dereferenced: every call below fails argument checks first
+
+
+def declared_functions():
+    text = open(tpa.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("tpattn_fwd", "tpattn_fwd_varlen", "tpattn_plan_fwd",
+                     "tpattn_workspace_bytes", "tpattn_lse_combine", "tpattn_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tpa.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert missing == []
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=64,
+             causal=0, wl=-1, scale=0.125, splits=0, dtype=tpa.BF16)
+    a.update(kw)
+    lib = tpa.load()
+    return lib.tpattn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Sk"], a["d"], a["causal"], a["wl"], a["scale"],
+                          a["splits"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(o=None), -1),
+    (dict(Hq=6, Hkv=4), -1),
+    (dict(Hkv=0), -1),
+    (dict(d=96), -2),
+    (dict(d=256), -2),
+    (dict(dtype=7), -2),
+    (dict(wl=-2), -1),
+    (dict(scale=0.0), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(splits=257), -1),
+    (dict(Sq=-1), -1),
+    (dict(B=70000), -1),
+])
+def test_bad_arguments_are_rejected_without_launch(kw, code):
+    assert _fwd(**kw) == code
+    assert tpa.load().tpattn_last_error().decode() != ""
+
+
+def test_varlen_requires_seqlens():
+    lib = tpa.load()
+    rc = lib.tpattn_fwd_varlen(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 4, 1, 64, 64, 0, -1, 0.1, 0,
+                               tpa.BF16, None, -1, None)
+    assert rc == -1
+
+
+def test_combine_rejects_bad_split_counts():
+    lib = tpa.load()
+    assert lib.tpattn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 128, 0, 1, None) == -1
+    assert lib.tpattn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 128, 300, 1, None) == -1
+    assert lib.tpattn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 80, 4, 1, None) == -2
+    assert lib.tpattn_lse_combine(None, FAKE, FAKE, None, 1, 1, 4, 128, 4, 1, None) == -1
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(tpa.TpAttnError):
+        tpa.plan(1, 3, 2, 4, 4, 64, num_cus=256)
+    with pytest.raises(tpa.TpAttnError):
+        tpa.plan(1, 4, 4, 4, 4, 80, num_cus=256)
+
+
+def test_workspace_bytes():
+    assert tpa.workspace_bytes(1, 32, 1, 128, 1) == 0
+    assert tpa.workspace_bytes(1, 32, 1, 128, 128) == 128 * 32 * 129 * 4
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        tpa.fwd(q, q, q)

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Tolerances (from the stated accuracy targets and the arithmetic):
+  fp32 inputs: max |o - ref| <= 1e-5.
+  bf16 inputs (fp32 accumulation): max |o - ref| <= 2e-2, and
+      max |o - ref| / |ref| <= 1e-2 where |ref| > 0.1.
+  lse (fp32 on both paths, exact bf16 inputs): |lse - ref| <= 2e-5 * max(1, |ref|);
+      -inf exactly where the row sees no key (and then o == 0 exactly).
+Small cases are compared element by element; full-size workloads run in the
+launch configuration the benchmark times and are compared on sampled query
+rows, each recomputed by the oracle on its own.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_prefill_amd as tpa
+from workloads import WORKLOADS, make_inputs, random_partials, small_case
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def assert_parity(o, lse, ro, rl, dtype, what=""):
+    o = o.detach().float().cpu().double().numpy()
+    err = np.abs(o - ro)
+    if dtype == "fp32":
+        assert err.max(initial=0.0) <= 1e-5, f"{what}: max abs {err.max()}"
+    else:
+        assert err.max(initial=0.0) <= 2e-2, f"{what}: max abs {err.max()}"
+        big = np.abs(ro) > 0.1
+        if big.any():
+            rel = (err[big] / np.abs(ro[big])).max()
+            assert rel <= 1e-2, f"{what}: max rel {rel}"
+    if lse is not None:
+        lse = lse.detach().cpu().double().numpy()
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(lse), fin), f"{what}: masked-row pattern differs"
+        assert np.all(lse[~fin] == -np.inf)
+        if fin.any():
+            d = np.abs(lse[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))
+            assert d.max() <= 2e-5, f"{what}: lse err {d.max()}"
+
+
+def run_case(dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl, S, seed=0, std=1.0):
+    q, k, v = small_case(seed, dtype, B, Hq, Hkv, Sq, Sk, d, std=std)
+    scale = 1.0 / math.sqrt(d)
+    print(f"case {dtype} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} d={d} causal={causal} "
+          f"wl={wl} S={S} seed={seed}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window_left=wl,
+                     scale=scale, num_splits=S)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_ref(q, k, v, causal, wl, scale)
+    assert_parity(o, lse, ro, rl, dtype, f"{dtype} {B},{Hq},{Hkv},{Sq},{Sk},{d} c={causal} wl={wl} S={S}")
+    return o, lse
+
+
+@pytest.mark.parametrize("S", [0, 1, 2, 3, 4, 5, 6, 7, 8])
+def test_decode_fp32_split_sweep(S):
+    # tiny fp32 decode, every split count 1..8 (4 key blocks: 5..8 leave empty splits)
+    w = WORKLOADS["decode_fp32"]
+    q, k, v, _ = make_inputs(w, seed=0)
+    print(f"decode_fp32 S={S}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=False, num_splits=S)
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, w.scale)
+    assert_parity(o, lse, ro, rl, "fp32", f"decode_fp32 S={S}")
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_spec_verify_fp32_full(S):
+    w = WORKLOADS["spec_verify_fp32"]
+    q, k, v, _ = make_inputs(w, seed=1)
+    print(f"spec_verify_fp32 S={S}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, num_splits=S)
+    ro, rl = oracle.attn_ref(q, k, v, True, -1, w.scale)
+    assert_parity(o, lse, ro, rl, "fp32", f"spec_verify S={S}")
+
+
+@pytest.mark.parametrize("B,H,q_len,kv_len", [(2, 16, 17, 2065), (1, 64, 33, 161),
+                                              (2, 64, 9, 521), (2, 8, 9, 9)])
+def test_verify_page_shapes_fp32(B, H, q_len, kv_len):
+    # shapes of the verify-attention parity run on the occupancy blog page
+    run_case("fp32", B, H, H, q_len, kv_len, 128, True, -1, 0, seed=2)
+
+
+SMALL = [
+    # dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl, S
+    ("bf16", 2, 4, 4, 200, 200, 128, True, -1, 1),
+    ("bf16", 1, 8, 2, 130, 300, 128, True, 50, 1),
+    ("bf16", 1, 8, 2, 130, 300, 64, False, -1, 3),
+    ("bf16", 2, 16, 2, 3, 500, 128, True, -1, 0),
+    ("bf16", 1, 32, 4, 1, 1000, 128, False, -1, 0),
+    ("bf16", 1, 32, 4, 1, 1000, 64, False, -1, 7),
+    ("bf16", 1, 4, 4, 300, 100, 128, True, -1, 1),
+    ("bf16", 1, 4, 1, 5, 77, 128, True, 2, 2),
+    ("bf16", 3, 6, 3, 40, 40, 64, True, 0, 1),
+    ("bf16", 1, 2, 2, 1, 1, 128, False, -1, 1),
+    ("bf16", 2, 8, 8, 64, 64, 128, False, 10, 1),
+    ("bf16", 1, 16, 16, 257, 1025, 128, True, 300, 4),
+    ("bf16", 2, 4, 2, 16, 700, 128, True, -1, 0),
+    ("fp32", 1, 4, 2, 33, 70, 64, True, 5, 0),
+    ("fp32", 2, 2, 2, 20, 150, 128, False, -1, 4),
+    ("fp32", 1, 8, 1, 2, 333, 128, False, -1, 0),
+    ("fp32", 1, 4, 4, 90, 60, 64, True, -1, 1),
+    ("fp32", 1, 2, 2, 130, 130, 128, True, 17, 2),
+]
+
+
+@pytest.mark.parametrize("case", SMALL)
+def test_small_shapes(case):
+    run_case(*case, seed=3)
+
+
+def test_empty_keys_give_masked_rows():
+    for dtype in ("fp32", "bf16"):
+        q, k, v = small_case(4, dtype, 1, 4, 2, 3, 0, 64)
+        o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+        torch.cuda.synchronize()
+        assert torch.all(o.float().cpu() == 0)
+        assert torch.all(lse.cpu() == float("-inf"))
+
+
+def test_empty_query_is_noop():
+    q, k, v = small_case(5, "bf16", 1, 4, 4, 0, 16, 64)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+
+
+def test_lse_not_requested():
+    q, k, v = small_case(6, "bf16", 1, 8, 2, 70, 90, 128)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, return_lse=False)
+    assert lse is None
+    ro, _ = oracle.attn_ref(q, k, v, True, -1, 1 / math.sqrt(128))
+    assert_parity(o, None, ro, None, "bf16", "no lse")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_split_invariance(dtype):
+    q, k, v = small_case(7, dtype, 1, 8, 2, 4, 1500, 128)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, 1 / math.sqrt(128))
+    outs = []
+    for S in (1, 2, 3, 7, 16, 64, 256):
+        o, lse = tpa.fwd(qd, kd, vd, num_splits=S)
+        assert_parity(o, lse, ro, rl, dtype, f"S={S}")
+        outs.append(o.float().cpu())
+    tol = 1e-5 if dtype == "fp32" else 2e-2
+    for x in outs[1:]:
+        assert (x - outs[0]).abs().max().item() <= tol
+
+
+def test_deterministic():
+    q, k, v = small_case(8, "bf16", 2, 8, 4, 100, 300, 128)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for S in (1, 5):
+        o1, l1 = tpa.fwd(qd, kd, vd, causal=True, num_splits=S)
+        o2, l2 = tpa.fwd(qd, kd, vd, causal=True, num_splits=S)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_non_default_stream():
+    q, k, v = small_case(9, "bf16", 1, 32, 4, 1, 2048, 128)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        o, lse = tpa.fwd(qd, kd, vd, stream=s)
+    s.synchronize()
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, 1 / math.sqrt(128))
+    assert_parity(o, lse, ro, rl, "bf16", "stream")
+
+
+@pytest.mark.parametrize("S,d,dtype", [(1, 128, "fp32"), (2, 64, "bf16"), (5, 128, "bf16"),
+                                       (64, 128, "fp32"), (256, 64, "fp32"), (128, 128, "bf16")])
+def test_combine_kernel_parity(S, d, dtype):
+    B, Sq, Hq = 2, 3, 5
+    rows = B * Sq * Hq
+    o_part, lse_part = random_partials(10 + S, S, rows, d, p_empty=0.3)
+    lse_part[:, 0] = float("-inf")  # a row with every split empty
+    o_part[:, 0] = 0
+    out = torch.empty((B, Sq, Hq, d), dtype=torch.float32 if dtype == "fp32" else torch.bfloat16,
+                      device=DEV)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
+    tpa.lse_combine(o_part.to(DEV), lse_part.to(DEV), out, lse, B, Sq, Hq)
+    ro, rl = oracle.lse_combine_ref(o_part, lse_part)
+    ro = ro.reshape(B, Sq, Hq, d)
+    rl = rl.reshape(B, Sq, Hq).transpose(0, 2, 1)
+    got = out.float().cpu().double().numpy()
+    tol = 1e-5 if dtype == "fp32" else 2e-2
+    assert np.abs(got - ro).max() <= tol * max(1.0, np.abs(ro).max())
+    lg = lse.cpu().double().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert np.abs(lg[fin] - rl[fin]).max() <= 2e-5 * max(1.0, np.abs(rl[fin]).max())
+
+
+def test_varlen_small():
+    B, Hq, Hkv, Sk, d = 5, 8, 2, 700, 128
+    q, k, v = small_case(11, "bf16", B, Hq, Hkv, 1, Sk, d)
+    seqlens = torch.tensor([700, 1, 0, 257, 513], dtype=torch.int32)
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, 1 / math.sqrt(d), seqlens_k=seqlens)
+    for S in (0, 1, 3):
+        o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV), num_splits=S,
+                                sum_seqlens_k=int(seqlens.sum()))
+        assert_parity(o, lse, ro, rl, "bf16", f"varlen S={S}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+def _sampled_rows_check(w, q, k, v, o, lse, rows):
+    """Recompute chosen query rows one by one with the oracle and compare."""
+    delta = w.Sk - w.Sq
+    for i in rows:
+        if w.causal:
+            kl = i + delta + 1  # keys the row can see, so the row aligns at the bottom right
+            ro, rl = oracle.attn_ref(q[:, i:i + 1], k[:, :kl], v[:, :kl], True, w.window_left, w.scale)
+        else:
+            ro, rl = oracle.attn_ref(q[:, i:i + 1], k, v, False, w.window_left, w.scale)
+        assert_parity(o[:, i:i + 1], lse[:, :, i:i + 1], ro, rl, w.dtype, f"{w.name} row {i}")
+
+
+def _full_props(o, v):
+    of = o.float()
+    assert torch.isfinite(of).all()
+    assert of.abs().max().item() <= v.float().abs().max().item() + 1e-3
+
+
+def test_gqa_decode_full():
+    w = WORKLOADS["gqa_decode_bf16"]
+    q, k, v, _ = make_inputs(w, seed=0)
+    print("gqa_decode_bf16 full", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV))
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, w.scale)
+    assert_parity(o, lse, ro, rl, "bf16", "gqa_decode full")
+
+
+def test_varlen_decode_full():
+    w = WORKLOADS["varlen_decode_bf16"]
+    q, k, v, seqlens = make_inputs(w, seed=0)
+    print("varlen_decode_bf16 full", flush=True)
+    o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV),
+                            sum_seqlens_k=int(seqlens.sum()))
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, w.scale, seqlens_k=seqlens)
+    assert_parity(o, lse, ro, rl, "bf16", "varlen_decode full")
+
+
+@pytest.mark.parametrize("name", ["causal_prefill_bf16", "window_prefill_bf16"])
+def test_prefill_full_sampled(name):
+    w = WORKLOADS[name]
+    q, k, v, _ = make_inputs(w, seed=0)
+    print(f"{name} full", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, window_left=w.window_left)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    _full_props(o, v)
+    S = w.Sq
+    rows = sorted({0, 1, 15, 16, 63, 64, 127, 128, 129, 1000, 1023, 1024, 1025, 2047, 2048,
+                   S // 2 + 7, S - 129, S - 128, S - 65, S - 2, S - 1})
+    _sampled_rows_check(w, q, k, v, o, lse, rows)

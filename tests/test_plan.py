@@ -1,0 +1,140 @@
+"""Host planner: block ranges, split partition, PackGQA and split-count rules.
+
+Checked against the oracle's brute-force visible key blocks and against the
+worked examples printed on the tiling-strategy page (tests/golden/).
+"""
+import json
+import os
+
+import pytest
+
+import oracle
+import tiled_prefill_amd as tpa
+from workloads import WORKLOADS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ranges(Sq, Skb, G, pack, causal, wl, BM, BN):
+    rows = Sq * (G if pack else 1)
+    return [tpa.n_block_range(Sq, Skb, G, pack, causal, wl, BM, BN, m)
+            for m in range((rows + BM - 1) // BM)]
+
+
+def test_printed_causal_block_count():
+    # "分块策略与调度" §3.3: N = 4096, B_r = B_c = 128 -> 528 of 1024 blocks.
+    g = json.load(open(os.path.join(GOLDEN, "causal_block_count.json")))
+    rng = _ranges(g["N"], g["N"], 1, False, True, -1, g["block_m"], g["block_n"])
+    assert sum(hi - lo for lo, hi in rng) == g["blocks_computed"]
+    assert len(rng) * len(rng) == g["blocks_total"]
+
+
+def test_printed_split_heuristic_example():
+    # "分块策略与调度" §5.2: 108 SMs, 48 tiles -> 2 splits (efficiencies 44%, 89%, 67%).
+    g = json.load(open(os.path.join(GOLDEN, "split_heuristic_example.json")))
+    s = tpa.num_splits_fa3(g["total_mblocks"], g["num_sms"], 64, 1, 1 << 20, False, 128)
+    assert s == g["chosen_splits"]
+    for k, pct in g["efficiency_percent"].items():
+        w = g["total_mblocks"] * int(k) / g["num_sms"]
+        assert round(100 * w / -(-w // 1)) == pct
+
+
+def test_printed_pack_gqa_example():
+    # "分块策略与调度" §6.2: Sq = 100, kBlockM = 128, G = 8 -> pack (78.1% < 0.9 x 89.3%).
+    g = json.load(open(os.path.join(GOLDEN, "pack_gqa_example.json")))
+    assert tpa.should_pack_gqa(False, g["seqlen_q"], g["qhead_per_khead"], g["block_m"]) == g["pack"]
+    assert round(100 * 100 / 128, 1) == g["nopack_efficiency_percent"]
+    assert round(100 * 800 / 896, 1) == g["pack_efficiency_percent"]
+    assert tpa.should_pack_gqa(True, 4096, 8, 128)      # varlen always packs
+    assert not tpa.should_pack_gqa(False, 4096, 8, 128)  # full tiles either way
+
+
+def test_fa3_rule_branches():
+    assert tpa.num_splits_fa3(200, 108, 64, 200, 1 << 20, False, 128) == 1  # grid already full
+    assert tpa.num_splits_fa3(10, 108, 4, 1, 1 << 20, False, 128) == 1     # too few key blocks
+    # long non-causal KV beyond the L2 budget splits by ceil(KV / 50 MB)
+    assert tpa.num_splits_fa3(500, 108, 64, 500, 120 << 20, False, 128) == 3
+    assert tpa.num_splits_fa3(500, 108, 64, 500, 120 << 20, True, 128) == 1
+
+
+CASES = [(Sq, Skb, G, pack, causal, wl, BM, BN)
+         for Sq, Skb in [(1, 1), (1, 37), (5, 5), (9, 40), (33, 17), (64, 64), (70, 200), (3, 130)]
+         for G, pack in [(1, False), (4, False), (4, True)]
+         for causal, wl in [(False, -1), (True, -1), (True, 0), (True, 7), (False, 5), (True, 64)]
+         for BM, BN in [(16, 16), (32, 64), (128, 64), (16, 128)]]
+
+
+@pytest.mark.parametrize("case", CASES[::3] + CASES[1::7])
+def test_block_ranges_cover_every_visible_pair(case):
+    Sq, Skb, G, pack, causal, wl, BM, BN = case
+    need = oracle.needed_block_range(Sq, Skb, causal, wl, BM, BN, G=G, pack=pack)
+    got = _ranges(Sq, Skb, G, pack, causal, wl, BM, BN)
+    assert len(got) == len(need)
+    vis = oracle.visible_mask(Sq, Skb, causal, wl)
+    for m, ((lo, hi), nd) in enumerate(zip(got, need)):
+        if nd is None:
+            continue
+        assert lo <= nd[0] and nd[1] <= hi, (m, (lo, hi), nd)
+        # tight whenever the block's first row sees a key
+        first_pos = (m * BM) // (G if pack else 1)
+        if vis[first_pos].any():
+            assert (lo, hi) == nd
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8, 64])
+def test_splits_partition_the_block_range(S):
+    for Sq, Skb, causal, wl in [(1, 300, False, -1), (17, 2065, True, -1), (200, 200, True, 30)]:
+        for m in range((Sq + 15) // 16):
+            lo, hi = tpa.n_block_range(Sq, Skb, 1, False, causal, wl, 16, 32, m)
+            covered = []
+            prev_end = lo
+            for s in range(S):
+                a, b = tpa.n_block_range(Sq, Skb, 1, False, causal, wl, 16, 32, m, s, S)
+                if b <= a:  # empty split: only trailing ones may be empty
+                    for s2 in range(s, S):
+                        a2, b2 = tpa.n_block_range(Sq, Skb, 1, False, causal, wl, 16, 32, m, s2, S)
+                        assert b2 <= a2
+                    break
+                assert a == prev_end
+                covered.extend(range(a, b))
+                prev_end = b
+            assert covered == list(range(lo, max(lo, hi)))
+
+
+def test_occupancy_rule():
+    # reach 2 workgroups per CU, then split further only while chunks keep 256 keys
+    assert tpa.num_splits_occupancy(4, 256, 256, 128) == 128     # 32K keys, 4 tiles
+    assert tpa.num_splits_occupancy(32, 256, 65, 32) == 16       # below the chunk, for occupancy
+    assert tpa.num_splits_occupancy(2048, 256, 128, 64) == 1     # grid already full
+    assert tpa.num_splits_occupancy(4, 256, 1, 64) == 1          # one key block
+    assert tpa.num_splits_occupancy(1, 256, 4096, 64) == 256     # capped at 256 splits
+    assert tpa.num_splits_occupancy(4, 256, 4, 64) == 4          # never more splits than blocks
+
+
+def _plan(name, **kw):
+    w = WORKLOADS[name]
+    return tpa.plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left,
+                    dtype=w.dtype, varlen=w.varlen, num_cus=256, **kw)
+
+
+def test_workload_plans():
+    p = _plan("gqa_decode_bf16")
+    assert p["pack_gqa"] == 1 and p["grid_heads"] == 4 and p["num_m_blocks"] == 1
+    assert p["num_splits"] == 128 and p["grid_y"] == 512  # 2 workgroups per CU, 256-key chunks
+    p = _plan("causal_prefill_bf16")
+    assert p["num_splits"] == 1 and p["pack_gqa"] == 0 and p["lpt"] == 1
+    assert p["grid_x"] * p["grid_y"] * p["grid_z"] >= 2 * 256
+    p = _plan("window_prefill_bf16")
+    assert p["num_splits"] == 1
+    p = _plan("spec_verify_fp32")
+    assert p["num_splits"] > 1 and p["grid_x"] * p["grid_y"] * p["grid_z"] >= 2 * 256
+    p = _plan("varlen_decode_bf16", sum_seqlens_k=16 * 8448)
+    assert p["pack_gqa"] == 1 and p["chunk_blocks"] * p["block_n"] >= 256
+    p = _plan("decode_fp32", num_splits=8)
+    assert p["num_splits"] == 8
+
+
+def test_causal_visited_blocks_about_half():
+    p = _plan("causal_prefill_bf16", num_splits=1)
+    dense = p["num_m_blocks"] * (8192 // p["block_n"]) * 32
+    assert 0.5 < p["visited_blocks"] / dense < 0.52

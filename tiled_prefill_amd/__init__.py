@@ -1,0 +1,245 @@
+"""Python binding of libtpattn.so, the MI355X tiled flash-attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C-ABI declared in include/tpattn.h. PyTorch provides
+device memory and the current stream. There is no fallback path: if the
+library is not built, or a tensor is not on a GPU, the call raises.
+
+Layouts: q, o [B, Sq, Hq, d]; k, v [B, Sk, Hkv, d]; lse [B, Hq, Sq] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtpattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "tpattn.h")
+
+FP32, BF16 = 0, 1
+MAX_SPLITS = 256
+ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EHIP", -4: "ENOMEM"}
+
+
+class TpAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"tpattn error {code} ({ERRORS.get(code, '?')}): {msg}")
+        self.code = code
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("pack_gqa", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+        ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int), ("num_m_blocks", ctypes.c_int),
+        ("grid_heads", ctypes.c_int), ("num_splits", ctypes.c_int), ("chunk_blocks", ctypes.c_int),
+        ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int), ("grid_z", ctypes.c_int),
+        ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("num_cus", ctypes.c_int),
+        ("lpt", ctypes.c_int), ("visited_blocks", ctypes.c_longlong),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def load():
+    """Load libtpattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run tiled_prefill_amd/_build.py "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    ll = ctypes.c_longlong
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.tpattn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.tpattn_fwd.restype = i
+    lib.tpattn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp, ll, vp]
+    lib.tpattn_fwd_varlen.restype = i
+    lib.tpattn_plan_fwd.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ll, i, ctypes.POINTER(Plan)]
+    lib.tpattn_plan_fwd.restype = i
+    lib.tpattn_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.tpattn_workspace_bytes.restype = ctypes.c_size_t
+    lib.tpattn_lse_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.tpattn_lse_combine.restype = i
+    lib.tpattn_n_block_range.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ip, ip]
+    lib.tpattn_n_block_range.restype = i
+    lib.tpattn_should_pack_gqa.argtypes = [i, i, i, i]
+    lib.tpattn_should_pack_gqa.restype = i
+    lib.tpattn_num_splits_fa3.argtypes = [i, i, i, i, ll, i, i]
+    lib.tpattn_num_splits_fa3.restype = i
+    lib.tpattn_num_splits_occupancy.argtypes = [i, i, i, i, i, i]
+    lib.tpattn_num_splits_occupancy.restype = i
+    lib.tpattn_profile_begin.argtypes = [i]
+    lib.tpattn_profile_begin.restype = i
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.tpattn_profile_end.argtypes = [dp, ip, dp, ip]
+    lib.tpattn_profile_end.restype = i
+    lib.tpattn_last_error.argtypes = []
+    lib.tpattn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise TpAttnError(rc, load().tpattn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (fp32 or bf16)")
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _check_tensors(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("batch and head dim of q and k must match")
+
+
+def fwd(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
+        num_splits: int = 0, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
+    """Attention forward on the GPU. Returns (o, lse) (lse None if not requested)."""
+    _check_tensors(q, k, v)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    rc = load().tpattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr() if lse is not None else None,
+                           B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+                           float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
+    _check(rc)
+    return out, lse
+
+
+def fwd_varlen(q, k, v, seqlens_k: torch.Tensor, causal: bool = False, window_left: int = -1,
+               scale: Optional[float] = None, num_splits: int = 0, sum_seqlens_k: int = -1,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               return_lse: bool = True, stream=None):
+    """Attention forward with per-sequence key lengths (device int32 seqlens_k [B])."""
+    _check_tensors(q, k, v)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if not (seqlens_k.is_cuda and seqlens_k.dtype == torch.int32 and seqlens_k.shape == (B,)
+            and seqlens_k.is_contiguous()):
+        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor of shape [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    rc = load().tpattn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None,
+                                  B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+                                  float(scale), int(num_splits), _dtype_code(q),
+                                  seqlens_k.data_ptr(), int(sum_seqlens_k), _stream_ptr(stream))
+    _check(rc)
+    return out, lse
+
+
+def lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
+                lse: Optional[torch.Tensor], B: int, Sq: int, Hq: int, stream=None):
+    """Merge split partials o_part [S, B*Sq*Hq, d] fp32, lse_part [S, B*Sq*Hq] into out/lse."""
+    S, rows, d = o_part.shape
+    if rows != B * Sq * Hq or lse_part.shape != (S, rows):
+        raise ValueError("partial shapes do not match B*Sq*Hq rows")
+    for t in (o_part, lse_part, out):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("tensors must be contiguous GPU tensors")
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("partials must be fp32")
+    rc = load().tpattn_lse_combine(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None,
+                                   B, Sq, Hq, d, S, _dtype_code(out), _stream_ptr(stream))
+    _check(rc)
+    return out, lse
+
+
+def plan(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, num_splits=0, dtype="bf16",
+         varlen=False, sum_seqlens_k=-1, num_cus=0) -> dict:
+    """The planner's choices for a problem (host only)."""
+    p = Plan()
+    code = FP32 if dtype in ("fp32", FP32, torch.float32) else BF16
+    rc = load().tpattn_plan_fwd(B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+                                int(num_splits), code, int(bool(varlen)), int(sum_seqlens_k),
+                                int(num_cus), ctypes.byref(p))
+    _check(rc)
+    return p.as_dict()
+
+
+def workspace_bytes(B, Hq, Sq, d, num_splits) -> int:
+    return int(load().tpattn_workspace_bytes(B, Hq, Sq, d, num_splits))
+
+
+def n_block_range(Sq, Skb, G, pack, causal, window_left, block_m, block_n, m_block,
+                  split=0, num_splits=1):
+    lo, hi = ctypes.c_int(), ctypes.c_int()
+    rc = load().tpattn_n_block_range(Sq, Skb, G, int(bool(pack)), int(bool(causal)),
+                                     window_left, block_m, block_n, m_block, split, num_splits,
+                                     ctypes.byref(lo), ctypes.byref(hi))
+    _check(rc)
+    return lo.value, hi.value
+
+
+def should_pack_gqa(varlen, seqlen_q, qhead_per_khead, block_m) -> bool:
+    return bool(load().tpattn_should_pack_gqa(int(bool(varlen)), seqlen_q, qhead_per_khead, block_m))
+
+
+def num_splits_fa3(total_mblocks, num_sms, num_n_blocks, num_m_blocks, size_one_kv_head,
+                   is_causal_or_local, max_splits) -> int:
+    return int(load().tpattn_num_splits_fa3(total_mblocks, num_sms, num_n_blocks, num_m_blocks,
+                                            size_one_kv_head, int(bool(is_causal_or_local)),
+                                            max_splits))
+
+
+def num_splits_occupancy(tiles, num_cus, n_blocks, block_n, min_chunk_rows=256, wg_per_cu=2):
+    return int(load().tpattn_num_splits_occupancy(tiles, num_cus, n_blocks, block_n,
+                                                  min_chunk_rows, wg_per_cu))
+
+
+def profile_begin(max_launches: int = 4096):
+    _check(load().tpattn_profile_begin(int(max_launches)))
+
+
+def profile_end() -> dict:
+    f_ms, c_ms = ctypes.c_double(), ctypes.c_double()
+    f_n, c_n = ctypes.c_int(), ctypes.c_int()
+    _check(load().tpattn_profile_end(ctypes.byref(f_ms), ctypes.byref(f_n), ctypes.byref(c_ms),
+                                     ctypes.byref(c_n)))
+    return {"fwd_ms": f_ms.value, "fwd_launches": f_n.value,
+            "combine_ms": c_ms.value, "combine_launches": c_n.value}

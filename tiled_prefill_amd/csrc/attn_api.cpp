@@ -1,0 +1,508 @@
+// attn_api.cpp -- the C-ABI of libtpattn.so: argument checks, the host planner
+// (tile choice, GQA packing, split count, grid), the split workspace, and the
+// launches of the forward and combine kernels.
+//
+// Citations:
+//   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
+//   [Occupancy]  "The Occupancy Awakening: Rewriting a Flash Attention Kernel for
+//                Blackwell's 188 SMs"
+//   [llama.cpp]  llama.cpp pull request 21086 review thread
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/tpattn.h"
+#include "attn_kernels.h"
+#include "attn_plan.h"
+
+using namespace tpa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+// ---------------------------------------------------------------------------
+// split-count rules
+// ---------------------------------------------------------------------------
+
+// Default rule, a reading of the [llama.cpp] thread for 256 CUs: first reach
+// wg_per_cu (2) workgroups per CU so a CU stays busy while one workgroup waits
+// at a barrier; beyond that, split further only while every split keeps at
+// least min_chunk_rows keys. Never more splits than key blocks, at most 256.
+int occupancy_rule(int tiles, int num_cus, int n_blocks, int block_n, int min_chunk_rows,
+                   int wg_per_cu) {
+    const int target = wg_per_cu * num_cus;
+    if (tiles >= target || n_blocks < 2) return 1;
+    const int min_chunk_blocks = imax(1, ceil_div(min_chunk_rows, block_n));
+    const int s_occ = imin(ceil_div(target, tiles), n_blocks);
+    const int s_chunk = n_blocks / min_chunk_blocks;
+    return imax(1, imin(TPATTN_MAX_SPLITS, imax(s_occ, s_chunk)));
+}
+
+// [FA-tiling] §5.2, as an ablation.
+int fa3_rule(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
+             long long size_one_kv_head, bool is_causal_or_local, int max_splits) {
+    if (total_mblocks >= 0.8f * num_sms) {
+        const long long size_l2 = 50LL * 1024 * 1024;
+        if (size_one_kv_head > size_l2 && num_m_blocks >= num_sms * 2 && !is_causal_or_local)
+            return imin((int)((size_one_kv_head + size_l2 - 1) / size_l2), max_splits);
+        return 1;
+    }
+    if (num_n_blocks <= 4) return 1;
+    max_splits = imin(imin(max_splits, num_sms), num_n_blocks);
+    float max_eff = 0.f;
+    std::vector<float> eff(max_splits + 1, 0.f);
+    for (int s = 1; s <= max_splits; ++s) {
+        const float waves = float(total_mblocks) * s / num_sms;
+        eff[s] = waves / ceilf(waves);
+        if (eff[s] > max_eff) max_eff = eff[s];
+    }
+    for (int s = 1; s <= max_splits; ++s)
+        if (eff[s] >= 0.85f * max_eff) return s;
+    return 1;
+}
+
+// [Occupancy] "The Fix": NSPLIT = clamp(ceil(kv_len / 2048), 1, 32), as an ablation.
+int blog_rule(int sk) { return imax(1, imin(32, ceil_div(sk, 2048))); }
+
+// [FA-tiling] §6.2
+bool should_pack(bool varlen, int seqlen_q, int g, int block_m) {
+    if (varlen) return true;
+    auto round_up = [](int a, int b) { return (a + b - 1) / b * b; };
+    const float nopack = float(seqlen_q) / float(round_up(seqlen_q, block_m));
+    const float pack = float(seqlen_q * g) / float(round_up(seqlen_q * g, block_m));
+    return nopack < 0.9f * pack;
+}
+
+int device_cus() {
+    static int cached = 0;
+    if (cached > 0) return cached;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        cached = n;
+    else
+        cached = 256;  // MI355X
+    return cached;
+}
+
+// ---------------------------------------------------------------------------
+// planner
+// ---------------------------------------------------------------------------
+struct Problem {
+    int B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, varlen;
+    long long sum_seqlens_k;
+    float scale;
+};
+
+int check_problem(const Problem& p) {
+    if (p.B < 0 || p.Sq < 0 || p.Sk < 0)
+        return fail(TPATTN_EINVAL, "negative size (B=%d Sq=%d Sk=%d)", p.B, p.Sq, p.Sk);
+    if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0)
+        return fail(TPATTN_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", p.Hq, p.Hkv);
+    if (p.dtype != TPATTN_FP32 && p.dtype != TPATTN_BF16)
+        return fail(TPATTN_EUNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p.dtype);
+    if (p.d != 64 && p.d != 128)
+        return fail(TPATTN_EUNSUPPORTED, "head dim %d is not built (64 or 128)", p.d);
+    if (p.window_left < -1) return fail(TPATTN_EINVAL, "window_left=%d < -1", p.window_left);
+    if (!(p.scale > 0.f) || !isfinite(p.scale))
+        return fail(TPATTN_EINVAL, "scale must be finite and > 0");
+    if (p.num_splits > TPATTN_MAX_SPLITS)
+        return fail(TPATTN_EINVAL, "num_splits=%d > %d", p.num_splits, TPATTN_MAX_SPLITS);
+    if (p.B > 65535) return fail(TPATTN_EINVAL, "B=%d exceeds the grid limit 65535", p.B);
+    const long long elems = (long long)p.B * p.Sq * p.Hq * p.d;
+    const long long kv = (long long)p.B * p.Sk * p.Hkv * p.d;
+    if (elems > (1LL << 40) || kv > (1LL << 40)) return fail(TPATTN_EINVAL, "tensor too large");
+    if ((long long)p.Sq * (p.Hq / p.Hkv) > 0x7fffffffLL / 2)
+        return fail(TPATTN_EINVAL, "Sq*G too large");
+    return TPATTN_OK;
+}
+
+struct Plan {
+    tpattn_plan pub;
+    const FwdVariant* var;
+};
+
+int make_plan(const Problem& p, int num_cus, Plan* out) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    const int G = p.Hq / p.Hkv;
+    if (num_cus <= 0) num_cus = device_cus();
+
+    // ---- tile choice ([FA-tiling] §2, retargeted to gfx950): a "decode" tile of
+    // 16 rows when all query rows of a KV head (packed) fit in 16, else a
+    // "prefill" tile; packing per [FA-tiling] §6.2.
+    const bool decode = (G > 1) ? (p.Sq * G <= 16) : (p.Sq <= 16);
+    const FwdVariant* var = nullptr;
+    for (const FwdVariant* v = fwd_variants(); v->launch; ++v) {
+        if (v->dtype != p.dtype || v->d != p.d) continue;
+        const bool is_decode = v->block_m <= 16;
+        if (is_decode == decode) {
+            var = v;
+            break;
+        }
+    }
+    if (!var) return fail(TPATTN_EUNSUPPORTED, "no kernel variant for dtype %d d %d", p.dtype, p.d);
+    const int BM = var->block_m, BN = var->block_n;
+    bool pack = false;
+    if (G > 1) pack = decode ? true : should_pack(p.varlen != 0, p.Sq, G, BM);
+
+    tpattn_plan& q = out->pub;
+    q = tpattn_plan{};
+    q.pack_gqa = pack;
+    q.block_m = BM;
+    q.block_n = BN;
+    q.waves_m = var->waves_m;
+    q.waves_n = var->waves_n;
+    q.threads = 64 * var->waves_m * var->waves_n;
+    q.lds_bytes = var->lds_bytes;
+    q.num_cus = num_cus;
+    const int rows = pack ? p.Sq * G : p.Sq;
+    q.num_m_blocks = ceil_div(imax(rows, 0), BM);
+    q.grid_heads = pack ? p.Hkv : p.Hq;
+    q.lpt = p.causal ? 1 : 0;
+
+    // ---- key blocks per tile (fixed-length view with Sk)
+    long long visited = 0;
+    int max_blocks = 0;
+    for (int m = 0; m < q.num_m_blocks; ++m) {
+        int lo, hi;
+        n_block_range(p.Sq, p.Sk, G, pack, p.causal, p.window_left, BM, BN, m, &lo, &hi);
+        const int nb = imax(0, hi - lo);
+        visited += nb;
+        max_blocks = imax(max_blocks, nb);
+    }
+    q.visited_blocks = visited * (long long)q.grid_heads * p.B;
+
+    // ---- split count ([llama.cpp] occupancy rule; [FA-tiling] §5 ablation)
+    const long long tiles = (long long)p.B * q.grid_heads * q.num_m_blocks;
+    const int min_chunk = env_int("TPATTN_MIN_CHUNK", 256);
+    const int wg_per_cu = imax(1, env_int("TPATTN_WG_PER_CU", 2));
+    const int rule = env_int("TPATTN_SPLIT_RULE", 0);  // 0 occupancy, 1 fa3, 2 blog
+    int S = 1;
+    int chunk = 0;
+    if (p.num_splits >= 1) {
+        S = p.num_splits;
+    } else if (tiles > 0) {
+        const int t = (int)(tiles > 0x7fffffff ? 0x7fffffff : tiles);
+        if (rule == 1) {
+            const long long kvh = (long long)p.Sk * p.d * 2 * (p.dtype == TPATTN_BF16 ? 2 : 4);
+            S = fa3_rule(t, num_cus, max_blocks, q.num_m_blocks, kvh,
+                         p.causal || p.window_left >= 0, 128);
+        } else if (rule == 2) {
+            S = blog_rule(p.Sk);
+        } else if (p.varlen) {
+            // per-sequence chunk: as many splits as keep >= min_chunk keys, but
+            // enough to reach the workgroup target when the batch is short
+            const long long sum = p.sum_seqlens_k > 0 ? p.sum_seqlens_k : (long long)p.B * p.Sk;
+            const long long blocks = (sum + BN - 1) / BN * q.grid_heads * (long long)q.num_m_blocks;
+            const long long target = (long long)wg_per_cu * num_cus;
+            int cb = imax(1, ceil_div(min_chunk, BN));
+            if (blocks / cb < target) cb = (int)imax(1, (int)(blocks / target));
+            chunk = cb;
+            S = imax(1, imin(TPATTN_MAX_SPLITS, ceil_div(imax(max_blocks, 1), cb)));
+            if (S == 1) chunk = 0;
+        } else {
+            S = occupancy_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
+        }
+    }
+    S = imax(1, imin(S, TPATTN_MAX_SPLITS));
+    q.num_splits = S;
+    q.chunk_blocks = chunk;
+    q.grid_x = q.num_m_blocks;
+    q.grid_y = q.grid_heads * S;
+    q.grid_z = p.B;
+    if (q.grid_y > 65535) return fail(TPATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
+    q.workspace_bytes = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, p.d, S) : 0;
+    out->var = var;
+    return TPATTN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// split workspace (one per device) and kernel timing
+// ---------------------------------------------------------------------------
+struct Workspace {
+    std::mutex mu;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+Workspace g_ws[64];
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    int max_launches = 0;
+    std::vector<hipEvent_t> ev;  // pairs
+    std::vector<int> kind;       // 0 forward, 1 combine
+    int used = 0;
+} g_prof;
+
+// Records a start event if profiling; returns the slot or -1.
+int prof_start(int kind, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (!g_prof.on || g_prof.used >= g_prof.max_launches) return -1;
+    const int slot = g_prof.used++;
+    g_prof.kind[slot] = kind;
+    (void)hipEventRecord(g_prof.ev[2 * slot], s);
+    return slot;
+}
+void prof_stop(int slot, hipStream_t s) {
+    if (slot < 0) return;
+    (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+}
+
+int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
+            const int* seqlens_k, void* stream_v) {
+    // pointers are checked only where they will be read (empty tensors may be null)
+    const bool has_rows = pr.B > 0 && pr.Sq > 0;
+    if (has_rows && (!q || !o)) return fail(TPATTN_EINVAL, "null q or o pointer");
+    if (has_rows && pr.Sk > 0 && (!k || !v)) return fail(TPATTN_EINVAL, "null k or v pointer");
+    if (pr.varlen && pr.B > 0 && !seqlens_k) return fail(TPATTN_EINVAL, "seqlens_k is null");
+    Plan plan;
+    int rc = make_plan(pr, 0, &plan);
+    if (rc) return rc;
+    if (!has_rows) return TPATTN_OK;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    const tpattn_plan& pl = plan.pub;
+
+    FwdParams fp{};
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.o = o;
+    fp.lse = lse;
+    fp.seqlens_k = seqlens_k;
+    fp.B = pr.B;
+    fp.Hq = pr.Hq;
+    fp.Hkv = pr.Hkv;
+    fp.Sq = pr.Sq;
+    fp.Sk = pr.Sk;
+    fp.G = pr.Hq / pr.Hkv;
+    fp.causal = pr.causal ? 1 : 0;
+    fp.window_left = pr.window_left;
+    fp.scale = pr.scale;
+    fp.scale_log2 = pr.scale * 1.4426950408889634f;
+    fp.pack = pl.pack_gqa;
+    fp.num_m_blocks = pl.num_m_blocks;
+    fp.grid_heads = pl.grid_heads;
+    fp.num_splits = pl.num_splits;
+    fp.chunk_blocks = pl.chunk_blocks;
+    fp.lpt = pl.lpt;
+
+    const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
+    if (pl.num_splits == 1) {
+        const int slot = prof_start(0, stream);
+        hipError_t e = plan.var->launch(fp, grid, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
+        return TPATTN_OK;
+    }
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(TPATTN_EHIP, "hipGetDevice failed");
+    Workspace& ws = g_ws[dev];
+    std::lock_guard<std::mutex> lk(ws.mu);
+    if (ws.bytes < pl.workspace_bytes) {
+        if (ws.ptr) {
+            (void)hipDeviceSynchronize();  // earlier calls may still read the old buffer
+            (void)hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        hipError_t e = hipMalloc(&ws.ptr, pl.workspace_bytes);
+        if (e != hipSuccess) {
+            ws.ptr = nullptr;
+            return fail(TPATTN_ENOMEM, "split workspace of %zu bytes: %s", pl.workspace_bytes,
+                        hipGetErrorString(e));
+        }
+        ws.bytes = pl.workspace_bytes;
+    }
+    const size_t rows = (size_t)pr.B * pr.Sq * pr.Hq;
+    fp.o_part = reinterpret_cast<float*>(ws.ptr);
+    fp.lse_part = fp.o_part + (size_t)pl.num_splits * rows * pr.d;
+
+    int slot = prof_start(0, stream);
+    hipError_t e = plan.var->launch(fp, grid, stream);
+    prof_stop(slot, stream);
+    if (e != hipSuccess) return fail(TPATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
+
+    CombineParams cp{};
+    cp.o_part = fp.o_part;
+    cp.lse_part = fp.lse_part;
+    cp.o = o;
+    cp.lse = lse;
+    cp.rows = (int)rows;
+    cp.num_splits = pl.num_splits;
+    cp.Sq = pr.Sq;
+    cp.Hq = pr.Hq;
+    slot = prof_start(1, stream);
+    e = launch_combine(cp, pr.d, pr.dtype == TPATTN_BF16, stream);
+    prof_stop(slot, stream);
+    if (e != hipSuccess) return fail(TPATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
+    return TPATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int Sq, int Sk, int d, int causal, int window_left, float scale,
+               int num_splits, int dtype, void* stream) {
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, scale};
+    return run_fwd(p, q, k, v, o, lse, nullptr, stream);
+}
+
+int tpattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                      float scale, int num_splits, int dtype, const int* seqlens_k,
+                      long long sum_seqlens_k, void* stream) {
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 1, sum_seqlens_k, scale};
+    return run_fwd(p, q, k, v, o, lse, seqlens_k, stream);
+}
+
+int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
+                    tpattn_plan* out) {
+    if (!out) return fail(TPATTN_EINVAL, "null plan pointer");
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, varlen ? 1 : 0,
+              sum_seqlens_k, 1.0f};
+    Plan plan;
+    int rc = make_plan(p, num_cus, &plan);
+    if (rc) return rc;
+    *out = plan.pub;
+    return TPATTN_OK;
+}
+
+size_t tpattn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits) {
+    if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0 || num_splits <= 1) return 0;
+    const size_t rows = (size_t)B * Hq * Sq;
+    return (size_t)num_splits * rows * ((size_t)d + 1) * sizeof(float);
+}
+
+int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B,
+                       int Sq, int Hq, int d, int num_splits, int dtype, void* stream_v) {
+    if (!o_part || !lse_part || !o) return fail(TPATTN_EINVAL, "null tensor pointer");
+    if (B < 0 || Sq < 0 || Hq < 1) return fail(TPATTN_EINVAL, "bad shape");
+    if (d != 64 && d != 128) return fail(TPATTN_EUNSUPPORTED, "head dim %d is not built", d);
+    if (dtype != TPATTN_FP32 && dtype != TPATTN_BF16)
+        return fail(TPATTN_EUNSUPPORTED, "dtype %d", dtype);
+    if (num_splits < 1 || num_splits > TPATTN_MAX_SPLITS)
+        return fail(TPATTN_EINVAL, "num_splits=%d outside [1, 256]", num_splits);
+    const long long rows = (long long)B * Sq * Hq;
+    if (rows > 0x7fffffffLL) return fail(TPATTN_EINVAL, "too many rows");
+    if (rows == 0) return TPATTN_OK;
+    CombineParams cp{};
+    cp.o_part = o_part;
+    cp.lse_part = lse_part;
+    cp.o = o;
+    cp.lse = lse;
+    cp.rows = (int)rows;
+    cp.num_splits = num_splits;
+    cp.Sq = Sq;
+    cp.Hq = Hq;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    const int slot = prof_start(1, stream);
+    hipError_t e = launch_combine(cp, d, dtype == TPATTN_BF16, stream);
+    prof_stop(slot, stream);
+    if (e != hipSuccess) return fail(TPATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
+    return TPATTN_OK;
+}
+
+int tpattn_n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
+                         int block_m, int block_n, int m_block, int split, int num_splits,
+                         int* n_min, int* n_max) {
+    if (!n_min || !n_max) return fail(TPATTN_EINVAL, "null output pointer");
+    if (Sq < 1 || Skb < 0 || G < 1 || block_m < 1 || block_n < 1 || m_block < 0 ||
+        num_splits < 1 || split < 0 || split >= num_splits || window_left < -1)
+        return fail(TPATTN_EINVAL, "bad block-range arguments");
+    int lo, hi;
+    n_block_range(Sq, Skb, G, pack, causal, window_left, block_m, block_n, m_block, &lo, &hi);
+    split_range(lo, hi, split, num_splits, n_min, n_max);
+    return TPATTN_OK;
+}
+
+int tpattn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int block_m) {
+    if (seqlen_q < 1 || qhead_per_khead < 1 || block_m < 1) return 0;
+    return should_pack(varlen != 0, seqlen_q, qhead_per_khead, block_m) ? 1 : 0;
+}
+
+int tpattn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
+                          long long size_one_kv_head, int is_causal_or_local, int max_splits) {
+    if (total_mblocks < 1 || num_sms < 1 || max_splits < 1) return 1;
+    return fa3_rule(total_mblocks, num_sms, num_n_blocks, num_m_blocks, size_one_kv_head,
+                    is_causal_or_local != 0, max_splits);
+}
+
+int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
+                                int min_chunk_rows, int wg_per_cu) {
+    if (tiles < 1 || num_cus < 1 || block_n < 1 || wg_per_cu < 1) return 1;
+    return occupancy_rule(tiles, num_cus, n_blocks, block_n, min_chunk_rows, wg_per_cu);
+}
+
+int tpattn_profile_begin(int max_launches) {
+    if (max_launches < 1 || max_launches > (1 << 20)) return fail(TPATTN_EINVAL, "max_launches");
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+    g_prof.kind.assign(max_launches, 0);
+    for (auto& e : g_prof.ev)
+        if (hipEventCreate(&e) != hipSuccess) return fail(TPATTN_EHIP, "hipEventCreate");
+    g_prof.max_launches = max_launches;
+    g_prof.used = 0;
+    g_prof.on = true;
+    return TPATTN_OK;
+}
+
+int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
+                       int* combine_launches) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    double t[2] = {0, 0};
+    int n[2] = {0, 0};
+    for (int i = 0; i < g_prof.used; ++i) {
+        if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) continue;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) == hipSuccess) {
+            t[g_prof.kind[i]] += ms;
+            n[g_prof.kind[i]] += 1;
+        }
+    }
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.kind.clear();
+    g_prof.on = false;
+    g_prof.used = 0;
+    if (fwd_ms) *fwd_ms = t[0];
+    if (fwd_launches) *fwd_launches = n[0];
+    if (combine_ms) *combine_ms = t[1];
+    if (combine_launches) *combine_launches = n[1];
+    return TPATTN_OK;
+}
+
+const char* tpattn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

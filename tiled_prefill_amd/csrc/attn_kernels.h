@@ -1,0 +1,28 @@
+// attn_kernels.h -- launchers of the gfx950 attention kernels (internal to the
+// library; the public C-ABI is include/tpattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_plan.h"
+
+namespace tpa {
+
+enum DType { DT_FP32 = 0, DT_BF16 = 1 };
+
+// One compiled forward-kernel instantiation: element type, head dim and tile.
+struct FwdVariant {
+    int dtype, d;
+    int block_m, block_n;   // query rows and key rows per tile
+    int waves_m, waves_n;   // waves along M (rows) and along N (keys)
+    int lds_bytes;
+    hipError_t (*launch)(const FwdParams&, dim3 grid, hipStream_t stream);
+};
+
+// All compiled variants (null-terminated by launch == nullptr).
+const FwdVariant* fwd_variants();
+
+// The log-sum-exp combine of split partials.
+hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);
+
+}  // namespace tpa

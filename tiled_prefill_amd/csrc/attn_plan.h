@@ -1,0 +1,111 @@
+// attn_plan.h -- block ranges, split ranges and kernel parameters shared by the
+// host planner and the gfx950 kernels (both sides of the product library).
+//
+// Citations name the page and section they follow:
+//   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
+//   [Occupancy]  "The Occupancy Awakening: Rewriting a Flash Attention Kernel for
+//                Blackwell's 188 SMs"
+//   [llama.cpp]  llama.cpp pull request 21086 review thread (blocks per SM and the
+//                stream-k fixup)
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TPA_HD __host__ __device__ __forceinline__
+#else
+#define TPA_HD inline
+#endif
+
+namespace tpa {
+
+TPA_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// floor division that is correct for negative numerators (b > 0)
+TPA_HD int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+TPA_HD int imin(int a, int b) { return a < b ? a : b; }
+TPA_HD int imax(int a, int b) { return a > b ? a : b; }
+
+// Key-block range [n_min, n_max) that query block m_block must visit
+// ([FA-tiling] §3.1-3.2). Rows of the block are rows [m_block*BM, (m_block+1)*BM)
+// of the query rows of one (batch, grid head); with GQA packing those are the
+// Sq*G packed rows and row r sits at sequence position r / G ([FA-tiling] §6.3).
+// The bounds use the first and last *existing* row of the block, which is the
+// tight form of the page's (m_block+1)*kBlockM upper index. Keys are aligned to
+// the bottom right: delta = Skb - Sq. causal => window_right = 0; window_left
+// < 0 => no lower bound. An empty range (n_max <= n_min) means no row of the
+// block sees any key.
+TPA_HD void n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
+                          int BM, int BN, int m_block, int* n_min, int* n_max) {
+    const int nrows = pack ? Sq * G : Sq;
+    const int r0 = m_block * BM;
+    const int r1 = imin((m_block + 1) * BM, nrows);  // exclusive
+    const int pos_min = pack ? r0 / G : r0;
+    const int pos_max = pack ? (r1 - 1) / G : r1 - 1;
+    const int delta = Skb - Sq;
+    int hi = ceil_div(Skb, BN);
+    if (causal) hi = imin(hi, floor_div(pos_max + delta, BN) + 1);
+    int lo = 0;
+    if (window_left >= 0) lo = imax(0, floor_div(pos_min + delta - window_left, BN));
+    *n_min = lo;
+    *n_max = hi;
+}
+
+// Number of splits that batch b actually uses. Fixed-length problems use all
+// num_splits. With a positive chunk (in key blocks) each sequence instead gets
+// ceil(blocks / chunk) splits, at most num_splits ([FA-tiling] §5.3: the split
+// count may differ per sequence in the variable-length case).
+TPA_HD int splits_for(int n_blocks, int num_splits, int chunk_blocks) {
+    if (chunk_blocks <= 0) return num_splits;
+    if (n_blocks <= 0) return 1;
+    return imin(num_splits, imax(1, ceil_div(n_blocks, chunk_blocks)));
+}
+
+// Even partition of [n_min, n_max) into `splits` pieces ([FA-tiling] §3.2 and
+// §5.3): per = ceil(len / splits); split s gets [n_min + s*per, min(.. + per,
+// n_max)). Trailing pieces may be empty (returned as n_max <= n_min).
+TPA_HD void split_range(int n_min, int n_max, int split, int splits, int* s_min, int* s_max) {
+    if (splits <= 1) {
+        *s_min = n_min;
+        *s_max = n_max;
+        return;
+    }
+    const int len = imax(0, n_max - n_min);
+    const int per = ceil_div(len, splits);
+    const int lo = n_min + split * per;
+    *s_min = lo;
+    *s_max = imin(lo + per, n_max);
+}
+
+// Arguments of the forward kernel (passed by value).
+struct FwdParams {
+    const void* q;          // [B][Sq][Hq][d]
+    const void* k;          // [B][Sk][Hkv][d]
+    const void* v;          // [B][Sk][Hkv][d]
+    void* o;                // [B][Sq][Hq][d], dtype of q
+    float* lse;             // [B][Hq][Sq] or null
+    float* o_part;          // [S][B*Sq*Hq][d] fp32 split partials (num_splits > 1)
+    float* lse_part;        // [S][B*Sq*Hq]
+    const int* seqlens_k;   // device int[B] or null (then Sk everywhere)
+    int B, Hq, Hkv, Sq, Sk, G;
+    int causal, window_left;
+    float scale_log2;       // scale * log2(e): scores enter exp2 pre-multiplied
+    float scale;            // softmax scale (natural-log units, for lse)
+    int pack;               // GQA packing: the G heads of a KV head share one tile
+    int num_m_blocks;       // query blocks per (batch, grid head)
+    int grid_heads;         // Hkv when packed, Hq otherwise
+    int num_splits;         // grid splits (1: no split, direct output)
+    int chunk_blocks;       // > 0: per-sequence split count (variable length)
+    int lpt;                // reverse query-block order (heaviest causal blocks first)
+};
+
+// Arguments of the log-sum-exp combine kernel. Every split writes its lse
+// partial (-inf for an empty split), so the combine needs no block ranges.
+struct CombineParams {
+    const float* o_part;    // [S][rows][d]
+    const float* lse_part;  // [S][rows]
+    void* o;                // [rows][d]; rows ordered (batch, position, head) as in o
+    float* lse;             // [B][Hq][Sq] or null
+    int rows, num_splits, Sq, Hq;
+};
+
+}  // namespace tpa
