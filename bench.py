@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run one leg only (for profiling)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first copy a buffer of this many MiB three times (a plain copy "
+                         "of known size, to calibrate HBM byte counters)")
     return ap.parse_args()
 
 
@@ -79,6 +82,13 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     out = {}
+    if args.copy_mb > 0:
+        src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------------ decode
     w = WORKLOADS["gqa_decode_bf16"]
