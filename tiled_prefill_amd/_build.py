@@ -10,8 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtpattn.so")
 
-SOURCES = ["attn_fwd.hip", "attn_api.cpp"]
-HEADERS = ["attn_plan.h", "attn_kernels.h"]
+SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_api.cpp"]
+HEADERS = ["attn_plan.h", "attn_kernels.h", "attn_device.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -157,7 +157,14 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     // "prefill" tile; packing per [FA-tiling] §6.2.
     const bool decode = (G > 1) ? (p.Sq * G <= 16) : (p.Sq <= 16);
     const FwdVariant* var = nullptr;
-    for (const FwdVariant* v = fwd_variants(); v->launch; ++v) {
+    if (decode && env_int("TPATTN_GENERIC_DECODE", 0) == 0) {
+        for (const FwdVariant* v = decode_variants(); v->launch; ++v)
+            if (v->dtype == p.dtype && v->d == p.d) {
+                var = v;
+                break;
+            }
+    }
+    for (const FwdVariant* v = fwd_variants(); !var && v->launch; ++v) {
         if (v->dtype != p.dtype || v->d != p.d) continue;
         const bool is_decode = v->block_m <= 16;
         if (is_decode == decode) {
@@ -311,6 +318,9 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.num_splits = pl.num_splits;
     fp.chunk_blocks = pl.chunk_blocks;
     fp.lpt = pl.lpt;
+    // decode grids: the workgroups of one key range (all grid heads) are
+    // dispatched together, so concurrent reads cover whole interleaved KV rows
+    fp.split_major = env_int("TPATTN_SPLIT_MAJOR", plan.var->block_m <= 16 ? 1 : 0);
 
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
     if (pl.num_splits == 1) {

@@ -1,0 +1,399 @@
+// attn_decode.hip -- gfx950 split-KV decode kernel and the log-sum-exp combine.
+//
+// Citations:
+//   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
+//   [Occupancy]  "The Occupancy Awakening: Rewriting a Flash Attention Kernel
+//                for Blackwell's 188 SMs"
+//
+// Decode is bound by reading K and V once from HBM. All query rows of one
+// (batch, KV head) -- the G packed query heads of a GQA group ([FA-tiling] §6),
+// at most 16 rows -- fit one MFMA column block, so a workgroup owns one
+// (batch, grid head, split) and its waves walk disjoint 64-key blocks of the
+// split's key range, each with its own online-softmax state, merged in LDS at the
+// end. K goes straight from global memory into the registers of the MFMA A
+// operand; V is staged row-major in a per-wave LDS region and read back
+// transposed with ds_read_b64_tr_b16. The loads of the next block are issued as
+// soon as the registers they overwrite are consumed, so every wave keeps a full
+// block of K and V in flight.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_device.h"
+#include "attn_kernels.h"
+#include "attn_plan.h"
+
+namespace tpa {
+
+template <int D, int NW>
+struct DecodeTile {
+    static constexpr int KB = 64;              // keys per wave block
+    static constexpr int NSLAB = D / 32;       // 32-d slabs of the QK contraction
+    static constexpr int NT = KB / 16;         // 16-key sub-tiles of a block
+    static constexpr int DT = D / 16;          // 16-wide d tiles of the output
+    static constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+    static constexpr int RPI = 64 / CPR;       // V rows per wave-wide load
+    static constexpr int NVL = KB / RPI;       // V loads per lane per block
+    static constexpr int ROWB = D * 2;         // bytes per V row in LDS (unpadded)
+    static constexpr int V_BYTES = NW * KB * ROWB;
+    static constexpr int RED_BYTES = NW * (DT * 4 * 64 + 2 * 64) * 4;
+    static constexpr int LDS_BYTES = V_BYTES > RED_BYTES ? V_BYTES : RED_BYTES;
+    // XOR swizzle of the 16-byte chunk of V row r in LDS: the transposed reads of
+    // 8 consecutive rows x 2 chunks then hit 16 distinct 16-byte bank groups.
+    static __device__ __forceinline__ int swz(int r) {
+        return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1;
+    }
+};
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
+    using C = DecodeTile<D, NW>;
+    constexpr int KB = C::KB, NSLAB = C::NSLAB, NT = C::NT, DT = C::DT;
+    constexpr int CPR = C::CPR, RPI = C::RPI, NVL = C::NVL, ROWB = C::ROWB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    char* vl = smem + wave * KB * ROWB;  // this wave's V block, swizzled rows
+
+    const int hg = p.split_major ? (int)blockIdx.y % p.grid_heads : (int)blockIdx.y / p.num_splits;
+    const int split = p.split_major ? (int)blockIdx.y / p.grid_heads : (int)blockIdx.y % p.num_splits;
+    const int b = blockIdx.z;
+    int Skb = p.Sk;
+    if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
+    const int G = p.G;
+    const int hkv = p.pack ? hg : hg / G;
+    const int nrows = p.pack ? p.Sq * G : p.Sq;
+    const int delta = Skb - p.Sq;
+
+    // key blocks of this split ([FA-tiling] §3.2, §5.3)
+    int n_lo, n_hi;
+    n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, 16, KB, 0, &n_lo, &n_hi);
+    const int S_b = splits_for(imax(0, n_hi - n_lo), p.num_splits, p.chunk_blocks);
+    int s_lo = 0, s_hi = 0;
+    if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+
+    // this lane's query row (column li of every S^T tile)
+    const int r = li;
+    const bool row_ok = r < nrows;
+    const int pos = row_ok ? (p.pack ? r / G : r) : 0;
+    const int head = p.pack ? hkv * G + (row_ok ? r % G : 0) : hg;
+    int row_lo = 0, row_hi = Skb - 1;
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+    if (row_ok) {
+        if (p.window_left >= 0) row_lo = pos + delta - p.window_left;
+        if (p.causal) row_hi = imin(row_hi, pos + delta);
+        wlo = row_lo;
+        whi = row_hi;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+
+    // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
+    const bf16_t* kp = reinterpret_cast<const bf16_t*>(p.k);
+    const bf16_t* vp = reinterpret_cast<const bf16_t*>(p.v);
+    u32x4 qf[NSLAB];
+    {
+        const bf16_t* qrow = qp + (((size_t)b * p.Sq + pos) * p.Hq + head) * D + 8 * lg;
+        const bool use = row_ok && s_hi > s_lo;
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c);  // row 0 when !row_ok
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qf[c] = use ? x : z;
+        }
+    }
+
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const bf16_t* kbase = kp + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = vp + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+
+    u32x4 kr[NT][NSLAB];  // K fragments of the current block
+    // Buffer resources over the block's rows that exist (rows at or past Skb read
+    // as zeros): the loads of a block are issued without any branch.
+    const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+    auto block_bytes = [&](int n) { return (uint32_t)imin(KB, Skb - n * KB) * row_bytes; };
+    auto load_k = [&](int n) {
+        const rsrc_t rk = make_rsrc(kbase + (size_t)n * KB * kv_stride, block_bytes(n));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int c = 0; c < NSLAB; ++c)
+                kr[t][c] = buf_load16(rk, (16 * t + li) * row_bytes + 2 * (8 * lg + 32 * c));
+    };
+    // V goes from global memory straight into LDS (buffer_load ... lds): lane l of
+    // load i fills bytes [16 l, 16 l + 16) of the i-th kilobyte of the region,
+    // i.e. row RPI*i + l / CPR, chunk slot l % CPR, which holds the row's chunk
+    // (slot ^ swz(row)).
+    auto load_v = [&](int n) {
+        const rsrc_t rv = make_rsrc(vbase + (size_t)n * KB * kv_stride, block_bytes(n));
+        const int r0 = lane / CPR, slot = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int rr = RPI * i + r0;
+            // (offset computed outside the builtin's argument list: a call there
+            // makes this compiler drop the kernel's host launch stub)
+            const uint32_t voff = rr * row_bytes + 16 * (slot ^ C::swz(rr));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, voff, 0, 0, 0);
+        }
+    };
+
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
+
+    int n = s_lo + wave;
+    if (n < s_hi) {
+        load_v(n);
+        load_k(n);
+    }
+    for (; n < s_hi; n += NW) {
+        const bool more = n + NW < s_hi;
+        // wait for this block's K (registers) and V (LDS, written by the DMA)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+        // S^T = K . Q^T for the 64 keys of the block
+        f32x4 sacc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NSLAB; ++c) sacc[t] = mfma_bf16(kr[t][c], qf[c], sacc[t]);
+        }
+        if (more) load_k(n + NW);
+
+        const int key0 = n * KB;
+        if (!(key0 >= wlo && key0 + KB - 1 <= whi)) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = key0 + 16 * t + 4 * lg + e;
+                    if (key < row_lo || key > row_hi) sacc[t][e] = -INFINITY;
+                }
+        }
+
+        // online softmax
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[t][e]);
+        mx = xor_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2((m_run - m_use) * sl2);
+        const float neg = -m_use * sl2;
+        float rs = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pv = fast_exp2(fmaf(sacc[t][e], sl2, neg));
+                sacc[t][e] = pv;
+                rs += pv;
+            }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
+
+        // O^T += V^T . P^T with P as bf16 hi + lo parts
+#pragma unroll
+        for (int pp = 0; pp < NT / 2; ++pp) {
+            const u32x2 s0 = split_bf16x2(sacc[2 * pp][0], sacc[2 * pp][1]);
+            const u32x2 s1 = split_bf16x2(sacc[2 * pp][2], sacc[2 * pp][3]);
+            const u32x2 s2 = split_bf16x2(sacc[2 * pp + 1][0], sacc[2 * pp + 1][1]);
+            const u32x2 s3 = split_bf16x2(sacc[2 * pp + 1][2], sacc[2 * pp + 1][3]);
+            const u32x4 ph = {s0[0], s1[0], s2[0], s3[0]};
+            const u32x4 pl = {s0[1], s1[1], s2[1], s3[1]};
+            // transposed reads of V rows 32pp + 4g + k and 32pp + 16 + 4g + k
+            const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
+            const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                const int ch = 2 * u + cb;
+                const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(
+                    vl + ra * ROWB + 16 * (ch ^ C::swz(ra)) + hb));
+                const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(
+                    vl + rb * ROWB + 16 * (ch ^ C::swz(rb)) + hb));
+                const u32x4 vf = {a[0], a[1], c[0], c[1]};
+                oacc[u] = mfma_bf16(vf, ph, oacc[u]);
+                oacc[u] = mfma_bf16(vf, pl, oacc[u]);
+            }
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this block's LDS reads are done
+            load_v(n + NW);
+        }
+    }
+    l_run = xor_sum(l_run);
+
+    // merge the waves' softmax states
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    float* red_o = red;                          // [NW][DT*4][64]
+    float* red_ml = red + NW * DT * 4 * 64;      // [NW][2][64]
+#pragma unroll
+    for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red_o[(wave * DT * 4 + u * 4 + e) * 64 + lane] = oacc[u][e];
+    red_ml[(wave * 2 + 0) * 64 + lane] = m_run;
+    red_ml[(wave * 2 + 1) * 64 + lane] = l_run;
+    __syncthreads();
+    if (wave != 0) return;
+    float mw[NW], mstar = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        mw[w] = red_ml[(w * 2 + 0) * 64 + lane];
+        mstar = fmaxf(mstar, mw[w]);
+    }
+    const float muse = mstar == -INFINITY ? 0.f : mstar;
+    float l = 0.f;
+#pragma unroll
+    for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float a = fast_exp2((mw[w] - muse) * sl2);
+        l += a * red_ml[(w * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < DT; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[u][e] += a * red_o[(w * DT * 4 + u * 4 + e) * 64 + lane];
+    }
+
+    // epilogue: the split partial (O_s normalised, lse_s) or the final O and lse
+    if (!row_ok) return;
+    const bool any = l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const float lse = any ? mstar * p.scale + logf(l) : -INFINITY;
+    const size_t row = ((size_t)b * p.Sq + pos) * p.Hq + head;
+    if (p.num_splits > 1) {
+        const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
+        if (lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+        if (any) {
+            float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
+#pragma unroll
+            for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4*>(orow + 16 * u) = oacc[u] * inv;
+        }
+    } else {
+        if (lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + head) * p.Sq + pos] = lse;
+        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * D + 4 * lg;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[u][0] * inv, oacc[u][1] * inv);
+            w[1] = pack_bf16x2(oacc[u][2] * inv, oacc[u][3] * inv);
+            *reinterpret_cast<u32x2*>(orow + 16 * u) = w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp combine of split partials ([FA-tiling] §5.1; [Occupancy] "The
+// Fix"): per output row, lse = M + ln sum_s exp(lse_s - M) with M = max_s lse_s,
+// O = sum_s exp(lse_s - lse) O_s. A workgroup owns one row and a 32-wide slice
+// of d: 8 lanes per float4 column x 32 split groups. The partial-output loads
+// are issued before the lse reductions so their latency overlaps. Empty splits
+// (lse_s = -inf) carry zero weight and their O_s is never used; a row whose
+// splits are all empty gets O = 0, lse = -inf.
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D) {
+    constexpr int SG = 32;                   // split groups
+    constexpr int MAXI = TPA_MAX_SPLITS / SG;
+    __shared__ float lse_s[TPA_MAX_SPLITS];
+    __shared__ float wred[2][4];
+    __shared__ f32x4 acc_s[32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x;
+    const int d0 = 32 * blockIdx.y;
+    const int c4 = tid & 7, sg = tid >> 3;
+    const int S = p.num_splits;
+    const size_t rows = (size_t)p.rows;
+
+    f32x4 ov[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int s = sg + SG * i;
+        if (s < S)
+            ov[i] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + d0 + 4 * c4);
+    }
+    const float x = tid < S ? p.lse_part[(size_t)tid * rows + row] : -INFINITY;
+    if (tid < S) lse_s[tid] = x;
+    const float mx = wave_max(x);
+    if (lane == 0) wred[0][wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+    const float sm = wave_sum((tid < S && M != -INFINITY) ? expf(x - M) : 0.f);
+    if (lane == 0) wred[1][wave] = sm;
+    __syncthreads();
+    const float lse = M == -INFINITY ? -INFINITY : M + logf(wred[1][0] + wred[1][1] + wred[1][2] + wred[1][3]);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int s = sg + SG * i;
+            if (s < S) {
+                const float ls = lse_s[s];
+                if (ls != -INFINITY) acc += expf(ls - lse) * ov[i];
+            }
+        }
+    }
+    // reduce over the 8 split groups of each wave (lanes c4, c4+8, ..., c4+56):
+    // row_mirror pairs lane 8 + j with 7 - j, so pre-permute with the half mirror
+    // to line up equal c4 before it; then the two lane-bit swaps
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float a = acc[e];
+        a += dpp<DPP_MIRROR>(dpp<DPP_HALF_MIRROR>(a));
+        acc[e] = xor_sum(a);
+    }
+    if (lane < 8) acc_s[wave * 8 + lane] = acc;
+    __syncthreads();
+    if (tid < 8) {
+        acc = acc_s[tid] + acc_s[8 + tid] + acc_s[16 + tid] + acc_s[24 + tid];
+        if constexpr (OUT_BF16) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[0], acc[1]);
+            w[1] = pack_bf16x2(acc[2], acc[3]);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + d0 + 4 * tid) = w;
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + d0 + 4 * tid) = acc;
+        }
+        if (tid == 0 && blockIdx.y == 0 && p.lse) {
+            const int h = row % p.Hq;
+            const int pos = (row / p.Hq) % p.Sq;
+            const int bb = row / (p.Hq * p.Sq);
+            p.lse[((size_t)bb * p.Hq + h) * p.Sq + pos] = lse;
+        }
+    }
+}
+
+template <int D, int NW>
+hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_decode_kernel<D, NW>), grid, dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
+const FwdVariant* decode_variants() {
+    static const FwdVariant v[] = {
+        {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>},
+        {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>},
+        {0, 0, 0, 0, 0, 0, 0, nullptr},
+    };
+    return v;
+}
+
+hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream) {
+    dim3 grid(p.rows, d / 32), block(256);
+    if (out_bf16) hipLaunchKernelGGL((lse_combine_kernel<true>), grid, block, 0, stream, p, d);
+    else hipLaunchKernelGGL((lse_combine_kernel<false>), grid, block, 0, stream, p, d);
+    return hipGetLastError();
+}
+
+}  // namespace tpa

@@ -1,0 +1,137 @@
+// attn_device.h -- gfx950 device helpers shared by the attention kernels:
+// MFMA wrappers, bf16 conversion, cross-lane reductions, the LDS transpose read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+typedef uint16_t bf16_t;  // bf16 storage (raw bits)
+
+// D[16x16] += A[16x32] . B[32x16], bf16 inputs, fp32 accumulate. Lane l supplies
+// A[l % 16][k(l / 16, e)] and B[k(l / 16, e)][l % 16] for its 8 elements e, and
+// holds D[4 (l / 16) + r][l % 16] for r = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// fp32 16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// A pair of values as two bf16 parts, x ~= hi + lo: returns {hi pair, lo pair}.
+__device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
+    const uint32_t hi = pack_bf16x2(a, b);
+    const uint32_t lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+    return u32x2{hi, lo};
+}
+
+// Cross-lane moves without the LDS crossbar. v_permlane16_swap(v, v) returns a
+// pair whose elements are {v[l], v[l ^ 16]} in some order for every lane l (and
+// v_permlane32_swap likewise for l ^ 32), so combining the pair reduces over
+// that lane bit. DPP quad_perm / row_half_mirror / row_mirror pair lanes inside
+// quads, half-rows and rows of 16.
+__device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __uint_as_float(x); }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+__device__ __forceinline__ float max16(float x) {  // max over lanes l, l ^ 16
+    auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float max32(float x) {  // max over lanes l, l ^ 32
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+__device__ __forceinline__ float sum16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+
+// Reductions over the four lanes i, i+16, i+32, i+48 that share a query column.
+__device__ __forceinline__ float xor_max(float x) { return max32(max16(x)); }
+__device__ __forceinline__ float xor_sum(float x) { return sum32(sum16(x)); }
+
+// Reductions over the 16 lanes of a row (lanes with equal l / 16).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<DPP_QUAD_1032>(x));
+    x = fmaxf(x, dpp<DPP_QUAD_2301>(x));
+    x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+    return fmaxf(x, dpp<DPP_MIRROR>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<DPP_QUAD_1032>(x);
+    x += dpp<DPP_QUAD_2301>(x);
+    x += dpp<DPP_HALF_MIRROR>(x);
+    return x + dpp<DPP_MIRROR>(x);
+}
+__device__ __forceinline__ int row16_imax(int x) {
+    x = max(x, dpp<DPP_QUAD_1032>(x));
+    x = max(x, dpp<DPP_QUAD_2301>(x));
+    x = max(x, dpp<DPP_HALF_MIRROR>(x));
+    return max(x, dpp<DPP_MIRROR>(x));
+}
+__device__ __forceinline__ int row16_imin(int x) {
+    x = min(x, dpp<DPP_QUAD_1032>(x));
+    x = min(x, dpp<DPP_QUAD_2301>(x));
+    x = min(x, dpp<DPP_HALF_MIRROR>(x));
+    return min(x, dpp<DPP_MIRROR>(x));
+}
+// Whole-wave (64 lane) reductions.
+__device__ __forceinline__ float wave_max(float x) { return xor_max(row16_max(x)); }
+__device__ __forceinline__ float wave_sum(float x) { return xor_sum(row16_sum(x)); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resource over [base, base + bytes): a buffer load whose offset is at
+// or beyond `bytes` returns zeros instead of touching memory, so ragged tiles
+// need no branches. base must be uniform across the wave.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane s
+// supplies an 8-byte address; lane n receives element k = 0..3 from source lane
+// 4k + n/4, element n % 4. With source lane s pointing at row k0 + s/4, columns
+// c0 + 4 (s % 4) .. +3 of a row-major 16-bit matrix, lane n receives
+// M[k0 + k][c0 + n] for k = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+}  // namespace tpa

@@ -5,7 +5,7 @@
 //                         range, runs S = K Q^T on MFMA, the online softmax in
 //                         fp32, and O += V^T P^T on MFMA; writes O and lse, or
 //                         the split partial (O_s, lse_s).
-// KB  lse_combine_kernel  merges the split partials by log-sum-exp.
+// (the log-sum-exp combine of split partials lives in attn_decode.hip)
 //
 // Citations:
 //   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
@@ -29,47 +29,11 @@
 
 #include <type_traits>
 
+#include "attn_device.h"
 #include "attn_kernels.h"
 #include "attn_plan.h"
 
 namespace tpa {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-typedef uint16_t bf16_t;  // bf16 storage (raw bits)
-
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// fp32 -> bf16 pair, round to nearest even (hardware conversion on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16x2 v;
-    v[0] = (__bf16)lo;
-    v[1] = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float xor_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
-}
-__device__ __forceinline__ float xor_sum(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // KA: forward kernel.
@@ -163,11 +127,8 @@ attn_fwd_kernel(FwdParams p) {
         row_ok[q] = ok;
     }
     // bounds over the whole wave: a key slice inside [wlo, whi] needs no mask
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        wlo = imax(wlo, __shfl_xor(wlo, s));
-        whi = imin(whi, __shfl_xor(whi, s));
-    }
+    wlo = row16_imax(wlo);  // lane groups g hold the same rows
+    whi = row16_imin(whi);
 
     // ---- Q^T fragments: lane group g holds d in [g*DL, (g+1)*DL) of its row
     constexpr int QV = DL * (int)sizeof(T) / 16;  // 16-byte vectors per lane per row
@@ -485,93 +446,6 @@ attn_fwd_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// KB: log-sum-exp combine of split partials ([FA-tiling] §5.1; [Occupancy]
-// "The Fix"). One 256-thread workgroup per output row:
-//   lse = M + ln sum_s exp(lse_s - M),  M = max_s lse_s
-//   O   = sum_s exp(lse_s - lse) * O_s
-// Empty splits (lse_s = -inf) carry zero weight and their O_s is never read;
-// a row whose splits are all empty gets O = 0, lse = -inf.
-// ---------------------------------------------------------------------------
-template <int D, bool OUT_BF16>
-__global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p) {
-    constexpr int C4 = D / 4;       // float4 chunks per row
-    constexpr int SG = 256 / C4;    // split groups
-    __shared__ float lse_s[256];
-    __shared__ float red[256];
-    __shared__ f32x4 acc_s[256];
-    const int tid = threadIdx.x;
-    const int row = blockIdx.x;
-    const int S = p.num_splits;
-    const size_t rows = (size_t)p.rows;
-
-    float mx = -INFINITY;
-    for (int s = tid; s < S; s += 256) {
-        const float x = p.lse_part[(size_t)s * rows + row];
-        lse_s[s] = x;
-        mx = fmaxf(mx, x);
-    }
-    red[tid] = mx;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
-    // row index (b, pos, head) -> lse index (b, head, pos)
-    const int head = row % p.Hq;
-    const int pos = (row / p.Hq) % p.Sq;
-    const int bb = row / (p.Hq * p.Sq);
-    const size_t lse_idx = ((size_t)bb * p.Hq + head) * p.Sq + pos;
-    if (M == -INFINITY) {
-        if (tid < C4) {
-            if constexpr (OUT_BF16) {
-                u32x2 z = {0u, 0u};
-                *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + 4 * tid) = z;
-            } else {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + 4 * tid) =
-                    f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        if (tid == 0 && p.lse) p.lse[lse_idx] = -INFINITY;
-        return;
-    }
-    float sm = 0.f;
-    for (int s = tid; s < S; s += 256) sm += expf(lse_s[s] - M);
-    red[tid] = sm;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    const float lse = M + logf(red[0]);
-
-    const int c4 = tid % C4, sg = tid / C4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = sg; s < S; s += SG) {
-        const float ls = lse_s[s];
-        if (ls == -INFINITY) continue;
-        const float w = expf(ls - lse);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + 4 * c4);
-        acc += w * x;
-    }
-    acc_s[tid] = acc;
-    __syncthreads();
-    if (sg == 0) {
-        for (int g = 1; g < SG; ++g) acc += acc_s[g * C4 + c4];
-        if constexpr (OUT_BF16) {
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[0], acc[1]);
-            w[1] = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + 4 * c4) = w;
-        } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + 4 * c4) = acc;
-        }
-        if (tid == 0 && p.lse) p.lse[lse_idx] = lse;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // launchers and the variant table
 // ---------------------------------------------------------------------------
 template <class T, int D, int BM, int BN, int WM, int WN>
@@ -603,17 +477,5 @@ static const FwdVariant kVariants[] = {
 };
 
 const FwdVariant* fwd_variants() { return kVariants; }
-
-hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream) {
-    dim3 grid(p.rows), block(256);
-    if (d == 128) {
-        if (out_bf16) hipLaunchKernelGGL((lse_combine_kernel<128, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((lse_combine_kernel<128, false>), grid, block, 0, stream, p);
-    } else {
-        if (out_bf16) hipLaunchKernelGGL((lse_combine_kernel<64, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((lse_combine_kernel<64, false>), grid, block, 0, stream, p);
-    }
-    return hipGetLastError();
-}
 
 }  // namespace tpa

@@ -19,8 +19,10 @@ struct FwdVariant {
     hipError_t (*launch)(const FwdParams&, dim3 grid, hipStream_t stream);
 };
 
-// All compiled variants (null-terminated by launch == nullptr).
+// Compiled variants of the general forward kernel and of the split-KV decode
+// kernel (each list null-terminated by launch == nullptr).
 const FwdVariant* fwd_variants();
+const FwdVariant* decode_variants();
 
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);

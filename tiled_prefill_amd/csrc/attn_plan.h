@@ -19,6 +19,8 @@
 
 namespace tpa {
 
+#define TPA_MAX_SPLITS 256
+
 TPA_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // floor division that is correct for negative numerators (b > 0)
 TPA_HD int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
@@ -96,6 +98,7 @@ struct FwdParams {
     int num_splits;         // grid splits (1: no split, direct output)
     int chunk_blocks;       // > 0: per-sequence split count (variable length)
     int lpt;                // reverse query-block order (heaviest causal blocks first)
+    int split_major;        // grid y = split * grid_heads + head (else head * splits + split)
 };
 
 // Arguments of the log-sum-exp combine kernel. Every split writes its lse
