@@ -164,6 +164,13 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                 break;
             }
     }
+    if (!decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
+        for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
+            if (v->dtype == p.dtype && v->d == p.d) {
+                var = v;
+                break;
+            }
+    }
     for (const FwdVariant* v = fwd_variants(); !var && v->launch; ++v) {
         if (v->dtype != p.dtype || v->d != p.d) continue;
         const bool is_decode = v->block_m <= 16;
@@ -239,10 +246,19 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     S = imax(1, imin(S, TPATTN_MAX_SPLITS));
     q.num_splits = S;
     q.chunk_blocks = chunk;
-    q.grid_x = q.num_m_blocks;
-    q.grid_y = q.grid_heads * S;
-    q.grid_z = p.B;
-    if (q.grid_y > 65535) return fail(TPATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
+    if (var->grid_1d) {
+        // one dimension over every tile, padded to a multiple of the 8 XCDs
+        const long long total = (long long)p.B * q.grid_heads * S * q.num_m_blocks;
+        if (total > 0x7fffffffLL - 8) return fail(TPATTN_EINVAL, "too many tiles");
+        q.grid_x = (int)((total + 7) / 8 * 8);
+        q.grid_y = 1;
+        q.grid_z = 1;
+    } else {
+        q.grid_x = q.num_m_blocks;
+        q.grid_y = q.grid_heads * S;
+        q.grid_z = p.B;
+        if (q.grid_y > 65535) return fail(TPATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
+    }
     q.workspace_bytes = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, p.d, S) : 0;
     out->var = var;
     return TPATTN_OK;

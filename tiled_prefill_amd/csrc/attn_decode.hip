@@ -382,9 +382,9 @@ hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
 
 const FwdVariant* decode_variants() {
     static const FwdVariant v[] = {
-        {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>},
-        {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>},
-        {0, 0, 0, 0, 0, 0, 0, nullptr},
+        {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>, 0},
+        {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>, 0},
+        {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;
 }

@@ -455,7 +455,7 @@ hipError_t launch_fwd(const FwdParams& p, dim3 grid, hipStream_t stream) {
 }
 
 #define TPA_VARIANT(T, DT, D, BM, BN, WM, WN) \
-    {DT, D, BM, BN, WM, WN, FwdTile<T, D, BM, BN, WM, WN>::LDS_BYTES, &launch_fwd<T, D, BM, BN, WM, WN>}
+    {DT, D, BM, BN, WM, WN, FwdTile<T, D, BM, BN, WM, WN>::LDS_BYTES, &launch_fwd<T, D, BM, BN, WM, WN>, 0}
 
 // Tile table for gfx950: 64-wide waves, 160 KB LDS per CU. "Decode" tiles
 // (16 rows, keys split across 4 waves) serve a handful of (packed) query rows;
@@ -473,7 +473,7 @@ static const FwdVariant kVariants[] = {
     // fp32 decode: 16 rows, 64-key tiles split over 4 waves
     TPA_VARIANT(float, DT_FP32, 128, 16, 64, 1, 4),
     TPA_VARIANT(float, DT_FP32, 64, 16, 64, 1, 4),
-    {0, 0, 0, 0, 0, 0, 0, nullptr},
+    {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
 };
 
 const FwdVariant* fwd_variants() { return kVariants; }

@@ -17,12 +17,14 @@ struct FwdVariant {
     int waves_m, waves_n;   // waves along M (rows) and along N (keys)
     int lds_bytes;
     hipError_t (*launch)(const FwdParams&, dim3 grid, hipStream_t stream);
+    int grid_1d;            // 1: one-dimensional XCD-aware grid over all tiles
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
 // kernel (each list null-terminated by launch == nullptr).
 const FwdVariant* fwd_variants();
 const FwdVariant* decode_variants();
+const FwdVariant* prefill_variants();
 
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);

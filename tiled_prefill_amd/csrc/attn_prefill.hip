@@ -1,0 +1,390 @@
+// attn_prefill.hip -- gfx950 flash-attention forward for many query rows (bf16).
+//
+// Citations:
+//   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
+//
+// One workgroup of NWV waves owns BM = NWV * MW query rows of one (batch, query
+// head[, split]) and walks its key-block range ([FA-tiling] §3) from the last
+// block to the first. Per 64-key tile:
+//   * K (bf16) streams from global memory straight into LDS (buffer_load ...
+//     lds), V is loaded into registers, converted to fp16 and written to LDS;
+//     both double-buffered, so tile n-1 loads while tile n computes, with one
+//     workgroup barrier per tile;
+//   * S^T = K Q^T on 16x16x32 bf16 MFMA (Q^T stays in registers);
+//   * online softmax in fp32 (row max over the 4 lanes of a query column with
+//     v_permlane16/32_swap); the rescale of O is skipped when no row of the wave
+//     raised its max;
+//   * O^T += V^T P^T on 16x16x32 fp16 MFMA: P is rounded to fp16 (11 significant
+//     bits: one bf16 rounding of P would cost up to 2^-9 per term) and V^T comes
+//     from ds_read_b64_tr_b16 of the row-major fp16 tile.
+// LDS rows are XOR-swizzled by 16-byte chunk so both the K fragment reads (16
+// rows, one chunk) and the V transpose reads (8 rows, two chunks) are
+// bank-conflict free.
+//
+// Grid: one dimension over all tiles. Workgroups are dealt round-robin to the 8
+// XCDs, so tile t is placed on XCD (t / per_xcd): the query blocks of one head
+// share one XCD's L2 and its K/V are fetched from HBM about once. Within a head
+// the query blocks run heaviest first ([FA-tiling] §4.4).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_device.h"
+#include "attn_kernels.h"
+#include "attn_plan.h"
+
+namespace tpa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// fp32 pair -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+// two bf16 (one 32-bit word) -> two fp16, exact for |x| <= 65504
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+constexpr int NUM_XCD = 8;
+
+template <int D, int NWV, int MW>
+struct PrefillTile {
+    static constexpr int BN = 64;              // keys per tile
+    static constexpr int BM = NWV * MW;        // query rows per workgroup
+    static constexpr int NTHR = 64 * NWV;
+    static constexpr int NQ = MW / 16;         // 16-row column blocks per wave
+    static constexpr int NT = BN / 16;         // 16-key sub-tiles
+    static constexpr int NSLAB = D / 32;       // QK contraction slabs
+    static constexpr int DT = D / 16;          // output d tiles
+    static constexpr int CPR = D / 8;          // 16-byte chunks per row
+    static constexpr int ROWB = 2 * D;         // bytes per K / V row in LDS
+    static constexpr int TILEB = BN * ROWB;    // bytes of one K (or V) tile
+    static constexpr int STAGEB = 2 * TILEB;   // K + V
+    static constexpr int LDS_BYTES = 2 * STAGEB;
+    static constexpr int KROWS_PER_DMA = 1024 / ROWB;              // rows per wave-wide DMA
+    static constexpr int KDMA = BN / KROWS_PER_DMA;                // DMA instructions per tile
+    static constexpr int KDMA_PER_WAVE = (KDMA + NWV - 1) / NWV;
+    static constexpr int VCH = BN * CPR / NTHR;                    // V chunks per thread
+    static_assert(BN * CPR % NTHR == 0, "V tile must split evenly over the threads");
+    static_assert(MW % 16 == 0, "rows per wave");
+    // chunk swizzles (see header comment)
+    static __host__ __device__ __forceinline__ int swz_k(int r) {
+        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    }
+    static __host__ __device__ __forceinline__ int swz_v(int r) {
+        return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1;
+    }
+};
+
+template <int D, int NWV, int MW>
+__global__ void __launch_bounds__(64 * NWV, 1) attn_prefill_kernel(FwdParams p) {
+    using C = PrefillTile<D, NWV, MW>;
+    constexpr int BN = C::BN, BM = C::BM, NQ = C::NQ, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
+    constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+
+    // ---- tile coordinates: XCD-aware placement, heaviest query block first
+    const int M = p.num_m_blocks, S = p.num_splits;
+    const int total = p.B * p.grid_heads * S * M;
+    const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
+    const int t = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
+    if (t >= total) return;
+    int rest = t / M;
+    const int m_rev = t % M;
+    const int m_block = p.lpt ? M - 1 - m_rev : m_rev;
+    const int split = rest % S;
+    rest /= S;
+    const int hg = rest % p.grid_heads;
+    const int b = rest / p.grid_heads;
+
+    int Skb = p.Sk;
+    if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
+    const int G = p.G;
+    const int hkv = p.pack ? hg : hg / G;
+    const int nrows = p.pack ? p.Sq * G : p.Sq;
+    const int delta = Skb - p.Sq;
+
+    int n_lo, n_hi;
+    n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, BM, BN, m_block, &n_lo, &n_hi);
+    const int S_b = splits_for(imax(0, n_hi - n_lo), S, p.chunk_blocks);
+    int s_lo = 0, s_hi = 0;
+    if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+    const bool has_work = s_hi > s_lo;
+
+    // ---- this lane's query rows and their visible key intervals
+    int row_pos[NQ], row_head[NQ], row_lo[NQ], row_hi[NQ];
+    bool row_ok[NQ];
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int r = m_block * BM + wave * MW + 16 * q + li;
+        const bool ok = r < nrows;
+        const int pos = ok ? (p.pack ? r / G : r) : 0;
+        const int head = p.pack ? hkv * G + (ok ? r % G : 0) : hg;
+        int lo = 0, hi = Skb - 1;
+        if (ok) {
+            if (p.window_left >= 0) lo = pos + delta - p.window_left;
+            if (p.causal) hi = imin(hi, pos + delta);
+            wlo = imax(wlo, lo);
+            whi = imin(whi, hi);
+        }
+        row_pos[q] = pos;
+        row_head[q] = head;
+        row_lo[q] = lo;
+        row_hi[q] = hi;
+        row_ok[q] = ok;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+
+    // ---- Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
+    u32x4 qf[NQ][NSLAB];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const bf16_t* qrow = qp + (((size_t)b * p.Sq + row_pos[q]) * p.Hq + row_head[q]) * D + 8 * lg;
+        const bool use = row_ok[q] && has_work;
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qf[q][c] = use ? x : z;
+        }
+    }
+
+    f32x4 oacc[DT][NQ];
+    float m_run[NQ], l_run[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        m_run[q] = -INFINITY;
+        l_run[q] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) oacc[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float sl2 = p.scale_log2;
+
+    // ---- K/V tile loads
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    auto tile_bytes = [&](int n) { return (uint32_t)imin(BN, Skb - n * BN) * row_bytes; };
+    // K: wave-wide DMAs into the stage's K tile; lane l of DMA i fills 16 bytes
+    // at 1024 i + 16 l, i.e. row KROWS_PER_DMA*i + l / CPR, slot l % CPR, which
+    // holds the row's chunk (slot ^ swz_k(row)).
+    auto load_k = [&](int n, int stage) {
+        const rsrc_t rk = make_rsrc(kbase + (size_t)n * BN * kv_stride, tile_bytes(n));
+        char* dst = smem + stage * STAGEB;
+#pragma unroll
+        for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
+            const int i = wave * C::KDMA_PER_WAVE + j;
+            if (C::KDMA % NWV == 0 || i < C::KDMA) {
+                const int rr = C::KROWS_PER_DMA * i + lane / CPR;
+                const int slot = lane % CPR;
+                const uint32_t voff = rr * row_bytes + 16 * (slot ^ C::swz_k(rr));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, voff, 0, 0, 0);
+            }
+        }
+    };
+    // V: each thread loads C::VCH chunks (row id / CPR, chunk id % CPR) into registers
+    u32x4 vst[C::VCH];
+    auto load_v = [&](int n) {
+        const rsrc_t rv = make_rsrc(vbase + (size_t)n * BN * kv_stride, tile_bytes(n));
+#pragma unroll
+        for (int j = 0; j < C::VCH; ++j) {
+            const int id = tid + C::NTHR * j;
+            vst[j] = buf_load16(rv, (id / CPR) * row_bytes + 16 * (id % CPR));
+        }
+    };
+    auto store_v = [&](int stage) {
+        char* dst = smem + stage * STAGEB + TILEB;
+#pragma unroll
+        for (int j = 0; j < C::VCH; ++j) {
+            const int id = tid + C::NTHR * j;
+            const int rr = id / CPR, ch = id % CPR;
+            u32x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(vst[j][e]);
+            *reinterpret_cast<u32x4*>(dst + rr * ROWB + 16 * (ch ^ C::swz_v(rr))) = h;
+        }
+    };
+
+    if (has_work) {
+        load_k(s_hi - 1, 0);
+        load_v(s_hi - 1);
+        store_v(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K DMA has landed
+    }
+    __syncthreads();
+
+    int stage = 0;
+    for (int n = s_hi - 1; n >= s_lo; --n) {
+        const bool more = n > s_lo;
+        if (more) {  // prefetch the next (lower) tile into the other stage
+            load_k(n - 1, stage ^ 1);
+            load_v(n - 1);
+        }
+        const char* kt = smem + stage * STAGEB;
+        const char* vt = kt + TILEB;
+
+        // S^T = K . Q^T
+        f32x4 sacc[NT][NQ];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) sacc[tt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int rr = 16 * tt + li;
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + rr * ROWB + 16 * ((4 * c + lg) ^ C::swz_k(rr)));
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) sacc[tt][q] = mfma_bf16(kf, qf[q][c], sacc[tt][q]);
+            }
+        }
+
+        const int key0 = n * BN;
+        if (!(key0 >= wlo && key0 + BN - 1 <= whi)) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = key0 + 16 * tt + 4 * lg + e;
+                        if (key < row_lo[q] || key > row_hi[q]) sacc[tt][q][e] = -INFINITY;
+                    }
+        }
+
+        // online softmax
+        bool raised = false;
+        float alpha[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[tt][q][e]);
+            mx = xor_max(mx);
+            const float m_new = fmaxf(m_run[q], mx);
+            raised |= m_new > m_run[q];
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            alpha[q] = fast_exp2((m_run[q] - m_use) * sl2);
+            const float neg = -m_use * sl2;
+            float rs = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pv = fast_exp2(fmaf(sacc[tt][q][e], sl2, neg));
+                    sacc[tt][q][e] = pv;
+                    rs += pv;
+                }
+            l_run[q] = l_run[q] * alpha[q] + rs;
+            m_run[q] = m_new;
+        }
+        // rescale O only if some row of this wave raised its running max
+        if (__builtin_amdgcn_ballot_w64(raised) != 0) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int u = 0; u < DT; ++u) oacc[u][q] *= alpha[q];
+        }
+
+        // O^T += V^T . P^T (fp16)
+#pragma unroll
+        for (int pp = 0; pp < NT / 2; ++pp) {
+            u32x4 pf[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                pf[q][0] = pack_f16x2(sacc[2 * pp][q][0], sacc[2 * pp][q][1]);
+                pf[q][1] = pack_f16x2(sacc[2 * pp][q][2], sacc[2 * pp][q][3]);
+                pf[q][2] = pack_f16x2(sacc[2 * pp + 1][q][0], sacc[2 * pp + 1][q][1]);
+                pf[q][3] = pack_f16x2(sacc[2 * pp + 1][q][2], sacc[2 * pp + 1][q][3]);
+            }
+            const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
+            const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                const int ch = 2 * u + cb;
+                const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + ra * ROWB + 16 * (ch ^ C::swz_v(ra)) + hb));
+                const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
+                const u32x4 vf = {a[0], a[1], c[0], c[1]};
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f16(vf, pf[q], oacc[u][q]);
+            }
+        }
+
+        if (more) {
+            store_v(stage ^ 1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K DMAs landed
+        }
+        __syncthreads();
+        stage ^= 1;
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) l_run[q] = xor_sum(l_run[q]);
+    const bool split_out = S > 1;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        if (!row_ok[q]) continue;
+        const float l = l_run[q];
+        const bool any = l > 0.f;
+        const float inv = any ? 1.f / l : 0.f;
+        const float lse = any ? m_run[q] * p.scale + logf(l) : -INFINITY;
+        const size_t row = ((size_t)b * p.Sq + row_pos[q]) * p.Hq + row_head[q];
+        if (split_out) {
+            const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
+            if (lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+            if (any) {
+                float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4*>(orow + 16 * u) = oacc[u][q] * inv;
+            }
+        } else {
+            if (lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + row_head[q]) * p.Sq + row_pos[q]] = lse;
+            bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * D + 4 * lg;
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[u][q][0] * inv, oacc[u][q][1] * inv);
+                w[1] = pack_bf16x2(oacc[u][q][2] * inv, oacc[u][q][3] * inv);
+                *reinterpret_cast<u32x2*>(orow + 16 * u) = w;
+            }
+        }
+    }
+}
+
+template <int D, int NWV, int MW>
+hipError_t launch_prefill(const FwdParams& p, dim3 grid, hipStream_t stream) {
+    // grid: one dimension over every tile, padded to a multiple of the XCD count
+    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW>), grid, dim3(64 * NWV), 0, stream, p);
+    return hipGetLastError();
+}
+
+const FwdVariant* prefill_variants() {
+    static const FwdVariant v[] = {
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32>, 1},
+        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32>, 1},
+        {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
+    };
+    return v;
+}
+
+}  // namespace tpa
