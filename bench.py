@@ -64,6 +64,22 @@ def traffic_for(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def warm(step, n_steps, min_seconds=0.3):
+    """Untimed warmup: n_steps steps, then more until min_seconds of GPU work have
+    run, so that the GPU clocks have settled before the timed region."""
+    import torch
+    i = 0
+    for i in range(n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(8):
+            i += 1
+            step(i)
+        torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -108,9 +124,7 @@ def main():
         def step(i):
             tpa.fwd(q, ks[i % n_rot], vs[i % n_rot], causal=False, out=o, lse=lse)
 
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
+        warm(step, args.warmup)
         t0 = time.perf_counter()
         for i in range(args.steps):
             step(i)
@@ -140,12 +154,10 @@ def main():
         o = torch.empty_like(q)
         lse = torch.empty((wp.B, wp.Hq, wp.Sq), dtype=torch.float32, device=dev)
 
-        def pstep():
+        def pstep(i=0):
             tpa.fwd(q, k, v, causal=True, out=o, lse=lse)
 
-        for _ in range(3):
-            pstep()
-        torch.cuda.synchronize()
+        warm(pstep, args.warmup)
         t0 = time.perf_counter()
         for _ in range(args.prefill_steps):
             pstep()

@@ -165,8 +165,11 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             }
     }
     if (!decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
+        // TPATTN_PREFILL_WAVES selects the workgroup size (ablation; default 8:
+        // one 256-row workgroup per CU measured faster than two 128-row ones)
+        const int want = env_int("TPATTN_PREFILL_WAVES", 8);
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d) {
+            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want) {
                 var = v;
                 break;
             }

@@ -12,8 +12,10 @@
 //     workgroup barrier per tile;
 //   * S^T = K Q^T on 16x16x32 bf16 MFMA (Q^T stays in registers);
 //   * online softmax in fp32 (row max over the 4 lanes of a query column with
-//     v_permlane16/32_swap); the rescale of O is skipped when no row of the wave
-//     raised its max;
+//     v_permlane16/32_swap) with a lazily moved reference max: O is rescaled
+//     only when a score exceeds the reference by more than 2^8, which after the
+//     first tile of a row almost never happens; the row sums of P come from an
+//     extra MFMA with an all-ones operand instead of VALU adds;
 //   * O^T += V^T P^T on 16x16x32 fp16 MFMA: P is rounded to fp16 (11 significant
 //     bits: one bf16 rounding of P would cost up to 2^-9 per term) and V^T comes
 //     from ds_read_b64_tr_b16 of the row-major fp16 tile.
@@ -85,7 +87,7 @@ struct PrefillTile {
 };
 
 template <int D, int NWV, int MW>
-__global__ void __launch_bounds__(64 * NWV, 1) attn_prefill_kernel(FwdParams p) {
+__global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdParams p) {
     using C = PrefillTile<D, NWV, MW>;
     constexpr int BN = C::BN, BM = C::BM, NQ = C::NQ, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
     constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
@@ -163,16 +165,24 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_prefill_kernel(FwdParams p) 
         }
     }
 
-    f32x4 oacc[DT][NQ];
-    float m_run[NQ], l_run[NQ];
+    // O^T accumulators, and the row sums of P computed on the matrix core: an
+    // all-ones A operand turns the PV MFMA into sum_j P[j][i] for every lane of
+    // query column i, which also keeps l consistent with the fp16-rounded P.
+    f32x4 oacc[DT][NQ], lacc[NQ];
+    float m_run[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         m_run[q] = -INFINITY;
-        l_run[q] = 0.f;
+        lacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < DT; ++u) oacc[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     const float sl2 = p.scale_log2;
+    // Lazy max: the reference max of a row moves only when a new score exceeds
+    // it by more than 2^LAZY (log2 units), so P <= 2^LAZY stays well inside fp16
+    // and the O rescale (and its exponential) is skipped on most tiles.
+    constexpr float LAZY = 8.f;
 
     // ---- K/V tile loads
     const size_t kv_stride = (size_t)p.Hkv * D;
@@ -269,40 +279,44 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_prefill_kernel(FwdParams p) 
                     }
         }
 
-        // online softmax
-        bool raised = false;
-        float alpha[NQ];
+        // online softmax with a lazily moved reference max
+        bool raise[NQ];
+        bool any_raise = false;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             float mx = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[tt][q][e]);
+                mx = fmaxf(fmaxf(mx, fmaxf(sacc[tt][q][0], sacc[tt][q][1])),
+                           fmaxf(sacc[tt][q][2], sacc[tt][q][3]));
             mx = xor_max(mx);
-            const float m_new = fmaxf(m_run[q], mx);
-            raised |= m_new > m_run[q];
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            alpha[q] = fast_exp2((m_run[q] - m_use) * sl2);
-            const float neg = -m_use * sl2;
-            float rs = 0.f;
+            raise[q] = m_run[q] == -INFINITY ? mx != -INFINITY : (mx - m_run[q]) * sl2 > LAZY;
+            any_raise |= raise[q];
+        }
+        if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {  // rare after the first tile
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                if (!raise[q]) continue;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[tt][q][e]);
+                mx = xor_max(mx);
+                const float alpha = m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mx) * sl2);
+                m_run[q] = mx;
+                lacc[q] *= alpha;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) oacc[u][q] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const float neg = m_run[q] == -INFINITY ? 0.f : -m_run[q] * sl2;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pv = fast_exp2(fmaf(sacc[tt][q][e], sl2, neg));
-                    sacc[tt][q][e] = pv;
-                    rs += pv;
-                }
-            l_run[q] = l_run[q] * alpha[q] + rs;
-            m_run[q] = m_new;
-        }
-        // rescale O only if some row of this wave raised its running max
-        if (__builtin_amdgcn_ballot_w64(raised) != 0) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                for (int u = 0; u < DT; ++u) oacc[u][q] *= alpha[q];
+                for (int e = 0; e < 4; ++e) sacc[tt][q][e] = fast_exp2(fmaf(sacc[tt][q][e], sl2, neg));
         }
 
         // O^T += V^T . P^T (fp16)
@@ -318,6 +332,8 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_prefill_kernel(FwdParams p) 
             }
             const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
             const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) lacc[q] = mfma_f16(ones, pf[q], lacc[q]);
 #pragma unroll
             for (int u = 0; u < DT; ++u) {
                 const int ch = 2 * u + cb;
@@ -338,13 +354,11 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_prefill_kernel(FwdParams p) 
     }
 
     // ---- epilogue
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) l_run[q] = xor_sum(l_run[q]);
     const bool split_out = S > 1;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         if (!row_ok[q]) continue;
-        const float l = l_run[q];
+        const float l = lacc[q][0];
         const bool any = l > 0.f;
         const float inv = any ? 1.f / l : 0.f;
         const float lse = any ? m_run[q] * p.scale + logf(l) : -INFINITY;
@@ -380,8 +394,12 @@ hipError_t launch_prefill(const FwdParams& p, dim3 grid, hipStream_t stream) {
 
 const FwdVariant* prefill_variants() {
     static const FwdVariant v[] = {
+        // one 8-wave workgroup per CU: K/V tiles shared by 256 rows
         {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32>, 1},
         {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32>, 1},
+        // two 4-wave workgroups per CU (independent barriers), kept as an ablation
+        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32>, 1},
+        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32>, 1},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;
