@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run one leg only (for profiling)")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every workload (one JSON line each) instead of the headline line")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first copy a buffer of this many MiB three times (a plain copy "
                          "of known size, to calibrate HBM byte counters)")
@@ -80,6 +82,92 @@ def warm(step, n_steps, min_seconds=0.3):
         torch.cuda.synchronize()
 
 
+def visible_pairs(w, seqlens=None):
+    """Visible (query, key) pairs of workload w: sum over rows of the key interval
+    length (bottom-right aligned causal / window mask)."""
+    total = 0
+    for b in range(w.B):
+        skb = int(seqlens[b]) if seqlens is not None else w.Sk
+        delta = skb - w.Sq
+        for i in range(w.Sq):
+            hi = min(skb - 1, i + delta) if w.causal else skb - 1
+            lo = max(0, i + delta - w.window_left) if w.window_left >= 0 else 0
+            total += max(0, hi - lo + 1)
+    return total * w.Hq
+
+
+def visible_kv_rows(w, seqlens=None):
+    """Key rows some query row of a (batch, KV head) can see, summed over batches."""
+    total = 0
+    for b in range(w.B):
+        skb = int(seqlens[b]) if seqlens is not None else w.Sk
+        delta = skb - w.Sq
+        hi = min(skb - 1, w.Sq - 1 + delta) if w.causal else skb - 1
+        lo = max(0, delta - w.window_left) if w.window_left >= 0 else 0
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def run_suite(args):
+    import torch
+    import tiled_prefill_amd as tpa
+    from workloads import WORKLOADS, make_inputs
+    dev = "cuda:0"
+    for name, w in WORKLOADS.items():
+        q, k, v, seqlens = make_inputs(w, seed=0, device=dev)
+        esz = 4 if w.dtype == "fp32" else 2
+        sl = seqlens.cpu() if seqlens is not None else None
+        kv_bytes = 2 * visible_kv_rows(w, sl) * w.Hkv * w.d * esz
+        flops = 4.0 * w.d * visible_pairs(w, sl)
+        memory_bound = w.Sq * (w.Hq // w.Hkv) <= 32
+        n_rot = max(1, min(16, math.ceil(2 * LLC_BYTES / max(1, 2 * w.B * w.Sk * w.Hkv * w.d * esz)))) \
+            if memory_bound else 1
+        ks = [k] + [k.clone() for _ in range(n_rot - 1)]
+        vs = [v] + [v.clone() for _ in range(n_rot - 1)]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+        total_k = int(seqlens.sum()) if seqlens is not None else -1
+
+        def step(i):
+            if seqlens is not None:
+                tpa.fwd_varlen(q, ks[i % n_rot], vs[i % n_rot], seqlens, causal=w.causal,
+                               window_left=w.window_left, sum_seqlens_k=total_k, out=o, lse=lse)
+            else:
+                tpa.fwd(q, ks[i % n_rot], vs[i % n_rot], causal=w.causal,
+                        window_left=w.window_left, out=o, lse=lse)
+
+        warm(step, 10)
+        t0 = time.perf_counter()
+        step(0)
+        torch.cuda.synchronize()
+        one = time.perf_counter() - t0
+        steps = max(5, min(2000, int(0.3 / max(one, 1e-6))))
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        tpa.profile_begin(2 * steps + 8)
+        for i in range(steps):
+            step(i)
+        prof = tpa.profile_end()
+        plan = tpa.plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, dtype=w.dtype,
+                        varlen=w.varlen, sum_seqlens_k=total_k)
+        rec = {"workload": name, "dtype": w.dtype, "ms_per_step": round(ms, 5),
+               "kv_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+               "pct_hbm": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+               "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+               "fwd_us": round(1e3 * prof["fwd_ms"] / max(1, prof["fwd_launches"]), 2),
+               "combine_us": round(1e3 * prof["combine_ms"] / max(1, prof["combine_launches"]), 2),
+               "num_splits": plan["num_splits"], "pack_gqa": plan["pack_gqa"],
+               "block_m": plan["block_m"], "block_n": plan["block_n"], "kv_copies": n_rot,
+               "kv_bytes": kv_bytes, "flops": flops, "steps": steps}
+        if w.dtype == "bf16" and not memory_bound:
+            rec["pct_mfma_bf16"] = round(100 * rec["TFLOPs"] / BF16_PEAK_TFLOPS, 2)
+        print(json.dumps(rec), flush=True)
+        del ks, vs, q, k, v, o
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -95,6 +183,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     tpa.load()
+    if args.suite:
+        run_suite(args)
+        return
     dev = "cuda:0"
     torch.cuda.set_device(0)
     out = {}

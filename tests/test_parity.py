@@ -265,3 +265,27 @@ def test_prefill_full_sampled(name):
     rows = sorted({0, 1, 15, 16, 63, 64, 127, 128, 129, 1000, 1023, 1024, 1025, 2047, 2048,
                    S // 2 + 7, S - 129, S - 128, S - 65, S - 2, S - 1})
     _sampled_rows_check(w, q, k, v, o, lse, rows)
+
+
+# ---------------------------------------------------------------------------
+# every kernel path a planner switch can select (ablations included)
+# ---------------------------------------------------------------------------
+ABLATIONS = [
+    {"TPATTN_PREFILL_SKIP": "1"},             # prefill with raised wave priority
+    {"TPATTN_PREFILL_SKIP": "2"},             # software-pipelined prefill
+    {"TPATTN_PREFILL_WAVES": "4"},            # two 4-wave workgroups per CU
+    {"TPATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
+    {"TPATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
+    {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
+    {"TPATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
+    {"TPATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order
+]
+
+
+@pytest.mark.parametrize("env", ABLATIONS, ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
+def test_ablation_paths(env, monkeypatch):
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    for case in [("bf16", 1, 8, 2, 300, 300, 128, True, 40, 0), ("bf16", 2, 16, 2, 200, 333, 64, True, -1, 0),
+                 ("bf16", 1, 32, 4, 1, 3000, 128, False, -1, 0), ("bf16", 1, 4, 4, 130, 520, 128, False, -1, 0)]:
+        run_case(*case, seed=12)

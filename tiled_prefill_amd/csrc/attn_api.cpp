@@ -168,8 +168,9 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         // TPATTN_PREFILL_WAVES selects the workgroup size (ablation; default 8:
         // one 256-row workgroup per CU measured faster than two 128-row ones)
         const int want = env_int("TPATTN_PREFILL_WAVES", 8);
+        int skip = env_int("TPATTN_PREFILL_SKIP", 0);  // ablation: take a later match
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want) {
+            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && skip-- <= 0) {
                 var = v;
                 break;
             }

@@ -86,8 +86,9 @@ struct PrefillTile {
     }
 };
 
-template <int D, int NWV, int MW>
-__global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdParams p) {
+template <int D, int NWV, int MW, int PRI>
+__global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_kernel(FwdParams p) {
+    constexpr bool PRIO = PRI != 0;
     using C = PrefillTile<D, NWV, MW>;
     constexpr int BN = C::BN, BM = C::BM, NQ = C::NQ, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
     constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
@@ -249,7 +250,9 @@ __global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdPara
         const char* kt = smem + stage * STAGEB;
         const char* vt = kt + TILEB;
 
-        // S^T = K . Q^T
+        // S^T = K . Q^T (raised wave priority while feeding the matrix core, so the
+        // partner wave on the SIMD runs its VALU work in the gaps)
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
         f32x4 sacc[NT][NQ];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
@@ -266,6 +269,7 @@ __global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdPara
             }
         }
 
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
         const int key0 = n * BN;
         if (!(key0 >= wlo && key0 + BN - 1 <= whi)) {
 #pragma unroll
@@ -320,6 +324,7 @@ __global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdPara
         }
 
         // O^T += V^T . P^T (fp16)
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int pp = 0; pp < NT / 2; ++pp) {
             u32x4 pf[NQ];
@@ -345,6 +350,7 @@ __global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdPara
             }
         }
 
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
         if (more) {
             store_v(stage ^ 1);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K DMAs landed
@@ -385,21 +391,347 @@ __global__ void __launch_bounds__(64 * NWV, 8 / NWV) attn_prefill_kernel(FwdPara
     }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined variant: within every wave, the QK MFMAs of tile n-1 are
+// issued before the softmax of tile n (two score buffers), so the matrix core
+// works on the next tile while the VALU exponentiates the current one; the
+// exponentials of the second key half overlap the first half's PV MFMAs.
+// K runs one tile ahead of V: K tiles j and j-1 and V tiles j and j-1 occupy
+// the two K and two V buffers, still one workgroup barrier per tile.
+// ---------------------------------------------------------------------------
 template <int D, int NWV, int MW>
+__global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_pipe_kernel(FwdParams p) {
+    using C = PrefillTile<D, NWV, MW>;
+    constexpr int BN = C::BN, BM = C::BM, NQ = C::NQ, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
+    constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB;
+    // LDS: K buffers 0,1 then V buffers 0,1
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+
+    const int M = p.num_m_blocks, S = p.num_splits;
+    const int total = p.B * p.grid_heads * S * M;
+    const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
+    const int t = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
+    if (t >= total) return;
+    int rest = t / M;
+    const int m_rev = t % M;
+    const int m_block = p.lpt ? M - 1 - m_rev : m_rev;
+    const int split = rest % S;
+    rest /= S;
+    const int hg = rest % p.grid_heads;
+    const int b = rest / p.grid_heads;
+
+    int Skb = p.Sk;
+    if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
+    const int G = p.G;
+    const int hkv = p.pack ? hg : hg / G;
+    const int nrows = p.pack ? p.Sq * G : p.Sq;
+    const int delta = Skb - p.Sq;
+
+    int n_lo, n_hi;
+    n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, BM, BN, m_block, &n_lo, &n_hi);
+    const int S_b = splits_for(imax(0, n_hi - n_lo), S, p.chunk_blocks);
+    int s_lo = 0, s_hi = 0;
+    if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+    const bool has_work = s_hi > s_lo;
+
+    int row_pos[NQ], row_head[NQ], row_lo[NQ], row_hi[NQ];
+    bool row_ok[NQ];
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int r = m_block * BM + wave * MW + 16 * q + li;
+        const bool ok = r < nrows;
+        const int pos = ok ? (p.pack ? r / G : r) : 0;
+        const int head = p.pack ? hkv * G + (ok ? r % G : 0) : hg;
+        int lo = 0, hi = Skb - 1;
+        if (ok) {
+            if (p.window_left >= 0) lo = pos + delta - p.window_left;
+            if (p.causal) hi = imin(hi, pos + delta);
+            wlo = imax(wlo, lo);
+            whi = imin(whi, hi);
+        }
+        row_pos[q] = pos;
+        row_head[q] = head;
+        row_lo[q] = lo;
+        row_hi[q] = hi;
+        row_ok[q] = ok;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
+    u32x4 qf[NQ][NSLAB];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const bf16_t* qrow = qp + (((size_t)b * p.Sq + row_pos[q]) * p.Hq + row_head[q]) * D + 8 * lg;
+        const bool use = row_ok[q] && has_work;
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qf[q][c] = use ? x : z;
+        }
+    }
+
+    f32x4 oacc[DT][NQ], lacc[NQ];
+    float m_run[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        m_run[q] = -INFINITY;
+        lacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < DT; ++u) oacc[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+    const float sl2 = p.scale_log2;
+    constexpr float LAZY = 8.f;
+
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    auto tile_bytes = [&](int n) { return (uint32_t)imin(BN, Skb - n * BN) * row_bytes; };
+    auto kbuf = [&](int n) { return smem + (n & 1) * TILEB; };
+    auto vbuf = [&](int n) { return smem + 2 * TILEB + (n & 1) * TILEB; };
+    auto load_k = [&](int n) {
+        const rsrc_t rk = make_rsrc(kbase + (size_t)n * BN * kv_stride, tile_bytes(n));
+        char* dst = kbuf(n);
+#pragma unroll
+        for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
+            const int i = wave * C::KDMA_PER_WAVE + j;
+            if (C::KDMA % NWV == 0 || i < C::KDMA) {
+                const int rr = C::KROWS_PER_DMA * i + lane / CPR;
+                const int slot = lane % CPR;
+                const uint32_t voff = rr * row_bytes + 16 * (slot ^ C::swz_k(rr));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, voff, 0, 0, 0);
+            }
+        }
+    };
+    u32x4 vst[C::VCH];
+    auto load_v = [&](int n) {
+        const rsrc_t rv = make_rsrc(vbase + (size_t)n * BN * kv_stride, tile_bytes(n));
+#pragma unroll
+        for (int j = 0; j < C::VCH; ++j) {
+            const int id = tid + C::NTHR * j;
+            vst[j] = buf_load16(rv, (id / CPR) * row_bytes + 16 * (id % CPR));
+        }
+    };
+    auto store_v = [&](int n) {
+        char* dst = vbuf(n);
+#pragma unroll
+        for (int j = 0; j < C::VCH; ++j) {
+            const int id = tid + C::NTHR * j;
+            const int rr = id / CPR, ch = id % CPR;
+            u32x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(vst[j][e]);
+            *reinterpret_cast<u32x4*>(dst + rr * ROWB + 16 * (ch ^ C::swz_v(rr))) = h;
+        }
+    };
+    auto qk = [&](int n, f32x4 (&sacc)[NT][NQ]) {
+        const char* kt = kbuf(n);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) sacc[tt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int rr = 16 * tt + li;
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + rr * ROWB + 16 * ((4 * c + lg) ^ C::swz_k(rr)));
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) sacc[tt][q] = mfma_bf16(kf, qf[q][c], sacc[tt][q]);
+            }
+        }
+    };
+
+    f32x4 sa[NT][NQ], sb[NT][NQ];
+
+    // softmax bookkeeping for the scores of tile n held in sa: optional element
+    // mask, row max, lazy rescale of O (rare, branchy, before the main block)
+    auto prologue_softmax = [&](int n, bool masked, float (&neg)[NQ]) {
+        if (masked) {
+            const int key0 = n * BN;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = key0 + 16 * tt + 4 * lg + e;
+                        if (key < row_lo[q] || key > row_hi[q]) sa[tt][q][e] = -INFINITY;
+                    }
+        }
+        bool raise[NQ];
+        bool any_raise = false;
+        float mxs[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                mx = fmaxf(fmaxf(mx, fmaxf(sa[tt][q][0], sa[tt][q][1])), fmaxf(sa[tt][q][2], sa[tt][q][3]));
+            mx = xor_max(mx);
+            mxs[q] = mx;
+            raise[q] = m_run[q] == -INFINITY ? mx != -INFINITY : (mx - m_run[q]) * sl2 > LAZY;
+            any_raise |= raise[q];
+        }
+        if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                if (!raise[q]) continue;
+                const float alpha = m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mxs[q]) * sl2);
+                m_run[q] = mxs[q];
+                lacc[q] *= alpha;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) oacc[u][q] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) neg[q] = m_run[q] == -INFINITY ? 0.f : -m_run[q] * sl2;
+    };
+    // exponentials of one 32-key half of sa, packed to fp16 B operands
+    auto exp_half = [&](int pp, const float (&neg)[NQ], u32x4 (&pf)[NQ]) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int tt = 2 * pp + h;
+                const float p0 = fast_exp2(fmaf(sa[tt][q][0], sl2, neg[q]));
+                const float p1 = fast_exp2(fmaf(sa[tt][q][1], sl2, neg[q]));
+                const float p2 = fast_exp2(fmaf(sa[tt][q][2], sl2, neg[q]));
+                const float p3 = fast_exp2(fmaf(sa[tt][q][3], sl2, neg[q]));
+                pf[q][2 * h] = pack_f16x2(p0, p1);
+                pf[q][2 * h + 1] = pack_f16x2(p2, p3);
+            }
+    };
+    auto pv_half = [&](int n, int pp, const u32x4 (&pf)[NQ]) {
+        const char* vt = vbuf(n);
+        const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
+        const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) lacc[q] = mfma_f16(ones, pf[q], lacc[q]);
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+            const int ch = 2 * u + cb;
+            const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + ra * ROWB + 16 * (ch ^ C::swz_v(ra)) + hb));
+            const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
+            const u32x4 vf = {a[0], a[1], c[0], c[1]};
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f16(vf, pf[q], oacc[u][q]);
+        }
+    };
+    auto needs_mask = [&](int n) {
+        const int key0 = n * BN;
+        return !(key0 >= wlo && key0 + BN - 1 <= whi);
+    };
+
+    int n = s_hi - 1;
+    if (has_work) {
+        load_k(n);
+        load_v(n);
+        if (n - 1 >= s_lo) load_k(n - 1);
+        store_v(n);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __syncthreads();
+    if (has_work) qk(n, sa);
+    __syncthreads();  // every wave has read K(n) before its buffer is reused
+
+    // steady state: tiles n > s_lo (each has a next tile n - 1)
+    for (; n > s_lo; --n) {
+        float neg[NQ];
+        prologue_softmax(n, needs_mask(n), neg);
+        if (n - 2 >= s_lo) load_k(n - 2);
+        load_v(n - 1);
+        // one straight-line block: QK(n-1) | exp(n, first half) | PV(n) | exp(n, second half)
+        u32x4 pf0[NQ], pf1[NQ];
+        qk(n - 1, sb);
+        exp_half(0, neg, pf0);
+        pv_half(n, 0, pf0);
+        exp_half(1, neg, pf1);
+        pv_half(n, 1, pf1);
+        store_v(n - 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K DMA landed
+        __syncthreads();
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) sa[tt][q] = sb[tt][q];
+    }
+    // last tile (no next)
+    if (has_work) {
+        float neg[NQ];
+        prologue_softmax(n, needs_mask(n), neg);
+        u32x4 pf0[NQ], pf1[NQ];
+        exp_half(0, neg, pf0);
+        pv_half(n, 0, pf0);
+        exp_half(1, neg, pf1);
+        pv_half(n, 1, pf1);
+    }
+
+    const bool split_out = S > 1;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        if (!row_ok[q]) continue;
+        const float l = lacc[q][0];
+        const bool any = l > 0.f;
+        const float inv = any ? 1.f / l : 0.f;
+        const float lse = any ? m_run[q] * p.scale + logf(l) : -INFINITY;
+        const size_t row = ((size_t)b * p.Sq + row_pos[q]) * p.Hq + row_head[q];
+        if (split_out) {
+            const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
+            if (lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+            if (any) {
+                float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4*>(orow + 16 * u) = oacc[u][q] * inv;
+            }
+        } else {
+            if (lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + row_head[q]) * p.Sq + row_pos[q]] = lse;
+            bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * D + 4 * lg;
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[u][q][0] * inv, oacc[u][q][1] * inv);
+                w[1] = pack_bf16x2(oacc[u][q][2] * inv, oacc[u][q][3] * inv);
+                *reinterpret_cast<u32x2*>(orow + 16 * u) = w;
+            }
+        }
+    }
+}
+
+template <int D, int NWV, int MW>
+hipError_t launch_prefill_pipe(const FwdParams& p, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_prefill_pipe_kernel<D, NWV, MW>), grid, dim3(64 * NWV), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int NWV, int MW, int PRI = 1>
 hipError_t launch_prefill(const FwdParams& p, dim3 grid, hipStream_t stream) {
     // grid: one dimension over every tile, padded to a multiple of the XCD count
-    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW>), grid, dim3(64 * NWV), 0, stream, p);
+    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW, PRI>), grid, dim3(64 * NWV), 0, stream, p);
     return hipGetLastError();
 }
 
 const FwdVariant* prefill_variants() {
     static const FwdVariant v[] = {
         // one 8-wave workgroup per CU: K/V tiles shared by 256 rows
-        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32>, 1},
-        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32>, 1},
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 0>, 1},
+        // ablations: raised wave priority around the MFMA phases (measured slower),
+        // and the software-pipelined loop (QK of tile n-1 overlaps softmax of n;
+        // measured slower: both waves of a SIMD then compete in every phase)
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 1>, 1},
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill_pipe<128, 8, 32>, 1},
+        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32, 0>, 1},
         // two 4-wave workgroups per CU (independent barriers), kept as an ablation
-        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32>, 1},
-        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32>, 1},
+        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0>, 1},
+        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0>, 1},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;
