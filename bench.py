@@ -27,8 +27,10 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20       # MI355X Infinity Cache
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "tiled_prefill_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "tiled_prefill_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# kernel -> source file it is compiled from
+KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_prefill_kernel": "attn_prefill.hip"}
 
 
 def parse():
@@ -50,18 +52,20 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def source_hash(kernel: str) -> str:
+    path = os.path.join(CSRC, KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str):
-    """Counter-derived HBM bytes per launch, if recorded for the current kernel source."""
+    """Counter-derived HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated),
+    if they were recorded for the current source of that kernel; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     e = rec.get(f"{kernel}:{workload}")
-    if not e or e.get("kernel_sha") != kernel_hash():
+    if not e or e.get("source_sha") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -231,7 +235,7 @@ def main():
         fwd_ms = prof["fwd_ms"] / max(1, prof["fwd_launches"])
         comb_ms = prof["combine_ms"] / max(1, prof["combine_launches"])
         achieved = (kv_bytes + q_bytes) / (fwd_ms * 1e-3) / 1e9
-        traffic = traffic_for("attn_fwd_kernel", w.name)
+        traffic = traffic_for("attn_decode_kernel", w.name)
         out["decode"] = dict(value=value, ms_per_step=ms, fwd_ms=fwd_ms, combine_ms=comb_ms,
                              achieved=achieved, traffic=traffic, n_rot=n_rot)
         del ks, vs, q, k, v
@@ -319,7 +323,7 @@ def main():
     }
     if dec:
         line["pct_of_hbm_peak"] = round(100 * dec["value"] / HBM_PEAK_GBS, 2)
-        line["roofline"] = {"bound": "hbm", "kernel": "attn_fwd_kernel (decode tile)",
+        line["roofline"] = {"bound": "hbm", "kernel": "attn_decode_kernel<128, 4>",
                             "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": dec["traffic"],
@@ -332,10 +336,11 @@ def main():
             "pct_of_mfma_peak": round(100 * pre["value"] / BF16_PEAK_TFLOPS, 2),
             "config": {"workload": "causal_prefill_bf16: B=1 H=32 S=8192 d=128, causal, "
                                    "visible pairs only", "flops_per_step": flops},
-            "roofline": {"bound": "mfma", "achieved": round(pre["achieved"], 2),
+            "roofline": {"bound": "mfma", "kernel": "attn_prefill_kernel<128, 8, 32, 0>",
+                         "achieved": round(pre["achieved"], 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["achieved"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": traffic_for("attn_fwd_kernel", wp.name),
+                         "traffic": traffic_for("attn_prefill_kernel", wp.name),
                          "avg_launch_ms": round(pre["fwd_ms"], 4)},
         }
     line["cpu_baseline"] = cpu

@@ -145,15 +145,19 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale_log2;
 
+    // s_waitcnt encodings: vmcnt(NVL) (K landed, V's NVL DMAs may be in flight)
+    // and vmcnt(0); expcnt and lgkmcnt left at their maximum
+    constexpr int WAIT_K = (NVL & 15) | ((NVL >> 4) << 14) | 0x0F70;
+    constexpr int NKL = NT * NSLAB;  // K loads per block
+    constexpr int WAIT_KN = (NKL & 15) | ((NKL >> 4) << 14) | 0x0F70;
     int n = s_lo + wave;
     if (n < s_hi) {
+        load_k(n);  // K first: QK and the softmax can run while V still streams in
         load_v(n);
-        load_k(n);
     }
     for (; n < s_hi; n += NW) {
         const bool more = n + NW < s_hi;
-        // wait for this block's K (registers) and V (LDS, written by the DMA)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(WAIT_K);
 
         // S^T = K . Q^T for the 64 keys of the block
         f32x4 sacc[NT];
@@ -201,7 +205,10 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
 #pragma unroll
         for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
 
-        // O^T += V^T . P^T with P as bf16 hi + lo parts
+        // O^T += V^T . P^T with P as bf16 hi + lo parts. Outstanding loads, in
+        // issue order: V(n), then K(n + NW) when there is a next block.
+        if (more) __builtin_amdgcn_s_waitcnt(WAIT_KN);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
         for (int pp = 0; pp < NT / 2; ++pp) {
             const u32x2 s0 = split_bf16x2(sacc[2 * pp][0], sacc[2 * pp][1]);
@@ -296,18 +303,56 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
 // Log-sum-exp combine of split partials ([FA-tiling] §5.1; [Occupancy] "The
 // Fix"): per output row, lse = M + ln sum_s exp(lse_s - M) with M = max_s lse_s,
 // O = sum_s exp(lse_s - lse) O_s. A workgroup owns one row and a 32-wide slice
-// of d: 8 lanes per float4 column x 32 split groups. The partial-output loads
-// are issued before the lse reductions so their latency overlaps. Empty splits
-// (lse_s = -inf) carry zero weight and their O_s is never used; a row whose
-// splits are all empty gets O = 0, lse = -inf.
+// of d: lane c4 = tid % 8 owns a float4 column, split group sg = tid / 8 owns
+// splits sg, sg + 32, .... Every load is issued first; each thread merges its
+// splits in registers, then the (max, sum, weighted O) states are merged across
+// the 8 split groups of a wave with DPP / lane swaps and across the 4 waves with
+// one LDS exchange. Empty splits (lse_s = -inf) carry zero weight and their O_s
+// is never used; a row whose splits are all empty gets O = 0, lse = -inf.
 // ---------------------------------------------------------------------------
+struct LseState {
+    float m, l;
+    f32x4 acc;
+};
+// merge of two partial states (both may be empty: m = -inf)
+__device__ __forceinline__ LseState lse_merge(const LseState& a, const LseState& b) {
+    const float m = fmaxf(a.m, b.m);
+    const float wa = a.m == -INFINITY ? 0.f : __expf(a.m - m);
+    const float wb = b.m == -INFINITY ? 0.f : __expf(b.m - m);
+    return LseState{m, a.l * wa + b.l * wb, a.acc * wa + b.acc * wb};
+}
+template <int CTRL>
+__device__ __forceinline__ LseState lse_dpp(const LseState& x) {
+    LseState y;
+    y.m = dpp<CTRL>(x.m);
+    y.l = dpp<CTRL>(x.l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y.acc[e] = dpp<CTRL>(x.acc[e]);
+    return y;
+}
+__device__ __forceinline__ float swap16(float x) {  // value of lane l ^ 16
+    auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    return (__lane_id() & 16) ? u2f(r[0]) : u2f(r[1]);
+}
+__device__ __forceinline__ float swap32(float x) {  // value of lane l ^ 32
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return (__lane_id() & 32) ? u2f(r[0]) : u2f(r[1]);
+}
+__device__ __forceinline__ LseState lse_swap(const LseState& x, bool by32) {
+    LseState y;
+    y.m = by32 ? swap32(x.m) : swap16(x.m);
+    y.l = by32 ? swap32(x.l) : swap16(x.l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y.acc[e] = by32 ? swap32(x.acc[e]) : swap16(x.acc[e]);
+    return y;
+}
+
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D) {
     constexpr int SG = 32;                   // split groups
     constexpr int MAXI = TPA_MAX_SPLITS / SG;
-    __shared__ float lse_s[TPA_MAX_SPLITS];
-    __shared__ float wred[2][4];
-    __shared__ f32x4 acc_s[32];
+    __shared__ float red_m[4][8], red_l[4][8];
+    __shared__ f32x4 red_a[4][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = blockIdx.x;
     const int d0 = 32 * blockIdx.y;
@@ -316,61 +361,60 @@ __global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D
     const size_t rows = (size_t)p.rows;
 
     f32x4 ov[MAXI];
+    float ls[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
         const int s = sg + SG * i;
-        if (s < S)
+        ls[i] = -INFINITY;
+        if (s < S) {
+            ls[i] = p.lse_part[(size_t)s * rows + row];
             ov[i] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + d0 + 4 * c4);
+        }
     }
-    const float x = tid < S ? p.lse_part[(size_t)tid * rows + row] : -INFINITY;
-    if (tid < S) lse_s[tid] = x;
-    const float mx = wave_max(x);
-    if (lane == 0) wred[0][wave] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
-    const float sm = wave_sum((tid < S && M != -INFINITY) ? expf(x - M) : 0.f);
-    if (lane == 0) wred[1][wave] = sm;
-    __syncthreads();
-    const float lse = M == -INFINITY ? -INFINITY : M + logf(wred[1][0] + wred[1][1] + wred[1][2] + wred[1][3]);
-
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
+    // this thread's splits
+    LseState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) st.m = fmaxf(st.m, ls[i]);
+    if (st.m != -INFINITY) {
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
-            const int s = sg + SG * i;
-            if (s < S) {
-                const float ls = lse_s[s];
-                if (ls != -INFINITY) acc += expf(ls - lse) * ov[i];
-            }
+            if (ls[i] == -INFINITY) continue;
+            const float w = __expf(ls[i] - st.m);
+            st.l += w;
+            st.acc += w * ov[i];
         }
     }
-    // reduce over the 8 split groups of each wave (lanes c4, c4+8, ..., c4+56):
-    // row_mirror pairs lane 8 + j with 7 - j, so pre-permute with the half mirror
-    // to line up equal c4 before it; then the two lane-bit swaps
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float a = acc[e];
-        a += dpp<DPP_MIRROR>(dpp<DPP_HALF_MIRROR>(a));
-        acc[e] = xor_sum(a);
+    // merge the 8 split groups of the wave (lanes c4 + 8k): partner l ^ 8 is
+    // row_mirror(half_mirror(.)), then the lane-bit swaps for l ^ 16 and l ^ 32
+    st = lse_merge(st, lse_dpp<DPP_MIRROR>(lse_dpp<DPP_HALF_MIRROR>(st)));
+    st = lse_merge(st, lse_swap(st, false));
+    st = lse_merge(st, lse_swap(st, true));
+    if (lane < 8) {
+        red_m[wave][lane] = st.m;
+        red_l[wave][lane] = st.l;
+        red_a[wave][lane] = st.acc;
     }
-    if (lane < 8) acc_s[wave * 8 + lane] = acc;
     __syncthreads();
-    if (tid < 8) {
-        acc = acc_s[tid] + acc_s[8 + tid] + acc_s[16 + tid] + acc_s[24 + tid];
-        if constexpr (OUT_BF16) {
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[0], acc[1]);
-            w[1] = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + d0 + 4 * tid) = w;
-        } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + d0 + 4 * tid) = acc;
-        }
-        if (tid == 0 && blockIdx.y == 0 && p.lse) {
-            const int h = row % p.Hq;
-            const int pos = (row / p.Hq) % p.Sq;
-            const int bb = row / (p.Hq * p.Sq);
-            p.lse[((size_t)bb * p.Hq + h) * p.Sq + pos] = lse;
-        }
+    if (tid >= 8) return;
+    LseState t{red_m[0][tid], red_l[0][tid], red_a[0][tid]};
+#pragma unroll
+    for (int w = 1; w < 4; ++w) t = lse_merge(t, LseState{red_m[w][tid], red_l[w][tid], red_a[w][tid]});
+    const bool any = t.m != -INFINITY && t.l > 0.f;
+    const float inv = any ? 1.f / t.l : 0.f;
+    const f32x4 o = t.acc * inv;
+    if constexpr (OUT_BF16) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + d0 + 4 * tid) = w;
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + d0 + 4 * tid) = o;
+    }
+    if (tid == 0 && blockIdx.y == 0 && p.lse) {
+        const int h = row % p.Hq;
+        const int pos = (row / p.Hq) % p.Sq;
+        const int bb = row / (p.Hq * p.Sq);
+        p.lse[((size_t)bb * p.Hq + h) * p.Sq + pos] = any ? t.m + logf(t.l) : -INFINITY;
     }
 }
 
