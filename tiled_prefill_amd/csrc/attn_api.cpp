@@ -165,9 +165,12 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             }
     }
     if (!decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
-        // TPATTN_PREFILL_WAVES selects the workgroup size (ablation; default 8:
-        // one 256-row workgroup per CU measured faster than two 128-row ones)
-        const int want = env_int("TPATTN_PREFILL_WAVES", 8);
+        // Tile rows ([FA-tiling] §2.5: smaller blocks where masking cuts tiles):
+        // 256-row workgroups (8 waves) for full and causal masks, 128 rows (4
+        // waves) with a sliding window, where a 256-row tile spends ~20% of its
+        // work on masked corners for window 1024 (measured 599 vs 698 TFLOP/s).
+        // TPATTN_PREFILL_WAVES overrides (ablation).
+        const int want = env_int("TPATTN_PREFILL_WAVES", p.window_left >= 0 ? 4 : 8);
         int skip = env_int("TPATTN_PREFILL_SKIP", 0);  // ablation: take a later match
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
             if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && skip-- <= 0) {
