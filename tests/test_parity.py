@@ -273,7 +273,8 @@ def test_prefill_full_sampled(name):
 ABLATIONS = [
     {"TPATTN_PREFILL_SKIP": "1"},             # prefill with raised wave priority
     {"TPATTN_PREFILL_SKIP": "2"},             # software-pipelined prefill
-    {"TPATTN_PREFILL_WAVES": "4"},            # two 4-wave workgroups per CU
+    {"TPATTN_PREFILL_WAVES": "4"},            # 128-row tiles (default with a window)
+    {"TPATTN_PREFILL_WAVES": "8"},            # 256-row tiles (default without one)
     {"TPATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
     {"TPATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
     {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
