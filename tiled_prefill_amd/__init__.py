@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtpattn.so")
+# TPATTN_LIB may name another build of the same library (same ABI), e.g. one
+# compiled with different flags, to compare two builds in one process tree.
+LIB_PATH = os.environ.get("TPATTN_LIB") or os.path.join(_PKG, "libtpattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "tpattn.h")
 
 FP32, BF16 = 0, 1

@@ -185,9 +185,9 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[t][e]);
+            for (int e = 0; e < 4; ++e) mx = vmax(mx, sacc[t][e]);
         mx = xor_max(mx);
-        const float m_new = fmaxf(m_run, mx);
+        const float m_new = vmax(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2((m_run - m_use) * sl2);
         const float neg = -m_use * sl2;
@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         mw[w] = red_ml[(w * 2 + 0) * 64 + lane];
-        mstar = fmaxf(mstar, mw[w]);
+        mstar = vmax(mstar, mw[w]);
     }
     const float muse = mstar == -INFINITY ? 0.f : mstar;
     float l = 0.f;
@@ -316,7 +316,7 @@ struct LseState {
 };
 // merge of two partial states (both may be empty: m = -inf)
 __device__ __forceinline__ LseState lse_merge(const LseState& a, const LseState& b) {
-    const float m = fmaxf(a.m, b.m);
+    const float m = vmax(a.m, b.m);
     const float wa = a.m == -INFINITY ? 0.f : __expf(a.m - m);
     const float wb = b.m == -INFINITY ? 0.f : __expf(b.m - m);
     return LseState{m, a.l * wa + b.l * wb, a.acc * wa + b.acc * wb};
@@ -374,7 +374,7 @@ __global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D
     // this thread's splits
     LseState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) st.m = fmaxf(st.m, ls[i]);
+    for (int i = 0; i < MAXI; ++i) st.m = vmax(st.m, ls[i]);
     if (st.m != -INFINITY) {
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {

@@ -50,6 +50,12 @@ __device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
 // that lane bit. DPP quad_perm / row_half_mirror / row_mirror pair lanes inside
 // quads, half-rows and rows of 16.
 __device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
+
+// NaN-propagating maximum. fmaxf must quiet signalling NaNs, so the compiler puts
+// a canonicalising v_max_f32 x, x in front of every operand it cannot prove
+// canonical (MFMA results, lane moves); this form needs none, and a chain
+// max(max(m, a), b) folds into one v_maximum3_f32.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float u2f(uint32_t x) { return __uint_as_float(x); }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -63,11 +69,11 @@ constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_HALF_MIRROR = 0x14
 
 __device__ __forceinline__ float max16(float x) {  // max over lanes l, l ^ 16
     auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(r[0]), u2f(r[1]));
+    return vmax(u2f(r[0]), u2f(r[1]));
 }
 __device__ __forceinline__ float max32(float x) {  // max over lanes l, l ^ 32
     auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(r[0]), u2f(r[1]));
+    return vmax(u2f(r[0]), u2f(r[1]));
 }
 __device__ __forceinline__ float sum16(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
@@ -84,10 +90,10 @@ __device__ __forceinline__ float xor_sum(float x) { return sum32(sum16(x)); }
 
 // Reductions over the 16 lanes of a row (lanes with equal l / 16).
 __device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp<DPP_QUAD_1032>(x));
-    x = fmaxf(x, dpp<DPP_QUAD_2301>(x));
-    x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
-    return fmaxf(x, dpp<DPP_MIRROR>(x));
+    x = vmax(x, dpp<DPP_QUAD_1032>(x));
+    x = vmax(x, dpp<DPP_QUAD_2301>(x));
+    x = vmax(x, dpp<DPP_HALF_MIRROR>(x));
+    return vmax(x, dpp<DPP_MIRROR>(x));
 }
 __device__ __forceinline__ float row16_sum(float x) {
     x += dpp<DPP_QUAD_1032>(x);

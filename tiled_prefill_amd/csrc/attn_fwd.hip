@@ -277,9 +277,9 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[t][q][r]);
+                for (int r = 0; r < 4; ++r) mx = vmax(mx, sacc[t][q][r]);
             mx = xor_max(mx);
-            const float m_new = fmaxf(m_run[q], mx);
+            const float m_new = vmax(m_run[q], mx);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2((m_run[q] - m_use) * sl2);
             const float neg = -m_use * sl2;
@@ -380,7 +380,7 @@ attn_fwd_kernel(FwdParams p) {
                 const int ww = w * WM + wm;
                 mw[w] = red_ml[((ww * NQ + q) * 2 + 0) * 64 + lane];
                 lw[w] = red_ml[((ww * NQ + q) * 2 + 1) * 64 + lane];
-                mstar = fmaxf(mstar, mw[w]);
+                mstar = vmax(mstar, mw[w]);
             }
             const float muse = mstar == -INFINITY ? 0.f : mstar;
             float l = 0.f;

@@ -291,8 +291,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             float mx = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
-                mx = fmaxf(fmaxf(mx, fmaxf(sacc[tt][q][0], sacc[tt][q][1])),
-                           fmaxf(sacc[tt][q][2], sacc[tt][q][3]));
+                mx = vmax(vmax(vmax(vmax(mx, sacc[tt][q][0]), sacc[tt][q][1]), sacc[tt][q][2]), sacc[tt][q][3]);
             mx = xor_max(mx);
             raise[q] = m_run[q] == -INFINITY ? mx != -INFINITY : (mx - m_run[q]) * sl2 > LAZY;
             any_raise |= raise[q];
@@ -305,7 +304,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[tt][q][e]);
+                    for (int e = 0; e < 4; ++e) mx = vmax(mx, sacc[tt][q][e]);
                 mx = xor_max(mx);
                 const float alpha = m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mx) * sl2);
                 m_run[q] = mx;
@@ -575,7 +574,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             float mx = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
-                mx = fmaxf(fmaxf(mx, fmaxf(sa[tt][q][0], sa[tt][q][1])), fmaxf(sa[tt][q][2], sa[tt][q][3]));
+                mx = vmax(vmax(vmax(vmax(mx, sa[tt][q][0]), sa[tt][q][1]), sa[tt][q][2]), sa[tt][q][3]);
             mx = xor_max(mx);
             mxs[q] = mx;
             raise[q] = m_run[q] == -INFINITY ? mx != -INFINITY : (mx - m_run[q]) * sl2 > LAZY;
