@@ -152,12 +152,14 @@ int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_
                                 int min_chunk_rows, int wg_per_cu);
 
 /* Kernel timing for measurement tools: while enabled, every launch of the
- * forward and combine kernels is bracketed by HIP events on its stream.
+ * forward kernel, the combine kernel and the V pre-pass (bf16 prefill kernels
+ * that read V as fp16 V^T) is bracketed by HIP events on its stream.
  * tpattn_profile_end synchronises those events and returns the summed
- * durations (ms) and launch counts, then disables recording. */
+ * durations (ms) and launch counts per kind (any output pointer may be null),
+ * then disables recording. */
 int tpattn_profile_begin(int max_launches);
 int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
-                       int* combine_launches);
+                       int* combine_launches, double* prep_ms, int* prep_launches);
 
 /* Message of the last failure on this thread ("" if none). */
 const char* tpattn_last_error(void);

@@ -84,7 +84,7 @@ def load():
     lib.tpattn_profile_begin.argtypes = [i]
     lib.tpattn_profile_begin.restype = i
     dp = ctypes.POINTER(ctypes.c_double)
-    lib.tpattn_profile_end.argtypes = [dp, ip, dp, ip]
+    lib.tpattn_profile_end.argtypes = [dp, ip, dp, ip, dp, ip]
     lib.tpattn_profile_end.restype = i
     lib.tpattn_last_error.argtypes = []
     lib.tpattn_last_error.restype = ctypes.c_char_p
@@ -239,9 +239,10 @@ def profile_begin(max_launches: int = 4096):
 
 
 def profile_end() -> dict:
-    f_ms, c_ms = ctypes.c_double(), ctypes.c_double()
-    f_n, c_n = ctypes.c_int(), ctypes.c_int()
+    f_ms, c_ms, p_ms = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    f_n, c_n, p_n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(load().tpattn_profile_end(ctypes.byref(f_ms), ctypes.byref(f_n), ctypes.byref(c_ms),
-                                     ctypes.byref(c_n)))
+                                     ctypes.byref(c_n), ctypes.byref(p_ms), ctypes.byref(p_n)))
     return {"fwd_ms": f_ms.value, "fwd_launches": f_n.value,
-            "combine_ms": c_ms.value, "combine_launches": c_n.value}
+            "combine_ms": c_ms.value, "combine_launches": c_n.value,
+            "prep_ms": p_ms.value, "prep_launches": p_n.value}

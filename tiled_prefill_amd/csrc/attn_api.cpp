@@ -144,6 +144,8 @@ int check_problem(const Problem& p) {
 struct Plan {
     tpattn_plan pub;
     const FwdVariant* var;
+    size_t vt_offset = 0;  // byte offset of the V pre-pass output in the workspace
+    int skp = 0;           // its key pitch
 };
 
 int make_plan(const Problem& p, int num_cus, Plan* out) {
@@ -171,9 +173,12 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         // work on masked corners for window 1024 (measured 599 vs 698 TFLOP/s).
         // TPATTN_PREFILL_WAVES overrides (ablation).
         const int want = env_int("TPATTN_PREFILL_WAVES", p.window_left >= 0 ? 4 : 8);
+        // kernel family: 1 = 32x32x16 MFMA kernel on fp16 V^T (V pre-pass), 0 = 16x16x32
+        const int want_vt = env_int("TPATTN_PREFILL_VT", 0);
         int skip = env_int("TPATTN_PREFILL_SKIP", 0);  // ablation: take a later match
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && skip-- <= 0) {
+            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && (want_vt ? v->needs_vt == want_vt : v->needs_vt == 0) &&
+                skip-- <= 0) {
                 var = v;
                 break;
             }
@@ -266,7 +271,14 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         q.grid_z = p.B;
         if (q.grid_y > 65535) return fail(TPATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
     }
-    q.workspace_bytes = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, p.d, S) : 0;
+    // workspace: split partials, then (kernels that read it) the fp16 V^T of the
+    // V pre-pass, 256-byte aligned
+    size_t ws = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, p.d, S) : 0;
+    out->vt_offset = (ws + 255) & ~(size_t)255;
+    out->skp = ceil_div(imax(p.Sk, 0), 64) * 64;
+    if (var->needs_vt && p.Sk > 0)
+        ws = out->vt_offset + (size_t)p.B * p.Hkv * p.d * (size_t)out->skp * 2;
+    q.workspace_bytes = ws;
     out->var = var;
     return TPATTN_OK;
 }
@@ -286,7 +298,7 @@ struct Profiler {
     bool on = false;
     int max_launches = 0;
     std::vector<hipEvent_t> ev;  // pairs
-    std::vector<int> kind;       // 0 forward, 1 combine
+    std::vector<int> kind;       // 0 forward, 1 combine, 2 V pre-pass
     int used = 0;
 } g_prof;
 
@@ -345,8 +357,10 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     // dispatched together, so concurrent reads cover whole interleaved KV rows
     fp.split_major = env_int("TPATTN_SPLIT_MAJOR", plan.var->block_m <= 16 ? 1 : 0);
 
+    fp.d_head = pr.d;
+    fp.skp = plan.skp;
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
-    if (pl.num_splits == 1) {
+    if (pl.workspace_bytes == 0) {
         const int slot = prof_start(0, stream);
         hipError_t e = plan.var->launch(fp, grid, stream);
         prof_stop(slot, stream);
@@ -377,11 +391,22 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     const size_t rows = (size_t)pr.B * pr.Sq * pr.Hq;
     fp.o_part = reinterpret_cast<float*>(ws.ptr);
     fp.lse_part = fp.o_part + (size_t)pl.num_splits * rows * pr.d;
+    hipError_t e;
+    int slot;
+    if (plan.var->needs_vt) {
+        fp.vt = static_cast<char*>(ws.ptr) + plan.vt_offset;
+        fp.vt_blk = plan.var->needs_vt;
+        slot = prof_start(2, stream);
+        e = launch_v_to_f16t(fp, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "V pre-pass launch: %s", hipGetErrorString(e));
+    }
 
-    int slot = prof_start(0, stream);
-    hipError_t e = plan.var->launch(fp, grid, stream);
+    slot = prof_start(0, stream);
+    e = plan.var->launch(fp, grid, stream);
     prof_stop(slot, stream);
     if (e != hipSuccess) return fail(TPATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
+    if (pl.num_splits == 1) return TPATTN_OK;
 
     CombineParams cp{};
     cp.o_part = fp.o_part;
@@ -512,10 +537,10 @@ int tpattn_profile_begin(int max_launches) {
 }
 
 int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
-                       int* combine_launches) {
+                       int* combine_launches, double* prep_ms, int* prep_launches) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    double t[2] = {0, 0};
-    int n[2] = {0, 0};
+    double t[3] = {0, 0, 0};
+    int n[3] = {0, 0, 0};
     for (int i = 0; i < g_prof.used; ++i) {
         if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) continue;
         float ms = 0.f;
@@ -533,6 +558,8 @@ int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
     if (fwd_launches) *fwd_launches = n[0];
     if (combine_ms) *combine_ms = t[1];
     if (combine_launches) *combine_launches = n[1];
+    if (prep_ms) *prep_ms = t[2];
+    if (prep_launches) *prep_launches = n[2];
     return TPATTN_OK;
 }
 

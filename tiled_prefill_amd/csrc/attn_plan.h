@@ -99,6 +99,10 @@ struct FwdParams {
     int chunk_blocks;       // > 0: per-sequence split count (variable length)
     int lpt;                // reverse query-block order (heaviest causal blocks first)
     int split_major;        // grid y = split * grid_heads + head (else head * splits + split)
+    const void* vt;         // fp16 V^T written by the V pre-pass (kernels that take it), else null
+    int skp;                // key pitch of vt (Sk rounded up to 64)
+    int d_head;             // head dim (for launchers that dispatch on it)
+    int vt_blk;             // key-permutation block of vt (16 or 32; see the V pre-pass)
 };
 
 // Arguments of the log-sum-exp combine kernel. Every split writes its lse
