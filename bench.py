@@ -46,6 +46,7 @@ def parse():
                     help="run one leg only (for profiling)")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload (one JSON line each) instead of the headline line")
+    ap.add_argument("--workload", default=None, help="with --suite: time only this workload")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first copy a buffer of this many MiB three times (a plain copy "
                          "of known size, to calibrate HBM byte counters)")
@@ -118,6 +119,8 @@ def run_suite(args):
     from workloads import WORKLOADS, make_inputs
     dev = "cuda:0"
     for name, w in WORKLOADS.items():
+        if args.workload and name != args.workload:
+            continue
         q, k, v, seqlens = make_inputs(w, seed=0, device=dev)
         esz = 4 if w.dtype == "fp32" else 2
         sl = seqlens.cpu() if seqlens is not None else None

@@ -275,6 +275,8 @@ ABLATIONS = [
     {"TPATTN_PREFILL_SKIP": "2"},             # software-pipelined prefill
     {"TPATTN_PREFILL_WAVES": "4"},            # 128-row tiles (default with a window)
     {"TPATTN_PREFILL_WAVES": "8"},            # 256-row tiles (default without one)
+    {"TPATTN_PREFILL_PERSIST": "1"},          # persistent workgroups, per-XCD tile queues
+    {"TPATTN_PREFILL_PERSIST": "1", "TPATTN_PREFILL_WAVES": "8"},
     {"TPATTN_PREFILL_VT": "16"},              # 32x32 MFMA kernel on fp16 V^T
     {"TPATTN_PREFILL_VT": "16", "TPATTN_PREFILL_WAVES": "8"},
     {"TPATTN_PREFILL_VT": "16", "TPATTN_PREFILL_WAVES": "4"},

@@ -138,3 +138,20 @@ def test_causal_visited_blocks_about_half():
     p = _plan("causal_prefill_bf16", num_splits=1)
     dense = p["num_m_blocks"] * (8192 // p["block_n"]) * 32
     assert 0.5 < p["visited_blocks"] / dense < 0.52
+
+
+def test_persistent_grid_is_resident_workgroups(monkeypatch):
+    """Persistent prefill: one workgroup per resident slot (8-wave: 1 per CU, 4-wave: 2), a
+    multiple of the 8 XCDs, never more than the tiles; the workspace holds the 8 queue counters."""
+    monkeypatch.setenv("TPATTN_PREFILL_PERSIST", "1")
+    p = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
+    assert p["block_m"] == 256 and p["grid_x"] == 256
+    assert p["workspace_bytes"] >= 8 * 4
+    p = tpa.plan(4, 32, 8, 4096, 4096, 128, causal=True, window_left=1024, num_cus=256)
+    assert p["block_m"] == 128 and p["grid_x"] == 512
+    p = tpa.plan(1, 2, 2, 300, 300, 128, causal=True, num_cus=256)  # few tiles: all of them, rounded to 8
+    tiles = p["grid_heads"] * p["num_m_blocks"] * p["num_splits"]
+    assert tiles < 256 and p["grid_x"] == -(-tiles // 8) * 8
+    monkeypatch.setenv("TPATTN_PREFILL_PERSIST", "0")
+    p = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
+    assert p["grid_x"] == 1024 and p["workspace_bytes"] == 0

@@ -14,6 +14,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -145,6 +146,7 @@ struct Plan {
     tpattn_plan pub;
     const FwdVariant* var;
     size_t vt_offset = 0;  // byte offset of the V pre-pass output in the workspace
+    size_t ctr_offset = 0; // byte offset of the persistent kernels' tile counters
     int skp = 0;           // its key pitch
 };
 
@@ -175,9 +177,11 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         const int want = env_int("TPATTN_PREFILL_WAVES", p.window_left >= 0 ? 4 : 8);
         // kernel family: 1 = 32x32x16 MFMA kernel on fp16 V^T (V pre-pass), 0 = 16x16x32
         const int want_vt = env_int("TPATTN_PREFILL_VT", 0);
+        // 1 = persistent workgroups over per-XCD tile queues
+        const int want_persist = env_int("TPATTN_PREFILL_PERSIST", 0) ? 1 : 0;
         int skip = env_int("TPATTN_PREFILL_SKIP", 0);  // ablation: take a later match
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && (want_vt ? v->needs_vt == want_vt : v->needs_vt == 0) &&
+            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && (want_vt ? v->needs_vt == want_vt : v->needs_vt == 0) && (v->persistent > 0) == (want_persist > 0) &&
                 skip-- <= 0) {
                 var = v;
                 break;
@@ -259,10 +263,13 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     q.num_splits = S;
     q.chunk_blocks = chunk;
     if (var->grid_1d) {
-        // one dimension over every tile, padded to a multiple of the 8 XCDs
+        // one dimension over every tile (persistent kernels: over the resident
+        // workgroups), padded to a multiple of the 8 XCDs
         const long long total = (long long)p.B * q.grid_heads * S * q.num_m_blocks;
         if (total > 0x7fffffffLL - 8) return fail(TPATTN_EINVAL, "too many tiles");
-        q.grid_x = (int)((total + 7) / 8 * 8);
+        long long launch = total;
+        if (var->persistent > 0) launch = std::min<long long>(total, (long long)num_cus * var->persistent);
+        q.grid_x = (int)((launch + 7) / 8 * 8);
         q.grid_y = 1;
         q.grid_z = 1;
     } else {
@@ -278,6 +285,8 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     out->skp = ceil_div(imax(p.Sk, 0), 64) * 64;
     if (var->needs_vt && p.Sk > 0)
         ws = out->vt_offset + (size_t)p.B * p.Hkv * p.d * (size_t)out->skp * 2;
+    out->ctr_offset = (ws + 255) & ~(size_t)255;
+    if (var->persistent > 0) ws = out->ctr_offset + 256;  // one tile counter per XCD
     q.workspace_bytes = ws;
     out->var = var;
     return TPATTN_OK;
@@ -400,6 +409,14 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         e = launch_v_to_f16t(fp, stream);
         prof_stop(slot, stream);
         if (e != hipSuccess) return fail(TPATTN_EHIP, "V pre-pass launch: %s", hipGetErrorString(e));
+    }
+
+    if (plan.var->persistent > 0) {
+        fp.tile_counters = reinterpret_cast<int*>(static_cast<char*>(ws.ptr) + plan.ctr_offset);
+        slot = prof_start(2, stream);
+        e = launch_tile_counters_reset(fp.tile_counters, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "tile counter reset: %s", hipGetErrorString(e));
     }
 
     slot = prof_start(0, stream);

@@ -20,6 +20,7 @@ struct FwdVariant {
     int grid_1d;            // 1: one-dimensional XCD-aware grid over all tiles
     int needs_vt;           // > 0: reads V as fp16 V^T from the V pre-pass (FwdParams::vt),
                             // keys permuted in blocks of this many (16 or 32)
+    int persistent;         // > 0: persistent workgroups (this many per CU) over tile queues
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
@@ -30,6 +31,9 @@ const FwdVariant* prefill_variants();
 
 // The V pre-pass: V (bf16) -> fp16 V^T in FwdParams::vt (pitch FwdParams::skp).
 hipError_t launch_v_to_f16t(const FwdParams& p, hipStream_t stream);
+
+// Zeroes the per-XCD tile queue counters of a persistent kernel.
+hipError_t launch_tile_counters_reset(int* counters, hipStream_t stream);
 
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);

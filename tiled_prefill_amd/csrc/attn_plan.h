@@ -103,6 +103,7 @@ struct FwdParams {
     int skp;                // key pitch of vt (Sk rounded up to 64)
     int d_head;             // head dim (for launchers that dispatch on it)
     int vt_blk;             // key-permutation block of vt (16 or 32; see the V pre-pass)
+    int* tile_counters;     // persistent kernels: one tile queue counter per XCD, zero at launch
 };
 
 // Arguments of the log-sum-exp combine kernel. Every split writes its lse

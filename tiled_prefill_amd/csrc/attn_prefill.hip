@@ -88,7 +88,7 @@ struct PrefillTile {
     }
 };
 
-template <int D, int NWV, int MW, int PRI>
+template <int D, int NWV, int MW, int PRI, int PERSIST = 0>
 __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_kernel(FwdParams p) {
     constexpr bool PRIO = PRI != 0;
     using C = PrefillTile<D, NWV, MW>;
@@ -99,12 +99,12 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
 
-    // ---- tile coordinates: XCD-aware placement, heaviest query block first
+    // ---- tiles: t in [0, total) ordered (batch, head, split, query block heaviest
+    // first); XCD x owns the section [x per_xcd, (x + 1) per_xcd)
     const int M = p.num_m_blocks, S = p.num_splits;
     const int total = p.B * p.grid_heads * S * M;
     const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
-    const int t = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
-    if (t >= total) return;
+    auto run_tile = [&](const int t) {
     int rest = t / M;
     const int m_rev = t % M;
     const int m_block = p.lpt ? M - 1 - m_rev : m_rev;
@@ -390,7 +390,48 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             }
         }
     }
+    };
+
+    if constexpr (PERSIST == 0) {
+        // one tile per workgroup; workgroups are dealt round-robin to the 8 XCDs,
+        // so tile t of section blockIdx % 8 lands on that XCD
+        const int t = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
+        if (t < total) run_tile(t);
+    } else {
+        // persistent: each workgroup pops tiles from its own XCD's queue (an
+        // atomic counter per section, zeroed before the launch), then from the
+        // other queues once its own is empty; every workgroup leaves when all
+        // eight are exhausted. (Measured slower than the dealt grid above on the
+        // causal and windowed prefills: the dispatcher already balances these
+        // tiles, and each pop adds an atomic's latency; popping during a tile
+        // instead breaks the heaviest-first balance.)
+        __shared__ int s_next;
+        const int xcd = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (NUM_XCD - 1);  // HW_REG_XCC_ID
+        int qi = 0;  // queues tried so far (thread 0)
+        while (true) {
+            if (tid == 0) {
+                int next = -1;
+                for (; qi < NUM_XCD; ++qi) {
+                    const int x = (xcd + qi) & (NUM_XCD - 1);
+                    const int size = imin(per_xcd, total - x * per_xcd);
+                    if (size <= 0) continue;
+                    const int i = atomicAdd(p.tile_counters + x, 1);
+                    if (i < size) {
+                        next = x * per_xcd + i;
+                        break;
+                    }
+                }
+                s_next = next;
+            }
+            __syncthreads();
+            const int t = s_next;
+            __syncthreads();  // all waves have read s_next before thread 0 overwrites it
+            if (t < 0) break;
+            run_tile(t);
+        }
+    }
 }
+
 
 // ---------------------------------------------------------------------------
 // Software-pipelined variant: within every wave, the QK MFMAs of tile n-1 are
@@ -1058,6 +1099,14 @@ hipError_t launch_prefill_m32(const FwdParams& p, dim3 grid, hipStream_t stream)
     return hipGetLastError();
 }
 
+__global__ void tile_counters_reset_kernel(int* c, int n) {
+    if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+}
+hipError_t launch_tile_counters_reset(int* counters, hipStream_t stream) {
+    hipLaunchKernelGGL(tile_counters_reset_kernel, dim3(1), dim3(64), 0, stream, counters, NUM_XCD);
+    return hipGetLastError();
+}
+
 hipError_t launch_v_to_f16t(const FwdParams& p, hipStream_t stream) {
     const dim3 grid(p.skp / 64, p.Hkv, p.B);
     const bf16_t* v = reinterpret_cast<const bf16_t*>(p.v);
@@ -1078,10 +1127,11 @@ hipError_t launch_prefill_pipe(const FwdParams& p, dim3 grid, hipStream_t stream
     return hipGetLastError();
 }
 
-template <int D, int NWV, int MW, int PRI = 1>
+template <int D, int NWV, int MW, int PRI = 1, int PERSIST = 0>
 hipError_t launch_prefill(const FwdParams& p, dim3 grid, hipStream_t stream) {
-    // grid: one dimension over every tile, padded to a multiple of the XCD count
-    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW, PRI>), grid, dim3(64 * NWV), 0, stream, p);
+    // grid: one dimension over every tile (persistent: over the resident
+    // workgroups), padded to a multiple of the XCD count
+    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW, PRI, PERSIST>), grid, dim3(64 * NWV), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1098,6 +1148,11 @@ const FwdVariant* prefill_variants() {
         // two 4-wave workgroups per CU (independent barriers), kept as an ablation
         {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0>, 1},
         {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0>, 1},
+        // persistent workgroups with per-XCD tile queues
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 0, 1>, 1, 0, 1},
+        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0, 1>, 1, 0, 2},
+        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32, 0, 1>, 1, 0, 1},
+        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0, 1>, 1, 0, 2},
         // 32x32x16 MFMA kernel on fp16 V^T from the V pre-pass
         {DT_BF16, 128, 256, 64, 8, 1, M32Tile<128, 8>::LDS_BYTES, &launch_prefill_m32<128, 8>, 1, 16},
         {DT_BF16, 128, 128, 64, 4, 1, M32Tile<128, 4>::LDS_BYTES, &launch_prefill_m32<128, 4>, 1, 16},
