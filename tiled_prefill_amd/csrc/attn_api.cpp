@@ -187,14 +187,20 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                 break;
             }
     }
-    for (const FwdVariant* v = fwd_variants(); !var && v->launch; ++v) {
-        if (v->dtype != p.dtype || v->d != p.d) continue;
-        const bool is_decode = v->block_m <= 16;
-        if (is_decode == decode) {
-            var = v;
-            break;
+    // general tile kernel: decode tiles (16 rows) for decode, 32-row tiles when a
+    // KV head's query rows (packed) are at most 32, else the widest row tile
+    const int head_rows = G > 1 ? p.Sq * G : p.Sq;
+    const int want_bm = decode ? 16 : (head_rows <= 32 && env_int("TPATTN_VERIFY_TILE", 1) ? 32 : 0);
+    for (int pass = 0; pass < 2 && !var; ++pass)
+        for (const FwdVariant* v = fwd_variants(); v->launch; ++v) {
+            if (v->dtype != p.dtype || v->d != p.d) continue;
+            const bool ok = pass == 0 ? (want_bm ? v->block_m == want_bm : v->block_m > 32)
+                                      : (decode ? v->block_m <= 16 : v->block_m > 16);
+            if (ok) {
+                var = v;
+                break;
+            }
         }
-    }
     if (!var) return fail(TPATTN_EUNSUPPORTED, "no kernel variant for dtype %d d %d", p.dtype, p.d);
     const int BM = var->block_m, BN = var->block_n;
     bool pack = false;

@@ -470,6 +470,10 @@ static const FwdVariant kVariants[] = {
     // fp32 prefill: 64 rows (4 waves x 16), 32-key tiles
     TPA_VARIANT(float, DT_FP32, 128, 64, 32, 4, 1),
     TPA_VARIANT(float, DT_FP32, 64, 64, 64, 4, 1),
+    // fp32 "verify" tiles for 17..32 rows: 2 waves x 16 rows, keys split over 2 waves
+    // (a 64-row tile would leave half its waves on padding rows)
+    TPA_VARIANT(float, DT_FP32, 128, 32, 64, 2, 2),
+    TPA_VARIANT(float, DT_FP32, 64, 32, 64, 2, 2),
     // fp32 decode: 16 rows, 64-key tiles split over 4 waves
     TPA_VARIANT(float, DT_FP32, 128, 16, 64, 1, 4),
     TPA_VARIANT(float, DT_FP32, 64, 16, 64, 1, 4),
