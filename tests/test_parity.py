@@ -282,6 +282,7 @@ ABLATIONS = [
     {"TPATTN_PREFILL_VT": "16", "TPATTN_PREFILL_WAVES": "4"},
     {"TPATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
     {"TPATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
+    {"TPATTN_DECODE_WAVES": "8"},             # 8-wave decode workgroups
     {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
     {"TPATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
     {"TPATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order

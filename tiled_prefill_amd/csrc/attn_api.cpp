@@ -162,8 +162,9 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     const bool decode = (G > 1) ? (p.Sq * G <= 16) : (p.Sq <= 16);
     const FwdVariant* var = nullptr;
     if (decode && env_int("TPATTN_GENERIC_DECODE", 0) == 0) {
+        const int want_waves = env_int("TPATTN_DECODE_WAVES", 4);  // waves per workgroup (4 or 8)
         for (const FwdVariant* v = decode_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d) {
+            if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves) {
                 var = v;
                 break;
             }

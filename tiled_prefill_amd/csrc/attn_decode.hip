@@ -45,7 +45,7 @@ struct DecodeTile {
 };
 
 template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 2) attn_decode_kernel(FwdParams p) {
+__global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams p) {
     using C = DecodeTile<D, NW>;
     constexpr int KB = C::KB, NSLAB = C::NSLAB, NT = C::NT, DT = C::DT;
     constexpr int CPR = C::CPR, RPI = C::RPI, NVL = C::NVL, ROWB = C::ROWB;
@@ -428,6 +428,9 @@ const FwdVariant* decode_variants() {
     static const FwdVariant v[] = {
         {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>, 0},
         {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>, 0},
+        // 8 waves (512 keys per workgroup at one block per wave), one workgroup per CU
+        {DT_BF16, 128, 16, 64, 1, 8, DecodeTile<128, 8>::LDS_BYTES, &launch_decode<128, 8>, 0},
+        {DT_BF16, 64, 16, 64, 1, 8, DecodeTile<64, 8>::LDS_BYTES, &launch_decode<64, 8>, 0},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;
