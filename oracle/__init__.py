@@ -59,6 +59,9 @@ def _load():
     lib.attn_ref_f64.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, ip, i, i, i,
                                  ctypes.c_double, i]
     lib.attn_ref_f64.restype = i
+    lib.attn_ref_dv_f64.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, ip, i, i, i, i,
+                                    ctypes.c_double, i]
+    lib.attn_ref_dv_f64.restype = i
     lib.attn_ref_partial_f64.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, ip, i, i, i,
                                          ctypes.c_double, i, i, i]
     lib.attn_ref_partial_f64.restype = i
@@ -99,20 +102,29 @@ def _seqlens(seqlens_k, B):
 
 def attn_ref(q, k, v, causal: bool, window_left: int, scale: float, seqlens_k=None,
              n_threads: int = 0, key_range=None):
-    """Exact attention in fp64. q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d].
+    """Exact attention in fp64. q [B,Sq,Hq,d], k [B,Sk,Hkv,d], v [B,Sk,Hkv,dv].
 
-    Returns (o [B,Sq,Hq,d] fp64, lse [B,Hq,Sq] fp64). ``key_range=(j0, j1)``
-    gives the partial result of one key split instead (attn_ref_partial_f64).
+    Returns (o [B,Sq,Hq,dv] fp64, lse [B,Hq,Sq] fp64). ``key_range=(j0, j1)``
+    gives the partial result of one key split instead (attn_ref_partial_f64,
+    dv == d only). With dv != d the values have a width of their own
+    (attn_ref_dv_f64: the latent-attention verify shape, 576-wide keys and
+    512-wide values).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Sq, Hq, d = q.shape
     Bk, Sk, Hkv, dk = k.shape
-    assert Bk == B and dk == d and v.shape == k.shape
-    o = np.zeros((B, Sq, Hq, d), dtype=np.float64)
+    dv = v.shape[-1]
+    assert Bk == B and dk == d and v.shape[:3] == k.shape[:3]
+    o = np.zeros((B, Sq, Hq, dv), dtype=np.float64)
     lse = np.zeros((B, Hq, Sq), dtype=np.float64)
     keep, sp = _seqlens(seqlens_k, B)
     lib = _load()
-    if key_range is None:
+    if dv != d:
+        assert key_range is None, "split partials are for dv == d"
+        rc = lib.attn_ref_dv_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq,
+                                 Sk, sp, d, dv, int(bool(causal)), int(window_left), float(scale),
+                                 int(n_threads))
+    elif key_range is None:
         rc = lib.attn_ref_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk,
                               sp, d, int(bool(causal)), int(window_left), float(scale),
                               int(n_threads))

@@ -34,12 +34,13 @@ static int visible(int i, int j, int skb, int sq, int causal, int window_left) {
     return 1;
 }
 
+/* d: width of q and k rows (the score contraction); dv: width of v and o rows */
 static int attn_core(const double* q, const double* k, const double* v, double* o, double* lse,
-                     int B, int Hq, int Hkv, int Sq, int Sk, const int* seqlens_k, int d,
+                     int B, int Hq, int Hkv, int Sq, int Sk, const int* seqlens_k, int d, int dv,
                      int causal, int window_left, double scale, int j_begin, int j_end,
                      int n_threads) {
     if (!q || !k || !v || !o) return -1;
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Sk < 0 || d <= 0) return -1;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Sk < 0 || d <= 0 || dv <= 0) return -1;
     if (Hq % Hkv != 0) return -1;
     if (window_left < -1) return -1;
     const int G = Hq / Hkv;
@@ -53,7 +54,7 @@ static int attn_core(const double* q, const double* k, const double* v, double* 
 #pragma omp parallel
     {
         double* s = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
-        double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)dv);
         if (!s || !acc) {
 #pragma omp atomic write
             bad = 1;
@@ -70,7 +71,7 @@ static int attn_core(const double* q, const double* k, const double* v, double* 
             if (skb > Sk) skb = Sk;
             if (skb < 0) skb = 0;
             const double* qi = q + (((long)b * Sq + i) * Hq + hq) * d;
-            double* oi = o + (((long)b * Sq + i) * Hq + hq) * d;
+            double* oi = o + (((long)b * Sq + i) * Hq + hq) * dv;
 
             /* pass 1: scores of the visible keys and their maximum */
             double m = -INFINITY;
@@ -88,21 +89,21 @@ static int attn_core(const double* q, const double* k, const double* v, double* 
                 ++nvis;
             }
             if (nvis == 0) {
-                for (int c = 0; c < d; ++c) oi[c] = 0.0;
+                for (int c = 0; c < dv; ++c) oi[c] = 0.0;
                 if (lse) lse[((long)b * Hq + hq) * Sq + i] = -INFINITY;
                 continue;
             }
             /* pass 2: normaliser and weighted sum of the value rows */
             double l = 0.0;
-            for (int c = 0; c < d; ++c) acc[c] = 0.0;
+            for (int c = 0; c < dv; ++c) acc[c] = 0.0;
             for (int j = 0; j < skb; ++j) {
                 if (s[j] == -INFINITY) continue;
                 const double p = exp(s[j] - m);
                 l += p;
-                const double* vj = v + (((long)b * Sk + j) * Hkv + hkv) * d;
-                for (int c = 0; c < d; ++c) acc[c] += p * vj[c];
+                const double* vj = v + (((long)b * Sk + j) * Hkv + hkv) * dv;
+                for (int c = 0; c < dv; ++c) acc[c] += p * vj[c];
             }
-            for (int c = 0; c < d; ++c) oi[c] = acc[c] / l;
+            for (int c = 0; c < dv; ++c) oi[c] = acc[c] / l;
             if (lse) lse[((long)b * Hq + hq) * Sq + i] = m + log(l);
         }
         free(s);
@@ -114,7 +115,14 @@ static int attn_core(const double* q, const double* k, const double* v, double* 
 int attn_ref_f64(const double* q, const double* k, const double* v, double* o, double* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, const int* seqlens_k, int d,
                  int causal, int window_left, double scale, int n_threads) {
-    return attn_core(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, seqlens_k, d, causal, window_left,
+    return attn_core(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, seqlens_k, d, d, causal, window_left,
+                     scale, 0, Sk, n_threads);
+}
+
+int attn_ref_dv_f64(const double* q, const double* k, const double* v, double* o, double* lse,
+                    int B, int Hq, int Hkv, int Sq, int Sk, const int* seqlens_k, int d, int dv,
+                    int causal, int window_left, double scale, int n_threads) {
+    return attn_core(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, seqlens_k, d, dv, causal, window_left,
                      scale, 0, Sk, n_threads);
 }
 
@@ -122,7 +130,7 @@ int attn_ref_partial_f64(const double* q, const double* k, const double* v, doub
                          double* lse, int B, int Hq, int Hkv, int Sq, int Sk,
                          const int* seqlens_k, int d, int causal, int window_left,
                          double scale, int j_begin, int j_end, int n_threads) {
-    return attn_core(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, seqlens_k, d, causal, window_left,
+    return attn_core(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, seqlens_k, d, d, causal, window_left,
                      scale, j_begin, j_end, n_threads);
 }
 

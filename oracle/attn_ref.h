@@ -40,6 +40,15 @@ int attn_ref_f64(const double* q, const double* k, const double* v, double* o, d
                  int B, int Hq, int Hkv, int Sq, int Sk, const int* seqlens_k, int d,
                  int causal, int window_left, double scale, int n_threads);
 
+/* Same, with value rows of their own width: q and k rows have d elements (the
+ * score contraction), v and o rows have dv -- the latent-attention verify shape
+ * of [Occupancy] (one shared KV head, 576-wide keys, 512-wide values).
+ * Layouts: q [B][Sq][Hq][d], k [B][Sk][Hkv][d], v [B][Sk][Hkv][dv],
+ * o [B][Sq][Hq][dv]. */
+int attn_ref_dv_f64(const double* q, const double* k, const double* v, double* o, double* lse,
+                    int B, int Hq, int Hkv, int Sq, int Sk, const int* seqlens_k, int d, int dv,
+                    int causal, int window_left, double scale, int n_threads);
+
 /* Same, with the keys further restricted to [j_begin, j_end): the partial
  * result of one key split. o is normalised over the keys of the split and
  * lse is that split's log-sum-exp; an empty split gives o = 0, lse = -inf. */

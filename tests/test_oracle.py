@@ -251,3 +251,57 @@ def test_combine_closed_forms():
     keep = torch.isfinite(lse_part).any(0)
     two_ref = torch.logsumexp(lse_part.double(), dim=0).numpy()
     np.testing.assert_allclose(la[keep.numpy()], two_ref[keep.numpy()], rtol=0, atol=1e-12)
+
+
+# --- values of their own width (the latent-attention verify shape: one shared KV
+# head, 576-wide keys, 512-wide values) --------------------------------------------
+
+def _values(seed, B, Sk, Hkv, dv):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(B, Sk, Hkv, dv, generator=g)
+
+
+@pytest.mark.parametrize("d,dv", [(8, 24), (24, 8), (576, 512)])
+def test_value_width_brute_force_against_torch_sdpa(d, dv):
+    # torch fp64 SDPA accepts values of another width; every mask on tiny shapes,
+    # all query heads sharing one KV head (repeated for torch)
+    n = 0
+    for Sq, Sk in [(1, 5), (3, 7), (5, 5), (4, 9)]:
+        q, k, _ = small_case(7 + Sq * Sk, "fp32", 2, 4, 1, Sq, Sk, d)
+        v = _values(3 + Sk, 2, Sk, 1, dv)
+        for causal, wl in [(False, -1), (True, -1), (True, 1), (False, 2)]:
+            o, lse = oracle.attn_ref(q, k, v, causal, wl, 0.07)
+            assert o.shape == (2, Sq, 4, dv)
+            ro, rl, mask = _torch_reference(q, k.repeat_interleave(4, dim=2), v.repeat_interleave(4, dim=2),
+                                            causal, wl, 0.07)
+            rows = mask.any(axis=1)
+            np.testing.assert_allclose(o[:, rows], ro[:, rows], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[:, :, rows], rl[:, :, rows], rtol=0, atol=1e-12)
+            assert np.all(o[:, ~rows] == 0.0)
+            n += 1
+    assert n == 16
+
+
+def test_value_columns_are_independent():
+    # softmax weights do not depend on V: attention with values [V1 | V2] is the
+    # concatenation of the results for V1 (same width as the keys, the plain
+    # path) and V2 (a width of its own) -- pins the value-row stride and offsets
+    q, k, v1 = small_case(21, "fp32", 2, 8, 2, 6, 11, 16)
+    v2 = _values(5, 2, 11, 2, 40)
+    o, lse = oracle.attn_ref(q, k, torch.cat([v1, v2], dim=-1), True, 4, 0.25)
+    o1, l1 = oracle.attn_ref(q, k, v1, True, 4, 0.25)
+    o2, l2 = oracle.attn_ref(q, k, v2, True, 4, 0.25)
+    np.testing.assert_allclose(o, np.concatenate([o1, o2], axis=-1), rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(lse, l1)
+    np.testing.assert_array_equal(lse, l2)
+
+
+def test_value_width_constant_keys_average_values():
+    q, k, _ = small_case(31, "fp32", 1, 4, 1, 3, 10, 576)
+    k[:] = k[:, :1]
+    v = _values(9, 1, 10, 1, 512)
+    o, _ = oracle.attn_ref(q, k, v, True, -1, 0.04)
+    v64 = v.double().numpy()
+    for i in range(3):
+        hi = i + 7  # causal, delta = 7
+        np.testing.assert_allclose(o[0, i, 2], v64[0, :hi + 1, 0].mean(axis=0), rtol=0, atol=1e-12)
