@@ -95,6 +95,20 @@ int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                int causal, int window_left, float scale, int num_splits,
                int dtype, void* stream);
 
+/* Values of their own width: the latent-attention verify shape of [Occupancy]
+ * (one KV head shared by every query head; keys 576 wide = 512 latent + 64
+ * rotary, values 512 wide). q [B][Sq][Hq][d], k [B][Sk][Hkv][d],
+ * v [B][Sk][Hkv][d_v], o [B][Sq][Hq][d_v] (dtype of q), lse as tpattn_fwd.
+ * d_v == d behaves as tpattn_fwd; otherwise only bf16 with d = 576, d_v = 512
+ * is built (TPATTN_EUNSUPPORTED else). The query heads of a KV head are always
+ * packed into the row dimension ([FA-tiling] §6.3); num_splits <= 0 takes the
+ * smaller of the workgroup target and a 512-key minimum chunk (the fp32 split
+ * partials are d_v wide). Other arguments as tpattn_fwd. */
+int tpattn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v,
+                  int causal, int window_left, float scale, int num_splits,
+                  int dtype, void* stream);
+
 /* Variable key lengths ([FA-tiling] §5.3: the split count may differ per
  * sequence). k and v are padded to [B][Sk][Hkv][d]; sequence b uses its first
  * seqlens_k[b] rows (device int32[B], each clamped to [0, Sk]). The split
@@ -142,6 +156,11 @@ int tpattn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int bl
  * whose wave efficiency reaches 0.85 of the best. */
 int tpattn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
                           long long size_one_kv_head, int is_causal_or_local, int max_splits);
+/* The plan tpattn_fwd_dv would use (host only). */
+int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
+                       int window_left, int num_splits, int dtype, int num_cus,
+                       tpattn_plan* out);
+
 /* Default split rule, a reading of [llama.cpp] for 256 CUs: 1 split when
  * tiles >= wg_per_cu * num_cus or there are fewer than 2 key blocks; else
  * max(s_occ, s_chunk) with s_occ = min(ceil(wg_per_cu * num_cus / tiles),

@@ -296,3 +296,39 @@ def test_ablation_paths(env, monkeypatch):
     for case in [("bf16", 1, 8, 2, 300, 300, 128, True, 40, 0), ("bf16", 2, 16, 2, 200, 333, 64, True, -1, 0),
                  ("bf16", 1, 32, 4, 1, 3000, 128, False, -1, 0), ("bf16", 1, 4, 4, 130, 520, 128, False, -1, 0)]:
         run_case(*case, seed=12)
+
+
+# --- values of their own width: the latent-attention verify shapes --------------
+from workloads import latent_case  # noqa: E402
+
+# the verify parity shapes printed on the occupancy blog page (B, H, q_len, kv_len),
+# at the latent-attention widths (keys 576 = 512 latent + 64 rotary, values 512)
+LATENT_SHAPES = [(2, 16, 17, 2065), (1, 64, 33, 161), (2, 64, 9, 521), (2, 8, 9, 9)]
+
+
+def run_latent(B, Hq, Sq, Sk, causal=True, wl=-1, S=0, seed=0):
+    q, k, v = latent_case(seed, B, Hq, Sq, Sk)
+    scale = 1.0 / math.sqrt(576)
+    print(f"latent B={B} Hq={Hq} Sq={Sq} Sk={Sk} causal={causal} wl={wl} S={S} seed={seed}", flush=True)
+    o, lse = tpa.fwd_dv(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window_left=wl, scale=scale,
+                        num_splits=S)
+    torch.cuda.synchronize()
+    assert o.shape == (B, Sq, Hq, 512)
+    ro, rl = oracle.attn_ref(q, k, v, causal, wl, scale)
+    assert_parity(o, lse, ro, rl, "bf16", f"latent {B},{Hq},{Sq},{Sk} c={causal} wl={wl} S={S}")
+
+
+@pytest.mark.parametrize("shape", LATENT_SHAPES, ids=lambda s: "B%d_H%d_q%d_kv%d" % s)
+def test_latent_verify_shapes(shape):
+    run_latent(*shape)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7])
+def test_latent_split_sweep(S):
+    run_latent(2, 16, 17, 2065, S=S, seed=1)
+
+
+def test_latent_noncausal_window_and_ragged():
+    run_latent(1, 8, 5, 77, causal=False, seed=2)           # ragged last key tile
+    run_latent(1, 8, 12, 300, causal=True, wl=50, seed=3)   # sliding window
+    run_latent(1, 3, 30, 20, causal=True, seed=4)           # Sq > Sk: fully masked rows

@@ -69,6 +69,10 @@ def load():
     lib.tpattn_fwd_varlen.restype = i
     lib.tpattn_plan_fwd.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ll, i, ctypes.POINTER(Plan)]
     lib.tpattn_plan_fwd.restype = i
+    lib.tpattn_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.tpattn_fwd_dv.restype = i
+    lib.tpattn_plan_fwd_dv.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.tpattn_plan_fwd_dv.restype = i
     lib.tpattn_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.tpattn_workspace_bytes.restype = ctypes.c_size_t
     lib.tpattn_lse_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
@@ -111,7 +115,7 @@ def _stream_ptr(stream) -> int:
     return int(stream.cuda_stream)
 
 
-def _check_tensors(q, k, v):
+def _check_tensors(q, k, v, same_width=True):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -121,8 +125,9 @@ def _check_tensors(q, k, v):
             raise ValueError(f"{name} must be 4-D")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
+    if (k.shape != v.shape) if same_width else (k.shape[:3] != v.shape[:3]):
+        raise ValueError("k and v must have the same shape" if same_width else
+                         "k and v must agree in batch, keys and heads")
     if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
         raise ValueError("batch and head dim of q and k must match")
 
@@ -144,6 +149,28 @@ def fwd(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[fl
                            lse.data_ptr() if lse is not None else None,
                            B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                            float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
+    _check(rc)
+    return out, lse
+
+
+def fwd_dv(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
+           num_splits: int = 0, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
+    """Forward with values of their own width (tpattn_fwd_dv): q, k [.., d], v [.., d_v].
+    Returns (o [B, Sq, Hq, d_v], lse)."""
+    _check_tensors(q, k, v, same_width=False)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, dv = v.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, dv), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    rc = load().tpattn_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None,
+                              B, Hq, Hkv, Sq, Sk, d, dv, int(bool(causal)), int(window_left),
+                              float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
     _check(rc)
     return out, lse
 
@@ -201,6 +228,16 @@ def plan(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, num_splits=0, dtyp
                                 int(num_splits), code, int(bool(varlen)), int(sum_seqlens_k),
                                 int(num_cus), ctypes.byref(p))
     _check(rc)
+    return p.as_dict()
+
+
+def plan_dv(B, Hq, Hkv, Sq, Sk, d, d_v, causal=False, window_left=-1, num_splits=0, dtype="bf16",
+            num_cus=0) -> dict:
+    """The plan of tpattn_fwd_dv (host only)."""
+    p = Plan()
+    code = FP32 if dtype in ("fp32", FP32, torch.float32) else BF16
+    _check(load().tpattn_plan_fwd_dv(B, Hq, Hkv, Sq, Sk, d, d_v, int(bool(causal)), int(window_left),
+                                     int(num_splits), code, int(num_cus), ctypes.byref(p)))
     return p.as_dict()
 
 

@@ -117,6 +117,7 @@ struct Problem {
     int B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, varlen;
     long long sum_seqlens_k;
     float scale;
+    int dv = 0;  // value / output width; 0 means d
 };
 
 int check_problem(const Problem& p) {
@@ -126,8 +127,13 @@ int check_problem(const Problem& p) {
         return fail(TPATTN_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", p.Hq, p.Hkv);
     if (p.dtype != TPATTN_FP32 && p.dtype != TPATTN_BF16)
         return fail(TPATTN_EUNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p.dtype);
-    if (p.d != 64 && p.d != 128)
+    const int dv = p.dv > 0 ? p.dv : p.d;
+    if (dv != p.d) {
+        if (!(p.d == 576 && dv == 512 && p.dtype == TPATTN_BF16))
+            return fail(TPATTN_EUNSUPPORTED, "d=%d with d_v=%d is not built (bf16 576/512 only)", p.d, dv);
+    } else if (p.d != 64 && p.d != 128) {
         return fail(TPATTN_EUNSUPPORTED, "head dim %d is not built (64 or 128)", p.d);
+    }
     if (p.window_left < -1) return fail(TPATTN_EINVAL, "window_left=%d < -1", p.window_left);
     if (!(p.scale > 0.f) || !isfinite(p.scale))
         return fail(TPATTN_EINVAL, "scale must be finite and > 0");
@@ -160,8 +166,17 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     // 16 rows when all query rows of a KV head (packed) fit in 16, else a
     // "prefill" tile; packing per [FA-tiling] §6.2.
     const bool decode = (G > 1) ? (p.Sq * G <= 16) : (p.Sq <= 16);
+    const int dv = p.dv > 0 ? p.dv : p.d;
     const FwdVariant* var = nullptr;
-    if (decode && env_int("TPATTN_GENERIC_DECODE", 0) == 0) {
+    if (dv != p.d) {  // values of their own width: the latent-attention kernel
+        for (const FwdVariant* v = mla_variants(); v->launch; ++v)
+            if (v->dtype == p.dtype && v->d == p.d && v->dv == dv) {
+                var = v;
+                break;
+            }
+        if (!var) return fail(TPATTN_EUNSUPPORTED, "no kernel for d=%d d_v=%d", p.d, dv);
+    }
+    if (!var && decode && env_int("TPATTN_GENERIC_DECODE", 0) == 0) {
         const int want_waves = env_int("TPATTN_DECODE_WAVES", 4);  // waves per workgroup (4 or 8)
         for (const FwdVariant* v = decode_variants(); v->launch; ++v)
             if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves) {
@@ -169,7 +184,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                 break;
             }
     }
-    if (!decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
+    if (!var && !decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
         // Tile rows ([FA-tiling] §2.5: smaller blocks where masking cuts tiles):
         // 256-row workgroups (8 waves) for full and causal masks, 128 rows (4
         // waves) with a sliding window, where a 256-row tile spends ~20% of its
@@ -205,7 +220,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     if (!var) return fail(TPATTN_EUNSUPPORTED, "no kernel variant for dtype %d d %d", p.dtype, p.d);
     const int BM = var->block_m, BN = var->block_n;
     bool pack = false;
-    if (G > 1) pack = decode ? true : should_pack(p.varlen != 0, p.Sq, G, BM);
+    if (G > 1) pack = (decode || var->dv) ? true : should_pack(p.varlen != 0, p.Sq, G, BM);
 
     tpattn_plan& q = out->pub;
     q = tpattn_plan{};
@@ -262,6 +277,12 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             chunk = cb;
             S = imax(1, imin(TPATTN_MAX_SPLITS, ceil_div(imax(max_blocks, 1), cb)));
             if (S == 1) chunk = 0;
+        } else if (var->dv) {
+            // 512-wide fp32 partials are costly: split only as far as both the
+            // workgroup target and a minimum chunk of 512 keys allow
+            const int mc = imax(1, ceil_div(env_int("TPATTN_MLA_MIN_CHUNK", 512), BN));
+            const int target = wg_per_cu * num_cus;
+            S = imin(ceil_div(target, t), imax(1, max_blocks / mc));
         } else {
             S = occupancy_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
         }
@@ -287,7 +308,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     }
     // workspace: split partials, then (kernels that read it) the fp16 V^T of the
     // V pre-pass, 256-byte aligned
-    size_t ws = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, p.d, S) : 0;
+    size_t ws = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, dv, S) : 0;
     out->vt_offset = (ws + 255) & ~(size_t)255;
     out->skp = ceil_div(imax(p.Sk, 0), 64) * 64;
     if (var->needs_vt && p.Sk > 0)
@@ -406,7 +427,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     }
     const size_t rows = (size_t)pr.B * pr.Sq * pr.Hq;
     fp.o_part = reinterpret_cast<float*>(ws.ptr);
-    fp.lse_part = fp.o_part + (size_t)pl.num_splits * rows * pr.d;
+    const int dvv = pr.dv > 0 ? pr.dv : pr.d;
+    fp.lse_part = fp.o_part + (size_t)pl.num_splits * rows * dvv;
     hipError_t e;
     int slot;
     if (plan.var->needs_vt) {
@@ -442,7 +464,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     cp.Sq = pr.Sq;
     cp.Hq = pr.Hq;
     slot = prof_start(1, stream);
-    e = launch_combine(cp, pr.d, pr.dtype == TPATTN_BF16, stream);
+    e = launch_combine(cp, dvv, pr.dtype == TPATTN_BF16, stream);
     prof_stop(slot, stream);
     if (e != hipSuccess) return fail(TPATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
     return TPATTN_OK;
@@ -465,6 +487,28 @@ int tpattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, floa
                       long long sum_seqlens_k, void* stream) {
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 1, sum_seqlens_k, scale};
     return run_fwd(p, q, k, v, o, lse, seqlens_k, stream);
+}
+
+int tpattn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                  int Hkv, int Sq, int Sk, int d, int d_v, int causal, int window_left,
+                  float scale, int num_splits, int dtype, void* stream) {
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, scale};
+    p.dv = d_v;
+    if (d_v <= 0) return fail(TPATTN_EINVAL, "d_v=%d must be positive", d_v);
+    return run_fwd(p, q, k, v, o, lse, nullptr, stream);
+}
+
+int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
+                       int window_left, int num_splits, int dtype, int num_cus, tpattn_plan* out) {
+    if (!out) return fail(TPATTN_EINVAL, "null plan pointer");
+    if (d_v <= 0) return fail(TPATTN_EINVAL, "d_v=%d must be positive", d_v);
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, 1.0f};
+    p.dv = d_v;
+    Plan plan;
+    int rc = make_plan(p, num_cus, &plan);
+    if (rc) return rc;
+    *out = plan.pub;
+    return TPATTN_OK;
 }
 
 int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,

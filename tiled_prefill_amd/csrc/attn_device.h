@@ -140,4 +140,28 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// ---- fp16 operands (the P.V product of the bf16 prefill kernels) ----------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// fp32 pair -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+// two bf16 (one 32-bit word) -> two fp16, exact for |x| <= 65504
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// Workgroups of a one-dimensional grid are dealt round-robin to the 8 XCDs of
+// an MI355X (workgroup i runs on XCD i % 8).
+constexpr int NUM_XCD = 8;
+
 }  // namespace tpa

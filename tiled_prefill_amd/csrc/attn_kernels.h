@@ -21,6 +21,7 @@ struct FwdVariant {
     int needs_vt;           // > 0: reads V as fp16 V^T from the V pre-pass (FwdParams::vt),
                             // keys permuted in blocks of this many (16 or 32)
     int persistent;         // > 0: persistent workgroups (this many per CU) over tile queues
+    int dv;                 // value / output width when it differs from d (0: equal to d)
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
@@ -28,6 +29,7 @@ struct FwdVariant {
 const FwdVariant* fwd_variants();
 const FwdVariant* decode_variants();
 const FwdVariant* prefill_variants();
+const FwdVariant* mla_variants();   // values of their own width (d_v != d)
 
 // The V pre-pass: V (bf16) -> fp16 V^T in FwdParams::vt (pitch FwdParams::skp).
 hipError_t launch_v_to_f16t(const FwdParams& p, hipStream_t stream);

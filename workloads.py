@@ -113,6 +113,19 @@ def small_case(seed: int, dtype: str, B: int, Hq: int, Hkv: int, Sq: int, Sk: in
     return q, k, v
 
 
+def latent_case(seed: int, B: int, Hq: int, Sq: int, Sk: int, d: int = 576, dv: int = 512,
+                std: float = 1.0, dtype: str = "bf16"):
+    """Random latent-attention verify inputs: one KV head shared by the Hq query
+    heads, q/k rows d wide, v rows dv wide; N(0, 1) * std in fp32, rounded on the
+    CPU to the dtype (the recipe of ``make_inputs``)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = (torch.randn((B, Sq, Hq, d), generator=g) * std).to(td)
+    k = (torch.randn((B, Sk, 1, d), generator=g) * std).to(td)
+    v = (torch.randn((B, Sk, 1, dv), generator=g) * std).to(td)
+    return q, k, v
+
+
 def random_partials(seed: int, S: int, rows: int, d: int, p_empty: float = 0.25):
     """Random split partials (O_s [S, rows, d] fp32, lse_s [S, rows] fp32).
 
