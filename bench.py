@@ -173,6 +173,55 @@ def run_suite(args):
             rec["pct_mfma_bf16"] = round(100 * rec["TFLOPs"] / BF16_PEAK_TFLOPS, 2)
         print(json.dumps(rec), flush=True)
         del ks, vs, q, k, v, o
+    run_latent_suite(args)
+
+
+def run_latent_suite(args):
+    """Latent-attention verify workloads (values of their own width, tpattn_fwd_dv)."""
+    import torch
+    import tiled_prefill_amd as tpa
+    from workloads import LATENT_WORKLOADS, latent_case
+    dev = "cuda:0"
+    for name, (B, Hq, Sq, Sk) in LATENT_WORKLOADS.items():
+        if args.workload and name != args.workload:
+            continue
+        q, k, v = (t.to(dev) for t in latent_case(0, B, Hq, Sq, Sk))
+        kv_bytes = B * Sk * (576 + 512) * 2
+        pairs = B * Hq * sum(min(i + 1 + Sk - Sq, Sk) for i in range(Sq))
+        flops = 2.0 * (576 + 512) * pairs
+        n_rot = max(1, min(16, math.ceil(2 * LLC_BYTES / kv_bytes)))
+        ks = [k] + [k.clone() for _ in range(n_rot - 1)]
+        vs = [v] + [v.clone() for _ in range(n_rot - 1)]
+        o = torch.empty((B, Sq, Hq, 512), dtype=q.dtype, device=dev)
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+
+        def step(i):
+            tpa.fwd_dv(q, ks[i % n_rot], vs[i % n_rot], causal=True, out=o, lse=lse)
+
+        warm(step, args.warmup)
+        steps = max(20, args.steps)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        tpa.profile_begin(2 * steps + 8)
+        for i in range(steps):
+            step(i)
+        prof = tpa.profile_end()
+        plan = tpa.plan_dv(B, Hq, 1, Sq, Sk, 576, 512, causal=True)
+        rec = {"workload": name, "dtype": "bf16", "B": B, "Hq": Hq, "Hkv": 1, "Sq": Sq, "Sk": Sk,
+               "d": 576, "d_v": 512, "ms_per_step": round(ms, 5),
+               "kv_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+               "pct_hbm": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+               "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+               "pct_mfma_bf16": round(100 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+               "fwd_us": round(1e3 * prof["fwd_ms"] / max(1, prof["fwd_launches"]), 2),
+               "combine_us": round(1e3 * prof["combine_ms"] / max(1, prof["combine_launches"]), 2),
+               "num_splits": plan["num_splits"], "grid": plan["grid_x"], "kv_copies": n_rot,
+               "kv_bytes": kv_bytes, "flops": flops, "steps": steps}
+        print(json.dumps(rec), flush=True)
+        del ks, vs, q, k, v, o
 
 
 def main():

@@ -177,9 +177,12 @@ def test_non_default_stream():
     assert_parity(o, lse, ro, rl, "bf16", "stream")
 
 
+@pytest.mark.parametrize("cols", ["0", "1"], ids=["split_groups", "columns"])
 @pytest.mark.parametrize("S,d,dtype", [(1, 128, "fp32"), (2, 64, "bf16"), (5, 128, "bf16"),
-                                       (64, 128, "fp32"), (256, 64, "fp32"), (128, 128, "bf16")])
-def test_combine_kernel_parity(S, d, dtype):
+                                       (64, 128, "fp32"), (256, 64, "fp32"), (128, 128, "bf16"),
+                                       (7, 512, "bf16")])
+def test_combine_kernel_parity(S, d, dtype, cols, monkeypatch):
+    monkeypatch.setenv("TPATTN_COMBINE_COLS", cols)
     B, Sq, Hq = 2, 3, 5
     rows = B * Sq * Hq
     o_part, lse_part = random_partials(10 + S, S, rows, d, p_empty=0.3)
@@ -286,6 +289,8 @@ ABLATIONS = [
     {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
     {"TPATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
     {"TPATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order
+    {"TPATTN_COMBINE_COLS": "0"},             # split-group combine kernel everywhere
+    {"TPATTN_COMBINE_COLS": "1"},             # column-parallel combine kernel everywhere
 ]
 
 

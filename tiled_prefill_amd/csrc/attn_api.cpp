@@ -534,7 +534,8 @@ int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, floa
                        int Sq, int Hq, int d, int num_splits, int dtype, void* stream_v) {
     if (!o_part || !lse_part || !o) return fail(TPATTN_EINVAL, "null tensor pointer");
     if (B < 0 || Sq < 0 || Hq < 1) return fail(TPATTN_EINVAL, "bad shape");
-    if (d != 64 && d != 128) return fail(TPATTN_EUNSUPPORTED, "head dim %d is not built", d);
+    if (d != 64 && d != 128 && d != 512)
+        return fail(TPATTN_EUNSUPPORTED, "value width %d is not built (64, 128, 512)", d);
     if (dtype != TPATTN_FP32 && dtype != TPATTN_BF16)
         return fail(TPATTN_EUNSUPPORTED, "dtype %d", dtype);
     if (num_splits < 1 || num_splits > TPATTN_MAX_SPLITS)

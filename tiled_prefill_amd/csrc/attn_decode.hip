@@ -17,12 +17,19 @@
 // block of K and V in flight.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
 #include "attn_plan.h"
 
 namespace tpa {
+
+// a switch read from the environment on the host (dflt when unset)
+static int env_flag(const char* name, int dflt) {
+    const char* v = getenv(name);
+    return v && *v ? atoi(v) : dflt;
+}
 
 template <int D, int NW>
 struct DecodeTile {
@@ -418,6 +425,67 @@ __global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D
     }
 }
 
+// Column-parallel combine, for few splits and many output elements: one thread
+// per (row, 4 columns) merges every split of its columns itself -- a pass over
+// the row's lse_s for M, then sum_s exp(lse_s - M) (O_s, 1) -- so no partial
+// state crosses lanes. Consecutive threads read consecutive 16-byte column
+// chunks of a partial row.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) lse_combine_cols_kernel(CombineParams p, int D) {
+    const int cpr = D / 4;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.rows * cpr) return;
+    const int row = (int)(idx / cpr), c4 = (int)(idx % cpr);
+    const size_t rows = (size_t)p.rows;
+    const int S = p.num_splits;
+    float m = -INFINITY;
+    for (int s = 0; s < S; ++s) m = vmax(m, p.lse_part[(size_t)s * rows + row]);
+    float l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (m != -INFINITY) {
+        int s = 0;
+        for (; s + 4 <= S; s += 4) {  // four partials in flight
+            float ls[4];
+            f32x4 ov[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ls[j] = p.lse_part[(size_t)(s + j) * rows + row];
+                ov[j] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)(s + j) * rows + row) * D + 4 * c4);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = ls[j] == -INFINITY ? 0.f : __expf(ls[j] - m);
+                l += w;
+                if (w != 0.f) acc += w * ov[j];
+            }
+        }
+        for (; s < S; ++s) {
+            const float ls = p.lse_part[(size_t)s * rows + row];
+            if (ls == -INFINITY) continue;
+            const float w = __expf(ls - m);
+            l += w;
+            acc += w * *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + 4 * c4);
+        }
+    }
+    const bool any = m != -INFINITY && l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const f32x4 o = acc * inv;
+    if constexpr (OUT_BF16) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + 4 * c4) = w;
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + 4 * c4) = o;
+    }
+    if (c4 == 0 && p.lse) {
+        const int h = row % p.Hq;
+        const int pos = (row / p.Hq) % p.Sq;
+        const int bb = row / (p.Hq * p.Sq);
+        p.lse[((size_t)bb * p.Hq + h) * p.Sq + pos] = any ? m + logf(l) : -INFINITY;
+    }
+}
+
 template <int D, int NW>
 hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((attn_decode_kernel<D, NW>), grid, dim3(64 * NW), 0, stream, p);
@@ -436,7 +504,26 @@ const FwdVariant* decode_variants() {
     return v;
 }
 
+// Kernel choice: the split-group kernel parallelises over splits (decode: many
+// splits, few rows); the column kernel over output elements.
+bool combine_by_columns(int rows, int d, int num_splits) {
+    const int env = env_flag("TPATTN_COMBINE_COLS", -1);
+    if (env >= 0) return env != 0;
+    (void)rows;
+    (void)d;
+    // measured: columns win at <= 16 splits (latent verify, 4 splits x 544 rows:
+    // 6.4 vs 32.8 us); split groups at 52..128 splits (varlen decode 16.2 vs 42.2)
+    return num_splits <= 16;
+}
+
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream) {
+    if (combine_by_columns(p.rows, d, p.num_splits)) {
+        const long long n = (long long)p.rows * (d / 4);
+        dim3 grid((unsigned)((n + 255) / 256)), block(256);
+        if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_kernel<true>), grid, block, 0, stream, p, d);
+        else hipLaunchKernelGGL((lse_combine_cols_kernel<false>), grid, block, 0, stream, p, d);
+        return hipGetLastError();
+    }
     dim3 grid(p.rows, d / 32), block(256);
     if (out_bf16) hipLaunchKernelGGL((lse_combine_kernel<true>), grid, block, 0, stream, p, d);
     else hipLaunchKernelGGL((lse_combine_kernel<false>), grid, block, 0, stream, p, d);

@@ -113,6 +113,17 @@ def small_case(seed: int, dtype: str, B: int, Hq: int, Hkv: int, Sq: int, Sk: in
     return q, k, v
 
 
+# Latent-attention verify workloads (tpattn_fwd_dv; keys 576 wide, values 512, one
+# KV head shared by Hq query heads, causal over the last Sq positions):
+# name -> (B, Hq, Sq, Sk). The first is the verify parity shape printed on the
+# occupancy blog page; the second its long-prefix case (the 65k prefix for which
+# the page derives 32 KV splits).
+LATENT_WORKLOADS = {
+    "latent_verify_bf16": (2, 16, 17, 2065),
+    "latent_verify_long_bf16": (1, 16, 17, 65536),
+}
+
+
 def latent_case(seed: int, B: int, Hq: int, Sq: int, Sk: int, d: int = 576, dv: int = 512,
                 std: float = 1.0, dtype: str = "bf16"):
     """Random latent-attention verify inputs: one KV head shared by the Hq query
