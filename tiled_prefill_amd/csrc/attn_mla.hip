@@ -191,16 +191,19 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
         const char* kt = smem + stage * STAGEB;
         const char* vt = kt + KTILEB;
 
-        // S^T = K . Q^T
+        // S^T = K . Q^T. The fragment of slab s2 is logical chunk 4 s2 + g of row
+        // 16 tt + i; its slot is 8 (s2 / 2) + ((4 (s2 % 2) + g) ^ ((i / 2) % 8)), so
+        // every address is one of two per-lane bases plus a constant offset.
         f32x4 sacc[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* kb0 = kt + li * KROWB + 16 * C::kslot(lg, li);
+        const char* kb1 = kt + li * KROWB + 16 * C::kslot(4 + lg, li);
 #pragma unroll
         for (int s2 = 0; s2 < NSLAB; ++s2)
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                const int rr = 16 * tt + li;
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + rr * KROWB + 16 * C::kslot(4 * s2 + lg, rr));
+                const u32x4 kf = *reinterpret_cast<const u32x4*>((s2 & 1 ? kb1 : kb0) + 128 * (s2 >> 1) + 16 * KROWB * tt);
                 sacc[tt] = mfma_bf16(kf, qf[s2], sacc[tt]);
             }
 
