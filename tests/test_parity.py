@@ -337,3 +337,20 @@ def test_latent_noncausal_window_and_ragged():
     run_latent(1, 8, 5, 77, causal=False, seed=2)           # ragged last key tile
     run_latent(1, 8, 12, 300, causal=True, wl=50, seed=3)   # sliding window
     run_latent(1, 3, 30, 20, causal=True, seed=4)           # Sq > Sk: fully masked rows
+
+
+def test_latent_long_prefix_sampled():
+    # the 65,536-key prefix at full size (103 splits), checked on sampled query
+    # positions: each recomputed by the oracle over exactly its visible keys
+    from workloads import LATENT_WORKLOADS
+    B, Hq, Sq, Sk = LATENT_WORKLOADS["latent_verify_long_bf16"]
+    q, k, v = latent_case(0, B, Hq, Sq, Sk)
+    scale = 1.0 / math.sqrt(576)
+    print(f"latent long B={B} Hq={Hq} Sq={Sq} Sk={Sk}", flush=True)
+    o, lse = tpa.fwd_dv(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    for i in (0, 8, Sq - 1):
+        kl = i + Sk - Sq + 1  # causal, bottom-right: row i sees keys [0, kl)
+        ro, rl = oracle.attn_ref(q[:, i:i + 1], k[:, :kl], v[:, :kl], False, -1, scale)
+        assert_parity(o[:, i:i + 1], lse[:, :, i:i + 1], ro, rl, "bf16", f"latent long row {i}")
