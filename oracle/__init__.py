@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the attention forward pass (ctypes wrapper).
+"""fp64 CPU oracle for the attention forward and backward passes (ctypes wrapper).
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this package. The product library
@@ -20,6 +20,18 @@ Parity status of each oracle function (what pins it, in tests/test_oracle.py):
   needed_block_range
                     pinned: the printed causal block count (528 of 1024) and
                     the closed-form count of a window.
+  attn_bwd_ref      pinned: central finite differences of attn_ref (tiny
+                    shapes with causal, window, GQA and fully masked rows), a
+                    library routine (torch fp64 autograd through an explicitly
+                    masked softmax), invariants (the key gradients of a head
+                    sum to zero; the value gradients sum to the output
+                    gradients of rows that see a key; a constant added to
+                    every value row leaves dq and dk unchanged) and a closed
+                    form (identical keys give dq = 0).
+  needed_m_block_range
+                    pinned: over all key blocks it visits as many (query
+                    block, key block) pairs as needed_block_range (the printed
+                    528 of 1024 for the causal example).
 """
 from __future__ import annotations
 
@@ -67,6 +79,9 @@ def _load():
     lib.attn_ref_partial_f64.restype = i
     lib.lse_combine_ref_f64.argtypes = [dp, dp, i, ctypes.c_long, i, dp, dp]
     lib.lse_combine_ref_f64.restype = i
+    lib.attn_bwd_ref_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, i, i,
+                                     ctypes.c_double, i]
+    lib.attn_bwd_ref_f64.restype = i
     _lib = lib
     return lib
 
@@ -190,4 +205,44 @@ def needed_block_range(Sq: int, Skb: int, causal: bool, window_left: int, BM: in
             out.append(None)
         else:
             out.append((int(cols[0]) // BN, int(cols[-1]) // BN + 1))
+    return out
+
+
+def attn_bwd_ref(q, k, v, dout, causal: bool, window_left: int, scale: float, n_threads: int = 0):
+    """Gradients of L = <dout, attn(q, k, v)> in fp64 (attn_bwd_ref_f64).
+
+    q, dout [B,Sq,Hq,d], k, v [B,Sk,Hkv,d]. Returns (dq, dk, dv) with the shapes
+    of q, k, v.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, d = q.shape
+    Bk, Sk, Hkv, dk_ = k.shape
+    assert Bk == B and dk_ == d and v.shape == k.shape and dout.shape == q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rc = _load().attn_bwd_ref_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)),
+                                  int(window_left), float(scale), int(n_threads))
+    if rc != 0:
+        raise ValueError("attn_bwd_ref_f64 rejected its arguments")
+    return dq, dk, dv
+
+
+def needed_m_block_range(Sq: int, Sk: int, causal: bool, window_left: int, BM: int, BN: int):
+    """Brute-force query-block range each key block must visit (backward loop order).
+
+    The backward pass of "分块策略与调度" §3.4 runs over key blocks outside and
+    the query blocks that see them inside. Returns, per key block n, (first,
+    last+1) query-block indices holding at least one (row, key) pair visible
+    under the mask of visible_mask, or None if no row sees any key of block n.
+    """
+    vis = visible_mask(Sq, Sk, causal, window_left)
+    out = []
+    for n in range((Sk + BN - 1) // BN):
+        rows = np.nonzero(vis[:, n * BN:min((n + 1) * BN, Sk)].any(axis=1))[0]
+        if rows.size == 0:
+            out.append(None)
+        else:
+            out.append((int(rows[0]) // BM, int(rows[-1]) // BM + 1))
     return out

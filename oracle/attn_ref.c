@@ -1,5 +1,5 @@
 /*
- * attn_ref.c -- fp64 CPU oracle for the attention forward pass.
+ * attn_ref.c -- fp64 CPU oracle for the attention forward and backward passes.
  *
  * TEST INFRASTRUCTURE ONLY (the checker, never the product path); see
  * attn_ref.h for the contract and the layouts.
@@ -161,4 +161,153 @@ int lse_combine_ref_f64(const double* o_part, const double* lse_part, int S, lon
         if (lse) lse[r] = lse_r;
     }
     return 0;
+}
+
+/*
+ * Backward pass: the gradient of the forward definition above.
+ *
+ * The pages describe the backward loop structure ([FA-tiling] §3.4: one key
+ * block outside, the query blocks that see it inside; §4.6: Q, dO and the dQ
+ * accumulator are what the backward scheduler keeps in L2) but print no
+ * gradient formulas; this is the chain rule applied to the forward definition,
+ * with no tiling. For a row i with visible keys V_i, probabilities
+ * p_ij = exp(s_ij - lse_i) and an output gradient g_i = dL/do_i:
+ *   dp_ij = <g_i, v_j>                      (o_i = sum_j p_ij v_j)
+ *   D_i   = sum_j p_ij dp_ij                (softmax Jacobian: ds = p (dp - <p, dp>))
+ *   ds_ij = p_ij (dp_ij - D_i)              (gradient w.r.t. the scaled score)
+ *   dq_i  = scale sum_j ds_ij k_j
+ *   dk_j  = scale sum_{i, heads of the group} ds_ij q_i
+ *   dv_j  = sum_{i, heads of the group} p_ij g_i
+ * Pass 1 runs over query rows (scores, lse_i, D_i, dq_i); pass 2 over key rows,
+ * recomputing p_ij and ds_ij from lse_i and D_i of pass 1.
+ */
+static int bwd_core(const double* q, const double* k, const double* v, const double* dout,
+                    double* dq, double* dk, double* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                    int d, int causal, int window_left, double scale, int n_threads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Sk < 0 || d <= 0) return -1;
+    if (Hq % Hkv != 0 || window_left < -1) return -1;
+    const int G = Hq / Hkv;
+    const long nrows = (long)B * Hq * Sq;
+    double* lse_row = (double*)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1));
+    double* d_row = (double*)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1));
+    if (!lse_row || !d_row) {
+        free(lse_row);
+        free(d_row);
+        return -1;
+    }
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    int bad = 0;
+    /* pass 1: per query row (b, hq, i) */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        double* dp = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        if (!s || !dp) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (long row = 0; row < nrows; ++row) {
+            if (!s || !dp) continue;
+            const int i = (int)(row % Sq);
+            const int hq = (int)((row / Sq) % Hq);
+            const int b = (int)(row / ((long)Sq * Hq));
+            const int hkv = hq / G;
+            const double* qi = q + (((long)b * Sq + i) * Hq + hq) * d;
+            const double* gi = dout + (((long)b * Sq + i) * Hq + hq) * d;
+            double* dqi = dq + (((long)b * Sq + i) * Hq + hq) * d;
+            for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+            double m = -INFINITY;
+            for (int j = 0; j < Sk; ++j) {
+                if (!visible(i, j, Sk, Sq, causal, window_left)) {
+                    s[j] = -INFINITY;
+                    continue;
+                }
+                const double* kj = k + (((long)b * Sk + j) * Hkv + hkv) * d;
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += qi[c] * kj[c];
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            if (m == -INFINITY) { /* no visible key: the row contributes nothing */
+                lse_row[row] = -INFINITY;
+                d_row[row] = 0.0;
+                continue;
+            }
+            double l = 0.0;
+            for (int j = 0; j < Sk; ++j)
+                if (s[j] != -INFINITY) l += exp(s[j] - m);
+            const double lse_i = m + log(l);
+            double Di = 0.0;
+            for (int j = 0; j < Sk; ++j) {
+                if (s[j] == -INFINITY) continue;
+                const double* vj = v + (((long)b * Sk + j) * Hkv + hkv) * d;
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += gi[c] * vj[c];
+                dp[j] = dot;
+                Di += exp(s[j] - lse_i) * dot;
+            }
+            for (int j = 0; j < Sk; ++j) {
+                if (s[j] == -INFINITY) continue;
+                const double ds = exp(s[j] - lse_i) * (dp[j] - Di);
+                const double* kj = k + (((long)b * Sk + j) * Hkv + hkv) * d;
+                for (int c = 0; c < d; ++c) dqi[c] += scale * ds * kj[c];
+            }
+            lse_row[row] = lse_i;
+            d_row[row] = Di;
+        }
+        free(s);
+        free(dp);
+    }
+    /* pass 2: per key row (b, hkv, j), summed over the G query heads of the group */
+    const long nkeys = (long)B * Hkv * Sk;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long key = 0; key < nkeys; ++key) {
+        const int j = (int)(key % Sk);
+        const int hkv = (int)((key / Sk) % Hkv);
+        const int b = (int)(key / ((long)Sk * Hkv));
+        const double* kj = k + (((long)b * Sk + j) * Hkv + hkv) * d;
+        const double* vj = v + (((long)b * Sk + j) * Hkv + hkv) * d;
+        double* dkj = dk + (((long)b * Sk + j) * Hkv + hkv) * d;
+        double* dvj = dv + (((long)b * Sk + j) * Hkv + hkv) * d;
+        for (int c = 0; c < d; ++c) {
+            dkj[c] = 0.0;
+            dvj[c] = 0.0;
+        }
+        for (int g = 0; g < G; ++g) {
+            const int hq = hkv * G + g;
+            for (int i = 0; i < Sq; ++i) {
+                if (!visible(i, j, Sk, Sq, causal, window_left)) continue;
+                const long row = ((long)b * Hq + hq) * Sq + i;
+                const double* qi = q + (((long)b * Sq + i) * Hq + hq) * d;
+                const double* gi = dout + (((long)b * Sq + i) * Hq + hq) * d;
+                double sdot = 0.0, pdot = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    sdot += qi[c] * kj[c];
+                    pdot += gi[c] * vj[c];
+                }
+                const double p = exp(scale * sdot - lse_row[row]);
+                const double ds = p * (pdot - d_row[row]);
+                for (int c = 0; c < d; ++c) {
+                    dkj[c] += scale * ds * qi[c];
+                    dvj[c] += p * gi[c];
+                }
+            }
+        }
+    }
+    free(lse_row);
+    free(d_row);
+    return bad ? -1 : 0;
+}
+
+int attn_bwd_ref_f64(const double* q, const double* k, const double* v, const double* dout,
+                     double* dq, double* dk, double* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                     int d, int causal, int window_left, double scale, int n_threads) {
+    return bwd_core(q, k, v, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, window_left, scale,
+                    n_threads);
 }

@@ -1,5 +1,5 @@
 /*
- * attn_ref.h -- fp64 CPU oracle for the tiled flash-attention forward pass.
+ * attn_ref.h -- fp64 CPU oracle for the tiled flash-attention forward and backward passes.
  *
  * TEST INFRASTRUCTURE ONLY. This library is the checker, not the product:
  * only the test suite, the smoke check and the benchmark's CPU-baseline leg
@@ -63,6 +63,16 @@ int attn_ref_partial_f64(const double* q, const double* k, const double* v, doub
  * Rows whose partials are all empty (-inf) get o = 0, lse = -inf. */
 int lse_combine_ref_f64(const double* o_part, const double* lse_part, int S, long rows, int d,
                         double* o, double* lse);
+
+/* Gradients of exact attention, fp64: given the output gradient dout (layout of
+ * o), returns dq (layout of q) and dk, dv (layout of k, v) of L = <dout, o>,
+ * o = attn(q, k, v) with the mask of attn_ref_f64 (fixed key length Sk). The
+ * chain rule through the softmax, with no tiling; dk and dv of a KV head sum
+ * over the query heads of its group. Rows with no visible key contribute
+ * nothing. Returns 0, or -1 on bad arguments. */
+int attn_bwd_ref_f64(const double* q, const double* k, const double* v, const double* dout,
+                     double* dq, double* dk, double* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                     int d, int causal, int window_left, double scale, int n_threads);
 
 #ifdef __cplusplus
 }

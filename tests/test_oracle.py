@@ -305,3 +305,129 @@ def test_value_width_constant_keys_average_values():
     for i in range(3):
         hi = i + 7  # causal, delta = 7
         np.testing.assert_allclose(o[0, i, 2], v64[0, :hi + 1, 0].mean(axis=0), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# backward pass (attn_bwd_ref): gradients of L = <dout, attn(q, k, v)>
+# ---------------------------------------------------------------------------
+BWD_MASKS = [(False, -1), (True, -1), (True, 2), (False, 3)]
+
+
+def _bwd_inputs(seed, B, Hq, Hkv, Sq, Sk, d):
+    q, k, v = small_case(seed, "fp32", B, Hq, Hkv, Sq, Sk, d)
+    rng = np.random.default_rng(seed + 101)
+    g = rng.standard_normal((B, Sq, Hq, d))
+    return q.double().numpy(), k.double().numpy(), v.double().numpy(), g
+
+
+def _loss(q, k, v, g, causal, wl, scale):
+    o, _ = oracle.attn_ref(q, k, v, causal, wl, scale)
+    return float(np.sum(o * g))
+
+
+@pytest.mark.parametrize("causal,wl", BWD_MASKS)
+@pytest.mark.parametrize("Sq,Sk", [(3, 5), (6, 4)])
+def test_bwd_matches_finite_differences(causal, wl, Sq, Sk):
+    # Central differences of the forward oracle, entry by entry (error O(h^2)).
+    # (6, 4) with a causal mask has rows that see no key: their gradient is 0.
+    q, k, v, g = _bwd_inputs(3, 1, 2, 1, Sq, Sk, 3)
+    scale = 0.7
+    dq, dk, dv = oracle.attn_bwd_ref(q, k, v, g, causal, wl, scale)
+    h = 1e-5
+    for x, grad in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            up = _loss(q, k, v, g, causal, wl, scale)
+            x[idx] = old - h
+            dn = _loss(q, k, v, g, causal, wl, scale)
+            x[idx] = old
+            assert abs((up - dn) / (2 * h) - grad[idx]) < 1e-7, idx
+
+
+def _torch_attn_fp64(q, k, v, causal, wl, scale):
+    """Explicitly masked softmax attention with torch fp64 ops (GQA by repeating
+    the KV heads); rows with no visible key give 0."""
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    kk = k.repeat_interleave(G, dim=2)
+    vv = v.repeat_interleave(G, dim=2)
+    s = torch.einsum("bihc,bjhc->bhij", q, kk) * scale
+    delta = Sk - Sq
+    mask = torch.ones(Sq, Sk, dtype=torch.bool)
+    if causal:
+        mask &= torch.tril(torch.ones(Sq, Sk, dtype=torch.bool), diagonal=delta)
+    if wl >= 0:
+        mask &= torch.triu(torch.ones(Sq, Sk, dtype=torch.bool), diagonal=delta - wl)
+    rowok = mask.any(dim=-1)
+    s = torch.where(mask, s, torch.tensor(float("-inf"), dtype=s.dtype))
+    s = torch.where(rowok[:, None], s, torch.zeros((), dtype=s.dtype))
+    p = torch.softmax(s, dim=-1) * rowok[:, None].to(s.dtype)
+    return torch.einsum("bhij,bjhc->bihc", p, vv)
+
+
+@pytest.mark.parametrize("causal,wl", BWD_MASKS + [(True, 0)])
+def test_bwd_against_torch_autograd(causal, wl):
+    # A library routine: torch autograd (fp64, CPU) through an explicitly masked
+    # softmax, GQA with group 3, Sq > Sk so that causal masks empty some rows.
+    q, k, v, g = _bwd_inputs(5, 2, 6, 2, 13, 9, 16)
+    scale = 0.25
+    dq, dk, dv = oracle.attn_bwd_ref(q, k, v, g, causal, wl, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = _torch_attn_fp64(tq, tk, tv, causal, wl, scale)
+    (o * torch.tensor(g)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("causal,wl", BWD_MASKS)
+def test_bwd_invariants(causal, wl):
+    q, k, v, g = _bwd_inputs(9, 2, 4, 2, 7, 11, 8)
+    scale = 0.4
+    dq, dk, dv = oracle.attn_bwd_ref(q, k, v, g, causal, wl, scale)
+    # Shifting every key of a head by one vector moves all scores of a row by the
+    # same amount, so the key gradients of a head sum to zero.
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    # Each row's probabilities sum to one: the value gradients of a KV head sum
+    # to the output gradients of the rows (of its query heads) that see a key.
+    vis = oracle.visible_mask(7, 11, causal, wl)
+    rows = vis.any(axis=1)
+    G = 2
+    for hkv in range(2):
+        want = g[:, rows][:, :, hkv * G:(hkv + 1) * G].sum(axis=(1, 2))
+        np.testing.assert_allclose(dv[:, :, hkv].sum(axis=1), want, atol=1e-12)
+    # A constant added to every value row shifts each output by that constant,
+    # whatever the probabilities: dq and dk do not change.
+    dq2, dk2, dv2 = oracle.attn_bwd_ref(q, k, v + np.arange(8) * 0.37, g, causal, wl, scale)
+    np.testing.assert_allclose(dq2, dq, atol=1e-12)
+    np.testing.assert_allclose(dk2, dk, atol=1e-12)
+    np.testing.assert_allclose(dv2, dv, atol=1e-12)
+
+
+def test_bwd_identical_keys_give_zero_query_gradient():
+    # With every key equal, each visible score of a row ties whatever q is, so
+    # the output does not depend on q.
+    q, k, v, g = _bwd_inputs(11, 1, 2, 1, 6, 9, 8)
+    k[:] = k[:, :1]
+    for causal, wl in BWD_MASKS:
+        dq, _, _ = oracle.attn_bwd_ref(q, k, v, g, causal, wl, 0.9)
+        np.testing.assert_allclose(dq, 0.0, atol=1e-12)
+
+
+def test_bwd_block_ranges_visit_the_printed_block_count():
+    # The backward loop (key block outside, the query blocks that see it inside,
+    # "分块策略与调度" §3.4) visits the same (query block, key block) pairs as the
+    # forward loop: 528 of 1024 for the causal example of §3.3.
+    gd = json.load(open(os.path.join(GOLDEN, "causal_block_count.json")))
+    N, bm, bn = gd["N"], gd["block_m"], gd["block_n"]
+    mr = oracle.needed_m_block_range(N, N, True, -1, bm, bn)
+    assert sum(hi - lo for lo, hi in mr) == gd["blocks_computed"]
+    for Sq, Sk, causal, wl, BM, BN in [(37, 53, True, -1, 8, 16), (53, 37, True, 5, 16, 8),
+                                       (40, 40, False, 7, 8, 8), (9, 30, True, 0, 4, 4)]:
+        fwd = oracle.needed_block_range(Sq, Sk, causal, wl, BM, BN)
+        bwd = oracle.needed_m_block_range(Sq, Sk, causal, wl, BM, BN)
+        pf = {(m, n) for m, r in enumerate(fwd) if r for n in range(*r)}
+        pb = {(m, n) for n, r in enumerate(bwd) if r for m in range(*r)}
+        assert pf == pb

@@ -150,3 +150,24 @@ def random_partials(seed: int, S: int, rows: int, d: int, p_empty: float = 0.25)
     lse[empty] = float("-inf")
     o[empty] = 0.0
     return o, lse
+
+
+# Backward workloads: the two bf16 prefill shapes above, run through the
+# backward pass (the pages describe its loop order and scheduler but measure no
+# backward workload, so the forward's prefill shapes stand in).
+BWD_WORKLOADS = {
+    "causal_prefill_bwd_bf16": WORKLOADS["causal_prefill_bf16"].replace(name="causal_prefill_bwd_bf16"),
+    "window_prefill_bwd_bf16": WORKLOADS["window_prefill_bf16"].replace(name="window_prefill_bwd_bf16"),
+}
+
+
+def output_grad(seed: int, shape, dtype: str = "bf16", std: float = 1.0, device=None):
+    """Random output gradient dO of the given shape ([B, Sq, Hq, d]) from its own
+    seeded generator (seed + 7919, so it is independent of the q, k, v draw of the
+    same seed); N(0, 1) * std in fp32, rounded on the CPU to the dtype."""
+    g = torch.Generator("cpu").manual_seed(int(seed) + 7919)
+    t = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    t = t.to(torch.float32 if dtype == "fp32" else torch.bfloat16)
+    return t.to(device) if device is not None else t
