@@ -6,7 +6,8 @@
  *     O = softmax(scale * Q K^T + mask) V,     lse = log sum_j exp(scale q.k_j)
  * as a tiled flash-attention forward pass with online softmax, block skipping
  * for causal / sliding-window masks, GQA packing and split-KV with a separate
- * log-sum-exp combine kernel.
+ * log-sum-exp combine kernel, and its gradients (tpattn_bwd) with the
+ * key-block-outer backward loop.
  *
  * Sources (page title, section):
  *   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling):
@@ -38,9 +39,11 @@
  *     asynchronous on the stream and never synchronise the device, except
  *     that growing the internal split workspace synchronises once.
  *   Ownership: all tensors belong to the caller; the library never frees
- *     them. Split partials go to a library-owned device workspace (one per
- *     device, grown on demand, released at unload); calls that use it on the
- *     same device are serialised by a lock, so the library is thread-safe.
+ *     them. Split partials (and the backward's dQ accumulator and row sums) go
+ *     to a library-owned device workspace (one per device, grown on demand,
+ *     released at unload). Host threads are serialised on it by a lock, so the
+ *     library is thread-safe; on the GPU, calls on one device that use it must
+ *     not overlap (issue them on one stream, or order the streams).
  *   Errors: a negative status code; nothing is launched and the message is
  *     available from tpattn_last_error() (thread-local). Argument checks never
  *     touch the GPU.
@@ -129,6 +132,37 @@ int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, i
                     int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
                     tpattn_plan* out);
 
+/* Backward pass: gradients of L = <dout, o> for o = attention(q, k, v) with the
+ * mask of tpattn_fwd ([FA-tiling] §3.4: one workgroup per key block, looping
+ * over the query blocks that see it -- get_m_block_min_max -- and the query
+ * heads of its KV head; §4.6: Q, dO and an fp32 dQ accumulator are the working
+ * set). Inputs: q, k, v as tpattn_fwd; o and lse the forward's outputs for
+ * them (lse natural log, [B][Hq][Sq], -inf for rows that see no key); dout the
+ * output gradient in o's layout. Outputs: dq in q's layout, dk and dv in k's
+ * layout, all in `dtype` (dk, dv sum over the G query heads of a KV head).
+ * Three kernels: row sums D = <dout, o> (which also zero the accumulator), the
+ * main kernel (dK, dV in registers, dQ by fp32 atomics), and dQ = scale * acc.
+ * dQ's summation order depends on atomic timing, so its last bits can vary
+ * from run to run. Sizes and errors as tpattn_fwd (d in {64, 128}; no
+ * num_splits). */
+int tpattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+               int Sk, int d, int causal, int window_left, float scale, int dtype, void* stream);
+
+/* What tpattn_bwd would launch (host only). */
+typedef struct tpattn_bwd_plan {
+    int block_m;         /* query rows per inner block                                     */
+    int block_n;         /* keys per workgroup                                             */
+    int num_n_blocks;    /* key blocks per (batch, KV head)                                */
+    int grid_x;          /* workgroups of the main kernel: num_n_blocks * Hkv * B          */
+    int threads;         /* threads per workgroup                                          */
+    int lds_bytes;       /* LDS per workgroup                                              */
+    long long visited_blocks;  /* (query block, key block) pairs visited, all heads        */
+    size_t workspace_bytes;    /* fp32 dQ accumulator + lse2 + row sums                    */
+} tpattn_bwd_plan;
+int tpattn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    int dtype, tpattn_bwd_plan* out);
+
 /* Split workspace bytes for B*Sq*Hq rows of head dim d and num_splits splits
  * (fp32 partial outputs plus fp32 partial lse). */
 size_t tpattn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits);
@@ -160,6 +194,11 @@ int tpattn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int bl
  * whose wave efficiency reaches 0.85 of the best. */
 int tpattn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
                           long long size_one_kv_head, int is_causal_or_local, int max_splits);
+/* [FA-tiling] §3.4 get_m_block_min_max: query-block range [m_min, m_max) whose
+ * rows see a key of key block n_block (fixed key length Sk; empty if
+ * m_max <= m_min). */
+int tpattn_m_block_range(int Sq, int Sk, int causal, int window_left, int block_m, int block_n,
+                         int n_block, int* m_min, int* m_max);
 /* The plan tpattn_fwd_dv would use (host only). */
 int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
                        int window_left, int num_splits, int dtype, int num_cus,
@@ -183,6 +222,10 @@ int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_
 int tpattn_profile_begin(int max_launches);
 int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
                        int* combine_launches, double* prep_ms, int* prep_launches);
+/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 5) with
+ * kinds 0 forward, 1 combine, 2 V pre-pass / counter reset, 3 backward main
+ * kernel, 4 backward pre- and post-passes. */
+int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds);
 
 /* Message of the last failure on this thread ("" if none). */
 const char* tpattn_last_error(void);

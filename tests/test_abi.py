@@ -92,3 +92,22 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         tpa.fwd(q, q, q)
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
+             Hq=4, Hkv=2, Sq=8, Sk=8, d=64, causal=0, wl=-1, scale=0.125, dtype=tpa.BF16)
+    a.update(kw)
+    return tpa.load().tpattn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                 a["d"], a["causal"], a["wl"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(do=None), -1), (dict(lse=None), -1), (dict(dq=None), -1),
+    (dict(dk=None), -1), (dict(v=None), -1), (dict(Hq=6, Hkv=4), -1), (dict(d=96), -2),
+    (dict(dtype=5), -2), (dict(wl=-3), -1), (dict(scale=-1.0), -1), (dict(Sk=-2), -1),
+])
+def test_bwd_bad_arguments_are_rejected_without_launch(kw, code):
+    assert _bwd(**kw) == code
+    assert tpa.load().tpattn_last_error().decode() != ""

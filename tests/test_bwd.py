@@ -1,0 +1,161 @@
+"""GPU parity of the backward pass (tpattn_bwd) against the fp64 oracle.
+
+The forward (o, lse) comes from the library's own forward kernels, as in
+training; the gradients are compared with attn_bwd_ref on the same seeded
+inputs and output gradient.
+
+Tolerances (per gradient tensor; scale = max |ref| of that tensor):
+  fp32: max |x - ref| <= 2e-5 * max(1, scale): fp32 products and sums end to end.
+  bf16: max |x - ref| <= 2e-2 * max(scale, 5e-3), and |x - ref| / |ref| <= 5e-2
+      where |ref| > 0.1 * scale. (The floor covers gradients that vanish exactly,
+      e.g. dq when each row sees a single key: the kernel's dP - D then cancels
+      to fp32 rounding, about 1e-6.) The kernel rounds P and dS to bf16 before their
+      matrix products (2^-9 relative each), reads D = <dO, O> from the bf16
+      forward output, and rounds the results to bf16; a CPU emulation of exactly
+      those roundings against the oracle gave at most 0.6% of scale and 1.7%
+      relative on five shapes (causal, window, GQA, d 64/128), and the limits
+      leave a factor of about three for the forward's own bf16 error in O.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_prefill_amd as tpa
+from workloads import BWD_WORKLOADS, make_inputs, output_grad, small_case
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def assert_grad_parity(x, ref, dtype, what):
+    x = x.detach().float().cpu().double().numpy()
+    assert x.shape == ref.shape, what
+    assert np.isfinite(x).all(), f"{what}: non-finite values"
+    err = np.abs(x - ref)
+    scale = float(np.abs(ref).max(initial=0.0))
+    if dtype == "fp32":
+        assert err.max(initial=0.0) <= 2e-5 * max(1.0, scale), f"{what}: max abs {err.max()}"
+        return
+    assert err.max(initial=0.0) <= 2e-2 * max(scale, 5e-3), \
+        f"{what}: max abs {err.max()} vs scale {scale}"
+    big = np.abs(ref) > 0.1 * scale
+    if scale > 0 and big.any():
+        rel = (err[big] / np.abs(ref[big])).max()
+        assert rel <= 5e-2, f"{what}: max rel {rel}"
+
+
+def bwd_case(dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl, seed=0, std=1.0):
+    q, k, v = small_case(seed, dtype, B, Hq, Hkv, Sq, Sk, d, std=std)
+    g = output_grad(seed, q.shape, dtype)
+    scale = 1.0 / math.sqrt(d)
+    tag = f"bwd {dtype} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} d={d} causal={causal} wl={wl}"
+    print(tag, flush=True)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    o, lse = tpa.fwd(qd, kd, vd, causal=causal, window_left=wl, scale=scale)
+    dq, dk, dv = tpa.bwd(qd, kd, vd, o, gd, lse, causal=causal, window_left=wl, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd_ref(q, k, v, g, causal, wl, scale)
+    assert_grad_parity(dq, rq, dtype, tag + " dq")
+    assert_grad_parity(dk, rk, dtype, tag + " dk")
+    assert_grad_parity(dv, rv, dtype, tag + " dv")
+    return dq, dk, dv
+
+
+BWD_SMALL = [
+    # dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl
+    ("bf16", 1, 4, 4, 200, 200, 128, True, -1),
+    ("bf16", 1, 8, 2, 130, 300, 128, True, 50),
+    ("bf16", 2, 4, 2, 100, 77, 64, False, -1),
+    ("bf16", 1, 4, 4, 300, 100, 128, True, -1),
+    ("bf16", 1, 2, 1, 1, 500, 128, False, -1),
+    ("bf16", 1, 2, 2, 65, 65, 128, False, 10),
+    ("bf16", 3, 6, 3, 40, 40, 64, True, 0),
+    ("bf16", 1, 2, 2, 1, 1, 128, False, -1),
+    ("bf16", 2, 8, 2, 257, 1025, 128, True, 300),
+    ("fp32", 1, 4, 2, 33, 70, 64, True, 5),
+    ("fp32", 2, 2, 2, 20, 150, 128, False, -1),
+    ("fp32", 1, 4, 4, 90, 60, 64, True, -1),
+    ("fp32", 1, 2, 2, 130, 130, 128, True, 17),
+    ("fp32", 1, 3, 1, 64, 64, 128, False, -1),
+]
+
+
+@pytest.mark.parametrize("case", BWD_SMALL)
+def test_bwd_small_shapes(case):
+    bwd_case(*case, seed=4)
+
+
+@pytest.mark.parametrize("bn", [64, 128])
+def test_bwd_key_block_variants(bn, monkeypatch):
+    # both bf16 key-block widths (16 and 32 keys per wave)
+    monkeypatch.setenv("TPATTN_BWD_BN", str(bn))
+    bwd_case("bf16", 1, 4, 2, 190, 333, 128, True, -1, seed=6)
+    bwd_case("bf16", 1, 4, 2, 190, 333, 64, True, 70, seed=6)
+
+
+def test_bwd_empty_sizes():
+    # no query rows: dk = dv = 0; no keys: dq = 0
+    for dtype in ("bf16", "fp32"):
+        td = torch.bfloat16 if dtype == "bf16" else torch.float32
+        q = torch.randn(1, 0, 4, 128, device=DEV).to(td)
+        k = torch.randn(1, 50, 2, 128, device=DEV).to(td)
+        v = torch.randn(1, 50, 2, 128, device=DEV).to(td)
+        o = torch.zeros_like(q)
+        lse = torch.zeros(1, 4, 0, device=DEV)
+        print(f"bwd empty Sq {dtype}", flush=True)
+        dq, dk, dv = tpa.bwd(q, k, v, o, o.clone(), lse)
+        torch.cuda.synchronize()
+        assert dk.abs().max().item() == 0 and dv.abs().max().item() == 0
+        q = torch.randn(1, 7, 4, 128, device=DEV).to(td)
+        k = torch.randn(1, 0, 2, 128, device=DEV).to(td)
+        o, lse = tpa.fwd(q, k, k.clone())
+        print(f"bwd empty Sk {dtype}", flush=True)
+        dq, dk, dv = tpa.bwd(q, k, k.clone(), o, torch.ones_like(q), lse)
+        torch.cuda.synchronize()
+        assert dq.abs().max().item() == 0
+
+
+def test_bwd_repeated_calls_reuse_the_accumulator():
+    # the dQ accumulator lives in the shared workspace: a second call (smaller
+    # problem, after a forward that uses split partials) must start from zero
+    a = bwd_case("bf16", 1, 4, 4, 128, 128, 128, True, -1, seed=8)
+    w = small_case(9, "bf16", 1, 32, 4, 1, 1000, 128)
+    tpa.fwd(*(t.to(DEV) for t in w))
+    b = bwd_case("bf16", 1, 4, 4, 128, 128, 128, True, -1, seed=8)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x.float().cpu().numpy(), y.float().cpu().numpy(),
+                                   rtol=0, atol=1e-2)
+
+
+def _head_slice(t, lo, hi):
+    return t[:, :, lo:hi].contiguous()
+
+
+@pytest.mark.parametrize("name", list(BWD_WORKLOADS))
+def test_bwd_full_size_sampled_heads(name):
+    # the full-size workloads, in the launch configuration the benchmark times;
+    # whole gradients of a few (batch, KV head) groups are recomputed by the
+    # oracle on those heads alone
+    w = BWD_WORKLOADS[name]
+    q, k, v, _ = make_inputs(w, seed=0)
+    g = output_grad(0, q.shape, w.dtype)
+    print(f"{name} full size", flush=True)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV)
+    o, lse = tpa.fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left)
+    dq, dk, dv = tpa.bwd(qd, kd, vd, o, gd, lse, causal=w.causal, window_left=w.window_left)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, hkv in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+        print(f"{name} oracle on batch {b} KV head {hkv}", flush=True)
+        sl = lambda t, lo, hi: t[b:b + 1, :, lo:hi].contiguous()
+        rq, rk, rv = oracle.attn_bwd_ref(sl(q, hkv * G, (hkv + 1) * G), sl(k, hkv, hkv + 1),
+                                         sl(v, hkv, hkv + 1), sl(g, hkv * G, (hkv + 1) * G),
+                                         w.causal, w.window_left, w.scale)
+        tag = f"{name} b={b} hkv={hkv}"
+        assert_grad_parity(sl(dq, hkv * G, (hkv + 1) * G), rq, w.dtype, tag + " dq")
+        assert_grad_parity(sl(dk, hkv, hkv + 1), rk, w.dtype, tag + " dk")
+        assert_grad_parity(sl(dv, hkv, hkv + 1), rv, w.dtype, tag + " dv")

@@ -155,3 +155,44 @@ def test_persistent_grid_is_resident_workgroups(monkeypatch):
     monkeypatch.setenv("TPATTN_PREFILL_PERSIST", "0")
     p = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
     assert p["grid_x"] == 1024 and p["workspace_bytes"] == 0
+
+
+# ---------------------------------------------------------------------------
+# backward: query-block range of each key block ([FA-tiling] §3.4)
+# ---------------------------------------------------------------------------
+M_CASES = [
+    (64, 64, True, -1, 16, 16), (37, 53, True, -1, 8, 16), (53, 37, True, 5, 16, 8),
+    (40, 40, False, 7, 8, 8), (9, 30, True, 0, 4, 4), (100, 100, False, -1, 64, 64),
+    (130, 129, True, 33, 64, 64), (1, 300, True, -1, 64, 64), (300, 1, True, -1, 64, 64),
+    (17, 2065, True, -1, 64, 64), (200, 150, False, 20, 64, 32),
+]
+
+
+@pytest.mark.parametrize("case", M_CASES)
+def test_m_block_range_matches_brute_force(case):
+    Sq, Sk, causal, wl, BM, BN = case
+    want = oracle.needed_m_block_range(Sq, Sk, causal, wl, BM, BN)
+    for n, w in enumerate(want):
+        lo, hi = tpa.m_block_range(Sq, Sk, causal, wl, BM, BN, n)
+        if w is None:
+            assert hi <= lo, (n, lo, hi)
+        else:
+            assert (lo, hi) == w, (n, lo, hi, w)
+
+
+def test_bwd_plan_visits_the_printed_block_count_and_the_forward_pairs():
+    g = json.load(open(os.path.join(GOLDEN, "causal_block_count.json")))
+    N, bm, bn = g["N"], g["block_m"], g["block_n"]
+    total = sum(max(0, hi - lo) for lo, hi in
+                (tpa.m_block_range(N, N, True, -1, bm, bn, n) for n in range(N // bn)))
+    assert total == g["blocks_computed"]
+    for name in ("causal_prefill_bf16", "window_prefill_bf16"):
+        w = WORKLOADS[name]
+        p = tpa.plan_bwd(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, w.dtype)
+        fwd = oracle.needed_block_range(w.Sq, w.Sk, w.causal, w.window_left,
+                                        p["block_m"], p["block_n"])
+        pairs = sum(hi - lo for r in fwd if r for lo, hi in [r])
+        assert p["visited_blocks"] == pairs * w.Hq * w.B
+        assert p["grid_x"] == p["num_n_blocks"] * w.Hkv * w.B
+        rows = w.B * w.Sq * w.Hq
+        assert p["workspace_bytes"] >= rows * (w.d + 2) * 4

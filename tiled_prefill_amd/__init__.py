@@ -1,4 +1,5 @@
-"""Python binding of libtpattn.so, the MI355X tiled flash-attention forward library.
+"""Python binding of libtpattn.so, the MI355X tiled flash-attention library
+(forward pass, split-KV combine, and backward pass).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C-ABI declared in include/tpattn.h. PyTorch provides
@@ -48,6 +49,17 @@ class Plan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class BwdPlan(ctypes.Structure):
+    _fields_ = [
+        ("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("num_n_blocks", ctypes.c_int),
+        ("grid_x", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+        ("visited_blocks", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -90,6 +102,14 @@ def load():
     dp = ctypes.POINTER(ctypes.c_double)
     lib.tpattn_profile_end.argtypes = [dp, ip, dp, ip, dp, ip]
     lib.tpattn_profile_end.restype = i
+    lib.tpattn_profile_end_kinds.argtypes = [dp, ip, i]
+    lib.tpattn_profile_end_kinds.restype = i
+    lib.tpattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.tpattn_bwd.restype = i
+    lib.tpattn_plan_bwd.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(BwdPlan)]
+    lib.tpattn_plan_bwd.restype = i
+    lib.tpattn_m_block_range.argtypes = [i, i, i, i, i, i, i, ip, ip]
+    lib.tpattn_m_block_range.restype = i
     lib.tpattn_last_error.argtypes = []
     lib.tpattn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -201,6 +221,55 @@ def fwd_varlen(q, k, v, seqlens_k: torch.Tensor, causal: bool = False, window_le
     return out, lse
 
 
+def bwd(q, k, v, o, dout, lse, causal: bool = False, window_left: int = -1,
+        scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+        dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, stream=None):
+    """Attention backward on the GPU (tpattn_bwd). o and lse are the forward's outputs
+    for (q, k, v); dout the gradient of o. Returns (dq, dk, dv) in the dtype of q."""
+    _check_tensors(q, k, v)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    for name, t in (("o", o), ("dout", dout)):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the shape and dtype of q")
+    if not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32
+            and lse.shape == (B, Hq, Sq)):
+        raise ValueError("lse must be a contiguous fp32 GPU tensor of shape [B, Hq, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor like {name[1:]}")
+    rc = load().tpattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+                           float(scale), _dtype_code(q), _stream_ptr(stream))
+    _check(rc)
+    return dq, dk, dv
+
+
+def plan_bwd(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, dtype="bf16") -> dict:
+    """The backward plan (host only)."""
+    p = BwdPlan()
+    code = FP32 if dtype in ("fp32", FP32, torch.float32) else BF16
+    _check(load().tpattn_plan_bwd(B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+                                  code, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def m_block_range(Sq, Sk, causal, window_left, block_m, block_n, n_block):
+    """get_m_block_min_max: query-block range of key block n_block (host mirror)."""
+    lo, hi = ctypes.c_int(), ctypes.c_int()
+    _check(load().tpattn_m_block_range(Sq, Sk, int(bool(causal)), window_left, block_m, block_n,
+                                       n_block, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
 def lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
                 lse: Optional[torch.Tensor], B: int, Sq: int, Hq: int, stream=None):
     """Merge split partials o_part [S, B*Sq*Hq, d] fp32, lse_part [S, B*Sq*Hq] into out/lse."""
@@ -273,6 +342,21 @@ def num_splits_occupancy(tiles, num_cus, n_blocks, block_n, min_chunk_rows=256, 
 
 def profile_begin(max_launches: int = 4096):
     _check(load().tpattn_profile_begin(int(max_launches)))
+
+
+KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost")
+
+
+def profile_end_kinds() -> dict:
+    """Summed event time (ms) and launch count of every kernel kind since profile_begin."""
+    ms = (ctypes.c_double * 5)()
+    n = (ctypes.c_int * 5)()
+    _check(load().tpattn_profile_end_kinds(ms, n, 5))
+    out = {}
+    for i, name in enumerate(KINDS):
+        out[name + "_ms"] = ms[i]
+        out[name + "_launches"] = n[i]
+    return out
 
 
 def profile_end() -> dict:

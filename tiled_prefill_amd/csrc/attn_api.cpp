@@ -330,12 +330,32 @@ struct Workspace {
 };
 Workspace g_ws[64];
 
+// The per-device workspace, at least `bytes` long (caller holds ws.mu).
+int ensure_workspace(Workspace& ws, size_t bytes) {
+    if (ws.bytes >= bytes) return TPATTN_OK;
+    if (ws.ptr) {
+        (void)hipDeviceSynchronize();  // earlier calls may still use the old buffer
+        (void)hipFree(ws.ptr);
+        ws.ptr = nullptr;
+        ws.bytes = 0;
+    }
+    hipError_t e = hipMalloc(&ws.ptr, bytes);
+    if (e != hipSuccess) {
+        ws.ptr = nullptr;
+        return fail(TPATTN_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    }
+    ws.bytes = bytes;
+    return TPATTN_OK;
+}
+
+
 struct Profiler {
     std::mutex mu;
     bool on = false;
     int max_launches = 0;
     std::vector<hipEvent_t> ev;  // pairs
-    std::vector<int> kind;       // 0 forward, 1 combine, 2 V pre-pass
+    std::vector<int> kind;       // 0 forward, 1 combine, 2 V pre-pass / counters,
+                                 // 3 backward main kernel, 4 backward pre/post passes
     int used = 0;
 } g_prof;
 
@@ -410,21 +430,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         return fail(TPATTN_EHIP, "hipGetDevice failed");
     Workspace& ws = g_ws[dev];
     std::lock_guard<std::mutex> lk(ws.mu);
-    if (ws.bytes < pl.workspace_bytes) {
-        if (ws.ptr) {
-            (void)hipDeviceSynchronize();  // earlier calls may still read the old buffer
-            (void)hipFree(ws.ptr);
-            ws.ptr = nullptr;
-            ws.bytes = 0;
-        }
-        hipError_t e = hipMalloc(&ws.ptr, pl.workspace_bytes);
-        if (e != hipSuccess) {
-            ws.ptr = nullptr;
-            return fail(TPATTN_ENOMEM, "split workspace of %zu bytes: %s", pl.workspace_bytes,
-                        hipGetErrorString(e));
-        }
-        ws.bytes = pl.workspace_bytes;
-    }
+    rc = ensure_workspace(ws, pl.workspace_bytes);
+    if (rc) return rc;
     const size_t rows = (size_t)pr.B * pr.Sq * pr.Hq;
     fp.o_part = reinterpret_cast<float*>(ws.ptr);
     const int dvv = pr.dv > 0 ? pr.dv : pr.d;
@@ -467,6 +474,126 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     e = launch_combine(cp, dvv, pr.dtype == TPATTN_BF16, stream);
     prof_stop(slot, stream);
     if (e != hipSuccess) return fail(TPATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
+    return TPATTN_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// backward pass ([FA-tiling] §3.4, §4.6)
+// ---------------------------------------------------------------------------
+struct BwdPlan {
+    tpattn_bwd_plan pub;
+    const BwdVariant* var;
+    size_t lse2_offset = 0, dsum_offset = 0;  // byte offsets in the workspace
+};
+
+int make_bwd_plan(const Problem& p, BwdPlan* out) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    // key block: 64 keys (16 per wave) unless TPATTN_BWD_BN asks for 128 (bf16)
+    const int want_bn = env_int("TPATTN_BWD_BN", 64);
+    const BwdVariant* var = nullptr;
+    for (int pass = 0; pass < 2 && !var; ++pass)
+        for (const BwdVariant* v = bwd_variants(); v->launch; ++v)
+            if (v->dtype == p.dtype && v->d == p.d && (pass == 1 || v->block_n == want_bn)) {
+                var = v;
+                break;
+            }
+    if (!var) return fail(TPATTN_EUNSUPPORTED, "no backward kernel for dtype %d d %d", p.dtype, p.d);
+    const int G = p.Hq / p.Hkv;
+    tpattn_bwd_plan& q = out->pub;
+    q = tpattn_bwd_plan{};
+    q.block_m = var->block_m;
+    q.block_n = var->block_n;
+    q.threads = 256;
+    q.lds_bytes = var->lds_bytes;
+    q.num_n_blocks = ceil_div(imax(p.Sk, 0), var->block_n);
+    const long long grid = (long long)q.num_n_blocks * p.Hkv * p.B;
+    if (grid > 0x7fffffffLL) return fail(TPATTN_EINVAL, "too many key blocks");
+    q.grid_x = (int)grid;
+    long long visited = 0;
+    for (int n = 0; n < q.num_n_blocks; ++n) {
+        int lo, hi;
+        m_block_range(p.Sq, p.Sk, p.causal, p.window_left, var->block_m, var->block_n, n, &lo, &hi);
+        visited += imax(0, hi - lo);
+    }
+    q.visited_blocks = visited * G * (long long)p.Hkv * p.B;
+    const size_t rows = (size_t)p.B * p.Sq * p.Hq;
+    const size_t acc = rows * (size_t)p.d * sizeof(float);
+    out->lse2_offset = (acc + 255) & ~(size_t)255;
+    out->dsum_offset = (out->lse2_offset + rows * sizeof(float) + 255) & ~(size_t)255;
+    q.workspace_bytes = rows ? out->dsum_offset + rows * sizeof(float) : 0;
+    out->var = var;
+    return TPATTN_OK;
+}
+
+int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* o,
+            const void* dout, const float* lse, void* dq, void* dk, void* dv, void* stream_v) {
+    const bool has_rows = pr.B > 0 && pr.Sq > 0;
+    const bool has_keys = pr.B > 0 && pr.Sk > 0;
+    if (has_rows && (!q || !o || !dout || !lse || !dq))
+        return fail(TPATTN_EINVAL, "null q, o, dout, lse or dq pointer");
+    if (has_keys && (!k || !v || !dk || !dv)) return fail(TPATTN_EINVAL, "null k, v, dk or dv pointer");
+    BwdPlan plan;
+    int rc = make_bwd_plan(pr, &plan);
+    if (rc) return rc;
+    if (!has_rows && !has_keys) return TPATTN_OK;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+
+    BwdParams bp{};
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.o = o;
+    bp.dout = dout;
+    bp.lse = lse;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.B = pr.B;
+    bp.Hq = pr.Hq;
+    bp.Hkv = pr.Hkv;
+    bp.Sq = pr.Sq;
+    bp.Sk = pr.Sk;
+    bp.G = pr.Hq / pr.Hkv;
+    bp.causal = pr.causal ? 1 : 0;
+    bp.window_left = pr.window_left;
+    bp.scale = pr.scale;
+    bp.scale_log2 = pr.scale * 1.4426950408889634f;
+    bp.num_n_blocks = plan.pub.num_n_blocks;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(TPATTN_EHIP, "hipGetDevice failed");
+    Workspace& ws = g_ws[dev];
+    std::lock_guard<std::mutex> lk(ws.mu);
+    if (plan.pub.workspace_bytes > 0) {
+        rc = ensure_workspace(ws, plan.pub.workspace_bytes);
+        if (rc) return rc;
+        bp.dq_acc = reinterpret_cast<float*>(ws.ptr);
+        bp.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + plan.lse2_offset);
+        bp.dsum = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + plan.dsum_offset);
+    }
+    hipError_t e;
+    int slot;
+    if (has_rows) {
+        slot = prof_start(4, stream);
+        e = plan.var->launch_pre(bp, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward pre-pass launch: %s", hipGetErrorString(e));
+    }
+    if (has_keys) {
+        slot = prof_start(3, stream);
+        e = plan.var->launch(bp, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward launch: %s", hipGetErrorString(e));
+    }
+    if (has_rows) {
+        slot = prof_start(4, stream);
+        e = plan.var->launch_post(bp, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward post-pass launch: %s", hipGetErrorString(e));
+    }
     return TPATTN_OK;
 }
 
@@ -521,6 +648,33 @@ int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, i
     int rc = make_plan(p, num_cus, &plan);
     if (rc) return rc;
     *out = plan.pub;
+    return TPATTN_OK;
+}
+
+int tpattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+               int Sk, int d, int causal, int window_left, float scale, int dtype, void* stream) {
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, 0, dtype, 0, 0, scale};
+    return run_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, stream);
+}
+
+int tpattn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    int dtype, tpattn_bwd_plan* out) {
+    if (!out) return fail(TPATTN_EINVAL, "null plan pointer");
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, 0, dtype, 0, 0, 1.0f};
+    BwdPlan plan;
+    int rc = make_bwd_plan(p, &plan);
+    if (rc) return rc;
+    *out = plan.pub;
+    return TPATTN_OK;
+}
+
+int tpattn_m_block_range(int Sq, int Sk, int causal, int window_left, int block_m, int block_n,
+                         int n_block, int* m_min, int* m_max) {
+    if (!m_min || !m_max) return fail(TPATTN_EINVAL, "null output pointer");
+    if (Sq < 0 || Sk < 0 || block_m < 1 || block_n < 1 || n_block < 0 || window_left < -1)
+        return fail(TPATTN_EINVAL, "bad block-range arguments");
+    m_block_range(Sq, Sk, causal, window_left, block_m, block_n, n_block, m_min, m_max);
     return TPATTN_OK;
 }
 
@@ -605,16 +759,15 @@ int tpattn_profile_begin(int max_launches) {
     return TPATTN_OK;
 }
 
-int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
-                       int* combine_launches, double* prep_ms, int* prep_launches) {
+int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    double t[3] = {0, 0, 0};
-    int n[3] = {0, 0, 0};
+    double t[5] = {0, 0, 0, 0, 0};
+    int n[5] = {0, 0, 0, 0, 0};
     for (int i = 0; i < g_prof.used; ++i) {
         if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) continue;
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) == hipSuccess) {
-            t[g_prof.kind[i]] += ms;
+        float e_ms = 0.f;
+        if (hipEventElapsedTime(&e_ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) == hipSuccess) {
+            t[g_prof.kind[i]] += e_ms;
             n[g_prof.kind[i]] += 1;
         }
     }
@@ -623,13 +776,25 @@ int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
     g_prof.kind.clear();
     g_prof.on = false;
     g_prof.used = 0;
+    for (int k = 0; k < n_kinds && k < 5; ++k) {
+        if (ms) ms[k] = t[k];
+        if (launches) launches[k] = n[k];
+    }
+    return TPATTN_OK;
+}
+
+int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
+                       int* combine_launches, double* prep_ms, int* prep_launches) {
+    double t[3];
+    int n[3];
+    int rc = tpattn_profile_end_kinds(t, n, 3);
     if (fwd_ms) *fwd_ms = t[0];
     if (fwd_launches) *fwd_launches = n[0];
     if (combine_ms) *combine_ms = t[1];
     if (combine_launches) *combine_launches = n[1];
     if (prep_ms) *prep_ms = t[2];
     if (prep_launches) *prep_launches = n[2];
-    return TPATTN_OK;
+    return rc;
 }
 
 const char* tpattn_last_error(void) { return g_last_error.c_str(); }

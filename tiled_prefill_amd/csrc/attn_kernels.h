@@ -37,6 +37,18 @@ hipError_t launch_v_to_f16t(const FwdParams& p, hipStream_t stream);
 // Zeroes the per-XCD tile queue counters of a persistent kernel.
 hipError_t launch_tile_counters_reset(int* counters, hipStream_t stream);
 
+// One compiled backward instantiation: element type, head dim, key block.
+struct BwdVariant {
+    int dtype, d;
+    int block_n;            // keys per workgroup
+    int block_m;            // query rows per inner block
+    int lds_bytes;
+    hipError_t (*launch)(const BwdParams&, hipStream_t stream);       // main kernel
+    hipError_t (*launch_pre)(const BwdParams&, hipStream_t stream);   // row sums, lse2, zero dQ acc
+    hipError_t (*launch_post)(const BwdParams&, hipStream_t stream);  // dQ = scale * acc
+};
+const BwdVariant* bwd_variants();  // null-terminated by launch == nullptr
+
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);
 

@@ -78,6 +78,46 @@ TPA_HD void split_range(int n_min, int n_max, int split, int splits, int* s_min,
     *s_max = imin(lo + per, n_max);
 }
 
+// Query-block range [m_min, m_max) whose rows see at least one key of key block
+// n_block: the backward pass's inverse of n_block_range ([FA-tiling] §3.4,
+// get_m_block_min_max). Row i sees key j iff j < Sk, and j <= i + delta if
+// causal, and j >= i + delta - window_left if window_left >= 0 (delta = Sk - Sq).
+// The first key of the block bounds the causal side, the last existing key the
+// window side. An empty range (m_max <= m_min) means no row sees the block.
+TPA_HD void m_block_range(int Sq, int Sk, int causal, int window_left, int BM, int BN,
+                          int n_block, int* m_min, int* m_max) {
+    const int k0 = n_block * BN;
+    const int k1 = imin((n_block + 1) * BN, Sk) - 1;  // last existing key of the block
+    const int delta = Sk - Sq;
+    int lo = 0, hi = ceil_div(imax(Sq, 0), BM);
+    if (k1 < k0) hi = 0;
+    if (causal) lo = imax(0, floor_div(k0 - delta, BM));
+    if (window_left >= 0) hi = imin(hi, imax(0, floor_div(k1 + window_left - delta, BM) + 1));
+    *m_min = lo;
+    *m_max = hi;
+}
+
+// Arguments of the backward kernels (passed by value).
+struct BwdParams {
+    const void* q;          // [B][Sq][Hq][d]
+    const void* k;          // [B][Sk][Hkv][d]
+    const void* v;          // [B][Sk][Hkv][d]
+    const void* o;          // [B][Sq][Hq][d], forward output
+    const void* dout;       // [B][Sq][Hq][d], gradient of the output
+    const float* lse;       // [B][Hq][Sq], forward log-sum-exp (natural log)
+    void* dq;               // [B][Sq][Hq][d]
+    void* dk;               // [B][Sk][Hkv][d]
+    void* dv;               // [B][Sk][Hkv][d]
+    float* dq_acc;          // [B][Sq][Hq][d] fp32 accumulator (workspace)
+    float* lse2;            // [B][Hq][Sq]: lse * log2(e); +inf for rows that see no key
+    float* dsum;            // [B][Hq][Sq]: rowsum(dO * O)
+    int B, Hq, Hkv, Sq, Sk, G;
+    int causal, window_left;
+    float scale;            // softmax scale
+    float scale_log2;       // scale * log2(e)
+    int num_n_blocks;       // key blocks per (batch, KV head)
+};
+
 // Arguments of the forward kernel (passed by value).
 struct FwdParams {
     const void* q;          // [B][Sq][Hq][d]
