@@ -174,6 +174,52 @@ def run_suite(args):
         print(json.dumps(rec), flush=True)
         del ks, vs, q, k, v, o
     run_latent_suite(args)
+    run_bwd_suite(args)
+
+
+def run_bwd_suite(args):
+    """Backward workloads (tpattn_bwd) on the prefill shapes: TFLOP/s over the five
+    matrix products of the backward (10 d flops per visible pair)."""
+    import torch
+    import tiled_prefill_amd as tpa
+    from workloads import BWD_WORKLOADS, make_inputs, output_grad
+    dev = "cuda:0"
+    for name, w in BWD_WORKLOADS.items():
+        if args.workload and name != args.workload:
+            continue
+        q, k, v, _ = make_inputs(w, seed=0, device=dev)
+        g = output_grad(0, q.shape, w.dtype, device=dev)
+        o, lse = tpa.fwd(q, k, v, causal=w.causal, window_left=w.window_left)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        flops = 10.0 * w.d * visible_pairs(w)
+
+        def step(i=0):
+            tpa.bwd(q, k, v, o, g, lse, causal=w.causal, window_left=w.window_left,
+                    dq=dq, dk=dk, dv=dv)
+
+        warm(step, 3)
+        steps = max(5, min(200, args.prefill_steps * 2))
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        tpa.profile_begin(4 * steps + 8)
+        for i in range(steps):
+            step(i)
+        prof = tpa.profile_end_kinds()
+        plan = tpa.plan_bwd(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, w.dtype)
+        n = max(1, prof["bwd_launches"])
+        rec = {"workload": name, "dtype": w.dtype, "ms_per_step": round(ms, 5),
+               "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+               "pct_mfma_bf16": round(100 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+               "dkdv_us": round(1e3 * prof["bwd_ms"] / n, 2),
+               "dq_us": round(1e3 * prof["bwd_dq_ms"] / n, 2),
+               "pre_us": round(1e3 * prof["bwd_prepost_ms"] / n, 2),
+               "block_n": plan["block_n"], "block_m": plan["block_m"],
+               "dq_block_m": plan["dq_block_m"], "flops": flops, "steps": steps}
+        print(json.dumps(rec), flush=True)
+        del q, k, v, g, o, dq, dk, dv
 
 
 def run_latent_suite(args):

@@ -140,10 +140,12 @@ int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, i
  * them (lse natural log, [B][Hq][Sq], -inf for rows that see no key); dout the
  * output gradient in o's layout. Outputs: dq in q's layout, dk and dv in k's
  * layout, all in `dtype` (dk, dv sum over the G query heads of a KV head).
- * Three kernels: row sums D = <dout, o> (which also zero the accumulator), the
- * main kernel (dK, dV in registers, dQ by fp32 atomics), and dQ = scale * acc.
- * dQ's summation order depends on atomic timing, so its last bits can vary
- * from run to run. Sizes and errors as tpattn_fwd (d in {64, 128}; no
+ * Three kernels: row sums D = <dout, o>, the key-block kernel (dK, dV in
+ * registers), and a query-block kernel for dQ that recomputes S and dP (no
+ * atomics: the result is the same bits on every run). TPATTN_BWD_ATOMIC=1
+ * selects the single-pass form of the pages instead (dQ added to an fp32
+ * accumulator with atomics by the key-block kernel, then scaled; its last bits
+ * depend on atomic timing). Sizes and errors as tpattn_fwd (d in {64, 128}; no
  * num_splits). */
 int tpattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
@@ -157,8 +159,9 @@ typedef struct tpattn_bwd_plan {
     int grid_x;          /* workgroups of the main kernel: num_n_blocks * Hkv * B          */
     int threads;         /* threads per workgroup                                          */
     int lds_bytes;       /* LDS per workgroup                                              */
-    long long visited_blocks;  /* (query block, key block) pairs visited, all heads        */
-    size_t workspace_bytes;    /* fp32 dQ accumulator + lse2 + row sums                    */
+    int dq_block_m;      /* query rows per workgroup of the dQ kernel (0: atomic form)     */
+    long long visited_blocks;  /* (query block, key block) pairs of the key-block kernel   */
+    size_t workspace_bytes;    /* lse2 + row sums (+ the fp32 dQ accumulator, atomic form) */
 } tpattn_bwd_plan;
 int tpattn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
                     int dtype, tpattn_bwd_plan* out);
@@ -222,9 +225,9 @@ int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_
 int tpattn_profile_begin(int max_launches);
 int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
                        int* combine_launches, double* prep_ms, int* prep_launches);
-/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 5) with
- * kinds 0 forward, 1 combine, 2 V pre-pass / counter reset, 3 backward main
- * kernel, 4 backward pre- and post-passes. */
+/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 6) with
+ * kinds 0 forward, 1 combine, 2 V pre-pass / counter reset, 3 backward
+ * key-block kernel, 4 backward pre- and post-passes, 5 backward dQ kernel. */
 int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds);
 
 /* Message of the last failure on this thread ("" if none). */

@@ -89,12 +89,33 @@ def test_bwd_small_shapes(case):
     bwd_case(*case, seed=4)
 
 
-@pytest.mark.parametrize("bn", [64, 128])
-def test_bwd_key_block_variants(bn, monkeypatch):
-    # both bf16 key-block widths (16 and 32 keys per wave)
-    monkeypatch.setenv("TPATTN_BWD_BN", str(bn))
+@pytest.mark.parametrize("env", [
+    {"TPATTN_BWD_BN": "128"},                              # 32 keys per wave
+    {"TPATTN_BWD_DQ_ROWS": "128"},                         # 128-row dQ blocks
+    {"TPATTN_BWD_ATOMIC": "1"},                            # dQ by fp32 atomics
+    {"TPATTN_BWD_ATOMIC": "1", "TPATTN_BWD_BN": "128"},
+])
+def test_bwd_variants(env, monkeypatch):
+    # the selectable variants (ablations) on ragged, masked, GQA shapes
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    print(f"bwd variant {env}", flush=True)
     bwd_case("bf16", 1, 4, 2, 190, 333, 128, True, -1, seed=6)
     bwd_case("bf16", 1, 4, 2, 190, 333, 64, True, 70, seed=6)
+    bwd_case("fp32", 1, 4, 2, 70, 90, 128, False, 20, seed=6)
+
+
+def test_bwd_is_deterministic():
+    # the default (two-pass) form has no atomics: repeated calls give the same bits
+    q, k, v = (t.to(DEV) for t in small_case(12, "bf16", 1, 8, 2, 300, 300, 128))
+    g = output_grad(12, q.shape, "bf16", device=DEV)
+    o, lse = tpa.fwd(q, k, v, causal=True)
+    print("bwd determinism", flush=True)
+    first = tpa.bwd(q, k, v, o, g, lse, causal=True)
+    for _ in range(3):
+        again = tpa.bwd(q, k, v, o, g, lse, causal=True)
+        for x, y in zip(first, again):
+            assert torch.equal(x, y)
 
 
 def test_bwd_empty_sizes():

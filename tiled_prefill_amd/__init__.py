@@ -53,7 +53,8 @@ class BwdPlan(ctypes.Structure):
     _fields_ = [
         ("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("num_n_blocks", ctypes.c_int),
         ("grid_x", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
-        ("visited_blocks", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t),
+        ("dq_block_m", ctypes.c_int), ("visited_blocks", ctypes.c_longlong),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
     def as_dict(self):
@@ -344,14 +345,14 @@ def profile_begin(max_launches: int = 4096):
     _check(load().tpattn_profile_begin(int(max_launches)))
 
 
-KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost")
+KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost", "bwd_dq")
 
 
 def profile_end_kinds() -> dict:
     """Summed event time (ms) and launch count of every kernel kind since profile_begin."""
-    ms = (ctypes.c_double * 5)()
-    n = (ctypes.c_int * 5)()
-    _check(load().tpattn_profile_end_kinds(ms, n, 5))
+    ms = (ctypes.c_double * len(KINDS))()
+    n = (ctypes.c_int * len(KINDS))()
+    _check(load().tpattn_profile_end_kinds(ms, n, len(KINDS)))
     out = {}
     for i, name in enumerate(KINDS):
         out[name + "_ms"] = ms[i]

@@ -355,7 +355,8 @@ struct Profiler {
     int max_launches = 0;
     std::vector<hipEvent_t> ev;  // pairs
     std::vector<int> kind;       // 0 forward, 1 combine, 2 V pre-pass / counters,
-                                 // 3 backward main kernel, 4 backward pre/post passes
+                                 // 3 backward key-block kernel, 4 backward pre/post
+                                 // passes, 5 backward dQ kernel
     int used = 0;
 } g_prof;
 
@@ -490,12 +491,17 @@ struct BwdPlan {
 int make_bwd_plan(const Problem& p, BwdPlan* out) {
     int rc = check_problem(p);
     if (rc) return rc;
-    // key block: 64 keys (16 per wave) unless TPATTN_BWD_BN asks for 128 (bf16)
+    // key block: 64 keys (16 per wave) unless TPATTN_BWD_BN asks for 128 (bf16);
+    // dQ by a second kernel unless TPATTN_BWD_ATOMIC=1 (fp32 atomics, ablation)
     const int want_bn = env_int("TPATTN_BWD_BN", 64);
+    const int want_atomic = env_int("TPATTN_BWD_ATOMIC", 0) ? 1 : 0;
+    const int want_dq_rows = env_int("TPATTN_BWD_DQ_ROWS", 0);  // 0: first listed
     const BwdVariant* var = nullptr;
     for (int pass = 0; pass < 2 && !var; ++pass)
         for (const BwdVariant* v = bwd_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && (pass == 1 || v->block_n == want_bn)) {
+            if (v->dtype == p.dtype && v->d == p.d && v->atomic_dq == want_atomic &&
+                (pass == 1 || (v->block_n == want_bn &&
+                               (want_dq_rows == 0 || v->atomic_dq || v->dq_block_m == want_dq_rows)))) {
                 var = v;
                 break;
             }
@@ -518,8 +524,9 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
         visited += imax(0, hi - lo);
     }
     q.visited_blocks = visited * G * (long long)p.Hkv * p.B;
+    q.dq_block_m = var->atomic_dq ? 0 : var->dq_block_m;
     const size_t rows = (size_t)p.B * p.Sq * p.Hq;
-    const size_t acc = rows * (size_t)p.d * sizeof(float);
+    const size_t acc = var->atomic_dq ? rows * (size_t)p.d * sizeof(float) : 0;
     out->lse2_offset = (acc + 255) & ~(size_t)255;
     out->dsum_offset = (out->lse2_offset + rows * sizeof(float) + 255) & ~(size_t)255;
     q.workspace_bytes = rows ? out->dsum_offset + rows * sizeof(float) : 0;
@@ -570,7 +577,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     if (plan.pub.workspace_bytes > 0) {
         rc = ensure_workspace(ws, plan.pub.workspace_bytes);
         if (rc) return rc;
-        bp.dq_acc = reinterpret_cast<float*>(ws.ptr);
+        if (plan.var->atomic_dq) bp.dq_acc = reinterpret_cast<float*>(ws.ptr);
         bp.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + plan.lse2_offset);
         bp.dsum = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + plan.dsum_offset);
     }
@@ -588,11 +595,16 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
         prof_stop(slot, stream);
         if (e != hipSuccess) return fail(TPATTN_EHIP, "backward launch: %s", hipGetErrorString(e));
     }
-    if (has_rows) {
+    if (has_rows && plan.var->atomic_dq) {
         slot = prof_start(4, stream);
         e = plan.var->launch_post(bp, stream);
         prof_stop(slot, stream);
         if (e != hipSuccess) return fail(TPATTN_EHIP, "backward post-pass launch: %s", hipGetErrorString(e));
+    } else if (has_rows) {
+        slot = prof_start(5, stream);
+        e = plan.var->launch_dq(bp, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward dQ launch: %s", hipGetErrorString(e));
     }
     return TPATTN_OK;
 }
@@ -761,8 +773,8 @@ int tpattn_profile_begin(int max_launches) {
 
 int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    double t[5] = {0, 0, 0, 0, 0};
-    int n[5] = {0, 0, 0, 0, 0};
+    double t[6] = {0, 0, 0, 0, 0, 0};
+    int n[6] = {0, 0, 0, 0, 0, 0};
     for (int i = 0; i < g_prof.used; ++i) {
         if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) continue;
         float e_ms = 0.f;
@@ -776,7 +788,7 @@ int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     g_prof.kind.clear();
     g_prof.on = false;
     g_prof.used = 0;
-    for (int k = 0; k < n_kinds && k < 5; ++k) {
+    for (int k = 0; k < n_kinds && k < 6; ++k) {
         if (ms) ms[k] = t[k];
         if (launches) launches[k] = n[k];
     }

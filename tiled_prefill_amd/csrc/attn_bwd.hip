@@ -1,19 +1,28 @@
 // attn_bwd.hip -- gfx950 (MI355X) flash-attention backward kernels.
 //
-//   bwd_pre_kernel   per query row: the row sum D = <dO, O>, lse2 = lse * log2(e)
-//                    (+inf where the row sees no key), and zero for the row's
-//                    fp32 dQ accumulator.
-//   attn_bwd_kernel  one workgroup per (key block, KV head, batch): key blocks
-//                    outside, the query blocks that see them inside
-//                    ([FA-tiling] §3.4, get_m_block_min_max). Its K and V rows
-//                    stay in registers, and so do the dK and dV accumulators of
-//                    those rows, summed over the G query heads of the group;
-//                    each query block recomputes S and P from lse, then
-//                    dV += P^T dO, dK += dS^T Q and dQ += dS K on MFMA, the last
-//                    added to the fp32 dQ accumulator with atomics ([FA-tiling]
-//                    §4.6 names Q, dO and that accumulator as the backward's
-//                    working set).
-//   bwd_post_kernel  dQ = scale * accumulator, in the output dtype.
+//   bwd_pre_kernel      per query row: the row sum D = <dO, O>, lse2 = lse *
+//                       log2(e) (+inf where the row sees no key), and (atomic
+//                       form) zero for the row's fp32 dQ accumulator.
+//   attn_bwd_kernel     one workgroup per (key block, KV head, batch): key blocks
+//                       outside, the query blocks that see them inside
+//                       ([FA-tiling] §3.4, get_m_block_min_max). Its K and V rows
+//                       stay in registers, and so do the dK and dV accumulators
+//                       of those rows, summed over the G query heads of the
+//                       group; each query block recomputes S and P from lse,
+//                       then dV += P^T dO and dK += dS^T Q on MFMA.
+//   attn_bwd_dq_kernel  one workgroup per (query block, query head, batch),
+//                       looping over the key blocks that query block sees:
+//                       recomputes S and dP and forms dQ = dS K on MFMA.
+//   (atomic form)       the pages' single pass ([FA-tiling] §4.6: Q, dO and an
+//                       fp32 dQ accumulator are the backward's working set):
+//                       attn_bwd_kernel<.., ATOMIC> also forms dQ = dS K per
+//                       (query block, key block) pair and adds it to the
+//                       accumulator with fp32 atomics; bwd_post_kernel scales it.
+//                       On this GPU those atomics cost about three times all of
+//                       the matrix work (6.6 ms vs 2.2 ms without them on the
+//                       causal 8192 x 32-head workload), so the default recomputes
+//                       S and dP in the dQ kernel instead (40% more matrix work,
+//                       no atomics, the same bits on every run).
 //
 // The pages print no gradient formulas; the kernels implement the chain rule
 // through the softmax: dP = dO V^T, D_i = sum_j P_ij dP_ij = <dO_i, O_i>,
@@ -22,8 +31,9 @@
 // Citations:
 //   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
 //
-// Matrix-core layout (wave64, 16x16 MFMA tiles; lane = 16 lg + li). Each wave
-// owns NKW keys of the workgroup's key block. Per query block of BM = 64 rows:
+// Matrix-core layout of attn_bwd_kernel (wave64, 16x16 MFMA tiles; lane =
+// 16 lg + li). Each wave owns NKW keys of the workgroup's key block. Per query
+// block of BM = 64 rows:
 //   S  [q][key]  = Q . K^T     A = Q rows (LDS), B = K rows (registers)
 //   dP [q][key]  = dO . V^T    A = dO rows (LDS), B = V rows (registers)
 // so lane (li, lg) holds key li and query rows 4 lg .. 4 lg + 3 of every 16x16
@@ -31,7 +41,8 @@
 // query rows:
 //   dV^T [d][key] += dO^T . P    A = dO columns (LDS transpose reads), B = P
 //   dK^T [d][key] += Q^T . dS    A = Q columns, B = dS
-// dS^T goes to LDS, and after a barrier each wave computes 16 rows of
+// In the atomic form dS^T then goes to LDS, and after a barrier each wave
+// computes 16 rows of
 //   dQ [q][d] = dS . K           A = dS (transpose reads of dS^T), B = K columns
 // For fp32 the same products run on the 16x16x4 fp32 MFMA with per-lane LDS
 // reads in place of the transpose reads.
@@ -46,7 +57,7 @@
 
 namespace tpa {
 
-template <class T, int D, int NKW>
+template <class T, int D, int NKW, bool ATOMIC = false>
 struct BwdTile {
     static constexpr bool BF = std::is_same<T, bf16_t>::value;
     static constexpr int NW = 4, NTHR = 64 * NW;
@@ -64,8 +75,9 @@ struct BwdTile {
     static constexpr int DL = D / 4;            // fp32: d elements of one lane group
     static constexpr int KC = BF ? D / 32 : DL / 4;  // register chunks per key row
     static constexpr int Q_BYTES = BM * QST * ESZ;
-    static constexpr int K_BYTES = BN * QST * ESZ;
-    static constexpr int S_BYTES = BN * SST * ESZ;
+    // the K tile and the dS^T tile are needed only when dQ is accumulated here
+    static constexpr int K_BYTES = ATOMIC ? BN * QST * ESZ : 0;
+    static constexpr int S_BYTES = ATOMIC ? BN * SST * ESZ : 0;
     static constexpr int LDS_BYTES = 2 * Q_BYTES + K_BYTES + S_BYTES + 2 * BM * 4;
     static_assert(NKW % 16 == 0 && (!BF || BN % 32 == 0), "key slice must fill the MFMA");
     static_assert(QITEMS >= 1 && BM * CPR % NTHR == 0, "Q tile load must divide evenly");
@@ -102,9 +114,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) dot += of[e] * gf[e];
         }
-        float* acc = p.dq_acc + row * D + c * CE;
+        if (p.dq_acc) {
+            float* acc = p.dq_acc + row * D + c * CE;
 #pragma unroll
-        for (int e = 0; e < CE; e += 4) *reinterpret_cast<f32x4*>(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < CE; e += 4) *reinterpret_cast<f32x4*>(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
 #pragma unroll
     for (int off = TPR / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
@@ -138,9 +152,9 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(BwdParams p, long long n4
 // ---------------------------------------------------------------------------
 // main kernel
 // ---------------------------------------------------------------------------
-template <class T, int D, int NKW, int OCC>
+template <class T, int D, int NKW, int OCC, bool ATOMIC>
 __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
-    using C = BwdTile<T, D, NKW>;
+    using C = BwdTile<T, D, NKW, ATOMIC>;
     constexpr bool BF = C::BF;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, NQB = C::NQB, CE = C::CE;
     constexpr int QST = C::QST, SST = C::SST, CPR = C::CPR, KC = C::KC;
@@ -196,7 +210,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
             }
         }
     }
-    if (total > 0) {
+    if (ATOMIC && total > 0) {
 #pragma unroll
         for (int it = 0; it < C::KITEMS; ++it) {
             const int item = tid + it * C::NTHR;
@@ -387,6 +401,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
                 }
         }
 
+        if constexpr (ATOMIC) {
         // dS^T -> LDS: key row kw0 + 16 t + li, query rows 16 qb + 4 lg .. +3
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -439,9 +454,10 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
                 for (int u = 0; u < D / 16; ++u) unsafeAtomicAdd(dst + 16 * u, dqa[u][r]);
             }
         }
+            }
     }
 
-    // ---- dK = scale dK^T^T, dV: lane holds d = 16u + 4lg .. +3 of key kw0 + 16t + li
+    // ---- dK = scale (dK^T)^T, dV: lane holds d = 16u + 4lg .. +3 of key kw0 + 16t + li
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int key = key0 + kw0 + 16 * t + li;
@@ -459,6 +475,287 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
             } else {
                 *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.dk) + off + 16 * u) = kv;
                 *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.dv) + off + 16 * u) = vv;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel: one workgroup per (query block, query head, batch), looping over
+// the key blocks the query block sees (the forward's n_block_range, [FA-tiling]
+// §3.2). With the query rows on the MFMA N axis (lane li = query row):
+//   S^T  [key][q] = K . Q^T      A = K rows (LDS), B = Q (registers)
+//   dP^T [key][q] = V . dO^T     A = V rows (LDS), B = dO (registers)
+//   dS^T = P^T (dP^T - D),  P^T = exp2(S^T scale log2e - lse2)
+//   dQ^T [d][q]  += K^T . dS^T   A = K^T tile (LDS, stored transposed),
+//                                B = dS^T (the accumulators, in place)
+// Each wave owns NQW 16-row blocks of the query block.
+// ---------------------------------------------------------------------------
+template <class T, int D, int NQW>
+struct BwdDqTile {
+    static constexpr bool BF = std::is_same<T, bf16_t>::value;
+    static constexpr int NW = 4, NTHR = 64 * NW;
+    static constexpr int MW = 16 * NQW;         // query rows per wave
+    static constexpr int BM = NW * MW;          // query rows per workgroup
+    static constexpr int BN = 64;               // keys per tile
+    static constexpr int NT = BN / 16;
+    static constexpr int ESZ = sizeof(T);
+    static constexpr int CE = 16 / ESZ;
+    static constexpr int KST = D + CE;          // K, V tile row pitch (elements)
+    static constexpr int TST = BN + CE;         // K^T tile row pitch (elements)
+    static constexpr int CPR = D / CE;
+    static constexpr int GROUPS = (BN / 4) * CPR;                   // (4 rows x chunk) items
+    static constexpr int ITEMS = (GROUPS + NTHR - 1) / NTHR;
+    static constexpr int DL = D / 4;
+    static constexpr int QV = DL / CE;          // 16-byte chunks per lane per row
+    static constexpr int K_BYTES = BN * KST * ESZ;
+    static constexpr int KT_BYTES = D * TST * ESZ;
+    static constexpr int LDS_BYTES = 2 * K_BYTES + KT_BYTES;
+};
+
+template <class T, int D, int NQW, int OCC>
+__global__ void __launch_bounds__(256, OCC) attn_bwd_dq_kernel(BwdParams p) {
+    using C = BwdDqTile<T, D, NQW>;
+    constexpr bool BF = C::BF;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT, CE = C::CE, DL = C::DL, QV = C::QV;
+    constexpr int KST = C::KST, TST = C::TST, CPR = C::CPR, ITEMS = C::ITEMS;
+
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+    T* Ks = reinterpret_cast<T*>(smem);
+    T* Vs = reinterpret_cast<T*>(smem + C::K_BYTES);
+    T* KT = reinterpret_cast<T*>(smem + 2 * C::K_BYTES);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int num_m = ceil_div(p.Sq, BM);
+    // heaviest causal query blocks (the last ones) first ([FA-tiling] §4.4)
+    const int m_block = p.causal ? num_m - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int hq = blockIdx.y, b = blockIdx.z;
+    const int hkv = hq / p.G;
+    const int Sq = p.Sq, Sk = p.Sk, delta = Sk - Sq;
+
+    int n_lo, n_hi;
+    n_block_range(Sq, Sk, 1, 0, p.causal, p.window_left, BM, BN, m_block, &n_lo, &n_hi);
+
+    // this lane's query rows and their visible key interval [row_lo, row_hi]
+    int row_pos[NQW], row_lo[NQW], row_hi[NQW];
+    float l2[NQW], dsum[NQW];
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        const int pos = m_block * BM + wave * C::MW + 16 * qq + li;
+        row_pos[qq] = pos;
+        int lo = 0, hi = Sk - 1;
+        l2[qq] = INFINITY;
+        dsum[qq] = 0.f;
+        if (pos < Sq) {
+            if (p.window_left >= 0) lo = pos + delta - p.window_left;
+            if (p.causal) hi = imin(hi, pos + delta);
+            wlo = imax(wlo, lo);
+            whi = imin(whi, hi);
+            const size_t idx = ((size_t)b * p.Hq + hq) * Sq + pos;
+            l2[qq] = p.lse2[idx];
+            dsum[qq] = p.dsum[idx];
+        }
+        row_lo[qq] = lo;
+        row_hi[qq] = hi;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+
+    // Q and dO fragments: lane group lg holds d in [lg DL, (lg + 1) DL) of its row
+    u32x4 qf[NQW][QV], gf[NQW][QV];
+    const bool has_work = n_hi > n_lo;
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        const size_t off = (((size_t)b * Sq + row_pos[qq]) * p.Hq + hq) * D + lg * DL;
+#pragma unroll
+        for (int c = 0; c < QV; ++c) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qf[qq][c] = z;
+            gf[qq][c] = z;
+            if (row_pos[qq] < Sq && has_work) {
+                qf[qq][c] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.q) + off + c * CE);
+                gf[qq][c] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.dout) + off + c * CE);
+            }
+        }
+    }
+
+    f32x4 dqT[D / 16][NQW];
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u)
+#pragma unroll
+        for (int qq = 0; qq < NQW; ++qq) dqT[u][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float sl2 = p.scale_log2;
+
+    // K/V tile staging through registers: item = (4 key rows, 16-byte chunk)
+    const T* kbase = reinterpret_cast<const T*>(p.k) + ((size_t)b * Sk * p.Hkv + hkv) * D;
+    const T* vbase = reinterpret_cast<const T*>(p.v) + ((size_t)b * Sk * p.Hkv + hkv) * D;
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    u32x4 kst[ITEMS][4], vst[ITEMS][4];
+    auto load_tile = [&](int n) {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + it * C::NTHR;
+            const int c = item % CPR, rg = item / CPR;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = n * BN + 4 * rg + r;
+                u32x4 z = {0u, 0u, 0u, 0u};
+                kst[it][r] = z;
+                vst[it][r] = z;
+                if (item < C::GROUPS && key < Sk) {
+                    kst[it][r] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + c * CE);
+                    vst[it][r] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + c * CE);
+                }
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + it * C::NTHR;
+            if (item >= C::GROUPS) continue;
+            const int c = item % CPR, rg = item / CPR;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                *reinterpret_cast<u32x4*>(Ks + (4 * rg + r) * KST + c * CE) = kst[it][r];
+                *reinterpret_cast<u32x4*>(Vs + (4 * rg + r) * KST + c * CE) = vst[it][r];
+            }
+            if constexpr (BF) {
+                // chunk c holds d = 8c..8c+7 of keys 4rg..4rg+3: write K^T[d][4rg..4rg+3]
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int w = e >> 1;
+                    const uint32_t a0 = kst[it][0][w], a1 = kst[it][1][w];
+                    const uint32_t a2 = kst[it][2][w], a3 = kst[it][3][w];
+                    u32x2 pr;
+                    if (e & 1) {
+                        pr[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+                        pr[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+                    } else {
+                        pr[0] = (a0 & 0xffffu) | (a1 << 16);
+                        pr[1] = (a2 & 0xffffu) | (a3 << 16);
+                    }
+                    *reinterpret_cast<u32x2*>(KT + (8 * c + e) * TST + 4 * rg) = pr;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u32x4 col = {kst[it][0][e], kst[it][1][e], kst[it][2][e], kst[it][3][e]};
+                    *reinterpret_cast<u32x4*>(KT + (4 * c + e) * TST + 4 * rg) = col;
+                }
+            }
+        }
+    };
+
+    if (has_work) load_tile(n_hi - 1);
+    for (int n = n_hi - 1; n >= n_lo; --n) {
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        if (n > n_lo) load_tile(n - 1);
+
+        // S^T = K Q^T and dP^T = V dO^T
+        f32x4 sacc[NT][NQW], pacc[NT][NQW];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int qq = 0; qq < NQW; ++qq) {
+                sacc[t][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pacc[t][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int c = 0; c < QV; ++c) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + (16 * t + li) * KST + lg * DL + c * CE);
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(Vs + (16 * t + li) * KST + lg * DL + c * CE);
+#pragma unroll
+                for (int qq = 0; qq < NQW; ++qq) {
+                    if constexpr (BF) {
+                        sacc[t][qq] = mfma_bf16(kf, qf[qq][c], sacc[t][qq]);
+                        pacc[t][qq] = mfma_bf16(vf, gf[qq][c], pacc[t][qq]);
+                    } else {
+                        const f32x4 kv = __builtin_bit_cast(f32x4, kf), vv = __builtin_bit_cast(f32x4, vf);
+                        const f32x4 qv = __builtin_bit_cast(f32x4, qf[qq][c]);
+                        const f32x4 gv = __builtin_bit_cast(f32x4, gf[qq][c]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            sacc[t][qq] = mfma_f32(kv[e], qv[e], sacc[t][qq]);
+                            pacc[t][qq] = mfma_f32(vv[e], gv[e], pacc[t][qq]);
+                        }
+                    }
+                }
+            }
+        }
+
+        // P^T and dS^T; element mask only where the tile is not inside every row's interval
+        const int key0 = n * BN;
+        const bool full = key0 >= wlo && key0 + BN - 1 <= whi;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int qq = 0; qq < NQW; ++qq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float pv = fast_exp2(fmaf(sacc[t][qq][r], sl2, -l2[qq]));
+                    if (!full) {
+                        const int key = key0 + 16 * t + 4 * lg + r;
+                        pv = (key < row_lo[qq] || key > row_hi[qq]) ? 0.f : pv;
+                    }
+                    pacc[t][qq][r] = pv * (pacc[t][qq][r] - dsum[qq]);
+                }
+
+        // dQ^T += K^T dS^T
+        if constexpr (BF) {
+#pragma unroll
+            for (int pp = 0; pp < NT / 2; ++pp) {
+                u32x4 sb[NQW];
+#pragma unroll
+                for (int qq = 0; qq < NQW; ++qq)
+                    sb[qq] = u32x4{pack_bf16x2(pacc[2 * pp][qq][0], pacc[2 * pp][qq][1]),
+                                   pack_bf16x2(pacc[2 * pp][qq][2], pacc[2 * pp][qq][3]),
+                                   pack_bf16x2(pacc[2 * pp + 1][qq][0], pacc[2 * pp + 1][qq][1]),
+                                   pack_bf16x2(pacc[2 * pp + 1][qq][2], pacc[2 * pp + 1][qq][3])};
+#pragma unroll
+                for (int u = 0; u < D / 16; ++u) {
+                    const T* krow = KT + (16 * u + li) * TST + 32 * pp + 4 * lg;
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(krow);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(krow + 16);
+                    const u32x4 ka = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int qq = 0; qq < NQW; ++qq) dqT[u][qq] = mfma_bf16(ka, sb[qq], dqT[u][qq]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int u = 0; u < D / 16; ++u) {
+                    const f32x4 ka = *reinterpret_cast<const f32x4*>(KT + (16 * u + li) * TST + 16 * t + 4 * lg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int qq = 0; qq < NQW; ++qq)
+                            dqT[u][qq] = mfma_f32(ka[r], pacc[t][qq][r], dqT[u][qq]);
+                }
+        }
+    }
+
+    // dQ = scale (dQ^T)^T: lane holds d = 16u + 4lg .. +3 of row 16qq + li
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        if (row_pos[qq] >= Sq) continue;
+        const size_t off = (((size_t)b * Sq + row_pos[qq]) * p.Hq + hq) * D + 4 * lg;
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+            const f32x4 v = dqT[u][qq] * p.scale;
+            if constexpr (BF) {
+                *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.dq) + off + 16 * u) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.dq) + off + 16 * u) = v;
             }
         }
     }
@@ -486,28 +783,52 @@ hipError_t launch_bwd_post(const BwdParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <class T, int D, int NKW, int OCC>
+template <class T, int D, int NKW, int OCC, bool ATOMIC>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const long long grid = (long long)p.num_n_blocks * p.Hkv * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bwd_kernel<T, D, NKW, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_kernel<T, D, NKW, OCC, ATOMIC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-#define TPA_BWD_VARIANT(T, DT, D, NKW, OCC)                                                   \
-    {DT, D, BwdTile<T, D, NKW>::BN, BwdTile<T, D, NKW>::BM, BwdTile<T, D, NKW>::LDS_BYTES, \
-     &launch_bwd<T, D, NKW, OCC>, &launch_bwd_pre<T, D>, &launch_bwd_post<T, D>}
+template <class T, int D, int NQW, int OCC>
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
+    const int num_m = ceil_div(p.Sq, BwdDqTile<T, D, NQW>::BM);
+    if (num_m == 0 || p.B == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, NQW, OCC>), dim3(num_m, p.Hq, p.B), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
 
-// bf16: 64-key blocks (16 keys per wave), two workgroups per CU; fp32: 64-key
-// blocks, one workgroup per CU (its tiles take 117 KB of LDS).
+// dQ by fp32 atomics from the key-block kernel (ATOMIC, one pass) or by a
+// second, query-block-outer kernel (two passes, no atomics, deterministic).
+#define TPA_BWD_ATOMIC(T, DT, D, NKW, OCC)                                                       \
+    {DT, D, BwdTile<T, D, NKW, true>::BN, BwdTile<T, D, NKW, true>::BM,                          \
+     BwdTile<T, D, NKW, true>::LDS_BYTES, 1, &launch_bwd<T, D, NKW, OCC, true>,                  \
+     &launch_bwd_pre<T, D>, &launch_bwd_post<T, D>, nullptr, 0}
+#define TPA_BWD_TWO_PASS(T, DT, D, NKW, OCC, NQW, QOCC)                                          \
+    {DT, D, BwdTile<T, D, NKW>::BN, BwdTile<T, D, NKW>::BM, BwdTile<T, D, NKW>::LDS_BYTES, 0,    \
+     &launch_bwd<T, D, NKW, OCC, false>, &launch_bwd_pre<T, D>, nullptr,                        \
+     &launch_bwd_dq<T, D, NQW, QOCC>, BwdDqTile<T, D, NQW>::BM}
+
 static const BwdVariant kBwdVariants[] = {
-    TPA_BWD_VARIANT(bf16_t, DT_BF16, 128, 16, 2),
-    TPA_BWD_VARIANT(bf16_t, DT_BF16, 64, 16, 2),
-    TPA_BWD_VARIANT(bf16_t, DT_BF16, 128, 32, 1),
-    TPA_BWD_VARIANT(bf16_t, DT_BF16, 64, 32, 1),
-    TPA_BWD_VARIANT(float, DT_FP32, 128, 16, 1),
-    TPA_BWD_VARIANT(float, DT_FP32, 64, 16, 1),
-    {0, 0, 0, 0, 0, nullptr, nullptr, nullptr},
+    // two passes (default): 64-key blocks for dK/dV, 64-row blocks for dQ
+    // (measured faster than 128-row blocks, which hold one workgroup per CU)
+    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 16, 2, 1, 2),
+    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 16, 2, 1, 2),
+    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 16, 2, 2, 1),  // 128-row dQ blocks
+    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 16, 2, 2, 2),
+    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 32, 1, 2, 1),  // 128-key blocks
+    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 32, 1, 2, 2),
+    TPA_BWD_TWO_PASS(float, DT_FP32, 128, 16, 1, 1, 1),
+    TPA_BWD_TWO_PASS(float, DT_FP32, 64, 16, 1, 1, 2),
+    // dQ by atomics (ablation)
+    TPA_BWD_ATOMIC(bf16_t, DT_BF16, 128, 16, 2),
+    TPA_BWD_ATOMIC(bf16_t, DT_BF16, 64, 16, 2),
+    TPA_BWD_ATOMIC(bf16_t, DT_BF16, 128, 32, 1),
+    TPA_BWD_ATOMIC(bf16_t, DT_BF16, 64, 32, 1),
+    TPA_BWD_ATOMIC(float, DT_FP32, 128, 16, 1),
+    TPA_BWD_ATOMIC(float, DT_FP32, 64, 16, 1),
+    {0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, 0},
 };
 
 const BwdVariant* bwd_variants() { return kBwdVariants; }

@@ -40,12 +40,15 @@ hipError_t launch_tile_counters_reset(int* counters, hipStream_t stream);
 // One compiled backward instantiation: element type, head dim, key block.
 struct BwdVariant {
     int dtype, d;
-    int block_n;            // keys per workgroup
+    int block_n;            // keys per workgroup of the key-block kernel
     int block_m;            // query rows per inner block
     int lds_bytes;
-    hipError_t (*launch)(const BwdParams&, hipStream_t stream);       // main kernel
+    int atomic_dq;          // 1: dQ accumulated with fp32 atomics (needs the accumulator)
+    hipError_t (*launch)(const BwdParams&, hipStream_t stream);       // key-block kernel (dK, dV)
     hipError_t (*launch_pre)(const BwdParams&, hipStream_t stream);   // row sums, lse2, zero dQ acc
-    hipError_t (*launch_post)(const BwdParams&, hipStream_t stream);  // dQ = scale * acc
+    hipError_t (*launch_post)(const BwdParams&, hipStream_t stream);  // atomic_dq: dQ = scale * acc
+    hipError_t (*launch_dq)(const BwdParams&, hipStream_t stream);    // else: the dQ kernel
+    int dq_block_m;         // query rows per workgroup of the dQ kernel
 };
 const BwdVariant* bwd_variants();  // null-terminated by launch == nullptr
 
