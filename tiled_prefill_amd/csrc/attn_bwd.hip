@@ -762,6 +762,220 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dQ kernel, bf16: the same products with K and V tiles DMA'd straight into
+// double-buffered LDS (buffer_load ... lds), so a whole tile of work hides each
+// tile's load and no registers stage it. Each 16-byte chunk c of LDS row r sits
+// in slot c ^ swz(r); the S^T / dP^T operands are 16-byte row reads, and K^T
+// for dQ^T comes from the same K tile by transpose reads (ds_read_b64_tr_b16),
+// whose 8-byte pieces never straddle a chunk.
+// ---------------------------------------------------------------------------
+template <int D, int NQW>
+struct BwdDqDmaTile {
+    static constexpr int NW = 4, NTHR = 64 * NW;
+    static constexpr int MW = 16 * NQW, BM = NW * MW, BN = 64, NT = BN / 16;
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int ROWB = 2 * D;            // bytes per K / V row in LDS
+    static constexpr int TILEB = BN * ROWB;
+    static constexpr int STAGEB = 2 * TILEB;      // K + V
+    static constexpr int LDS_BYTES = 2 * STAGEB;
+    static constexpr int KROWS = 1024 / ROWB;     // rows per wave-wide DMA
+    static constexpr int KDMA = BN / KROWS;       // DMAs per tile
+    static constexpr int KDMA_PER_WAVE = KDMA / NW;
+    static constexpr int DL = D / 4, QV = DL / 8;
+    static_assert(KDMA % NW == 0, "tile DMAs must split evenly over the waves");
+    static __host__ __device__ __forceinline__ int swz(int r) {
+        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    }
+};
+
+template <int D, int NQW, int OCC>
+__global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) {
+    using C = BwdDqDmaTile<D, NQW>;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT, DL = C::DL, QV = C::QV;
+    constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int num_m = ceil_div(p.Sq, BM);
+    const int m_block = p.causal ? num_m - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int hq = blockIdx.y, b = blockIdx.z;
+    const int hkv = hq / p.G;
+    const int Sq = p.Sq, Sk = p.Sk, delta = Sk - Sq;
+
+    int n_lo, n_hi;
+    n_block_range(Sq, Sk, 1, 0, p.causal, p.window_left, BM, BN, m_block, &n_lo, &n_hi);
+    const bool has_work = n_hi > n_lo;
+
+    int row_pos[NQW], row_lo[NQW], row_hi[NQW];
+    float l2[NQW], dsum[NQW];
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        const int pos = m_block * BM + wave * C::MW + 16 * qq + li;
+        row_pos[qq] = pos;
+        int lo = 0, hi = Sk - 1;
+        l2[qq] = INFINITY;
+        dsum[qq] = 0.f;
+        if (pos < Sq) {
+            if (p.window_left >= 0) lo = pos + delta - p.window_left;
+            if (p.causal) hi = imin(hi, pos + delta);
+            wlo = imax(wlo, lo);
+            whi = imin(whi, hi);
+            const size_t idx = ((size_t)b * p.Hq + hq) * Sq + pos;
+            l2[qq] = p.lse2[idx];
+            dsum[qq] = p.dsum[idx];
+        }
+        row_lo[qq] = lo;
+        row_hi[qq] = hi;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+
+    u32x4 qf[NQW][QV], gf[NQW][QV];
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        const size_t off = (((size_t)b * Sq + row_pos[qq]) * p.Hq + hq) * D + lg * DL;
+#pragma unroll
+        for (int c = 0; c < QV; ++c) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qf[qq][c] = z;
+            gf[qq][c] = z;
+            if (row_pos[qq] < Sq && has_work) {
+                qf[qq][c] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(p.q) + off + 8 * c);
+                gf[qq][c] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(p.dout) + off + 8 * c);
+            }
+        }
+    }
+
+    f32x4 dqT[D / 16][NQW];
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u)
+#pragma unroll
+        for (int qq = 0; qq < NQW; ++qq) dqT[u][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float sl2 = p.scale_log2;
+
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * Sk * p.Hkv + hkv) * D;
+    // lane l of DMA i fills 16 bytes at 1024 i + 16 l: row KROWS i + l / CPR, slot
+    // l % CPR, which holds the row's chunk slot ^ swz(row); rows at or beyond Sk
+    // lie past the buffer resource and read as zeros
+    auto load_kv = [&](int n, int stage) {
+        const uint32_t bytes = (uint32_t)imin(BN, Sk - n * BN) * row_bytes;
+        const rsrc_t rk = make_rsrc(kbase + (size_t)n * BN * kv_stride, bytes);
+        const rsrc_t rv = make_rsrc(vbase + (size_t)n * BN * kv_stride, bytes);
+        char* dk = smem + stage * STAGEB;
+        char* dv = dk + TILEB;
+#pragma unroll
+        for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
+            const int i = wave * C::KDMA_PER_WAVE + j;
+            const int rr = C::KROWS * i + lane / CPR;
+            const uint32_t voff = rr * row_bytes + 16 * ((lane % CPR) ^ C::swz(rr));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (__attribute__((address_space(3))) void*)(dk + 1024 * i), 16, voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void*)(dv + 1024 * i), 16, voff, 0, 0, 0);
+        }
+    };
+
+    if (has_work) {
+        load_kv(n_hi - 1, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
+    }
+    __syncthreads();
+
+    int stage = 0;
+    for (int n = n_hi - 1; n >= n_lo; --n) {
+        if (n > n_lo) load_kv(n - 1, stage ^ 1);
+        const char* kt = smem + stage * STAGEB;
+        const char* vt = kt + TILEB;
+
+        // S^T = K Q^T and dP^T = V dO^T (lane group lg contracts d in [lg DL, (lg+1) DL))
+        f32x4 sacc[NT][NQW], pacc[NT][NQW];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int qq = 0; qq < NQW; ++qq) {
+                sacc[t][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pacc[t][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int c = 0; c < QV; ++c) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int row = 16 * t + li;
+                const int off = row * ROWB + 16 * ((lg * QV + c) ^ C::swz(row));
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + off);
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + off);
+#pragma unroll
+                for (int qq = 0; qq < NQW; ++qq) {
+                    sacc[t][qq] = mfma_bf16(kf, qf[qq][c], sacc[t][qq]);
+                    pacc[t][qq] = mfma_bf16(vf, gf[qq][c], pacc[t][qq]);
+                }
+            }
+        }
+
+        const int key0 = n * BN;
+        const bool full = key0 >= wlo && key0 + BN - 1 <= whi;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int qq = 0; qq < NQW; ++qq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float pv = fast_exp2(fmaf(sacc[t][qq][r], sl2, -l2[qq]));
+                    if (!full) {
+                        const int key = key0 + 16 * t + 4 * lg + r;
+                        pv = (key < row_lo[qq] || key > row_hi[qq]) ? 0.f : pv;
+                    }
+                    pacc[t][qq][r] = pv * (pacc[t][qq][r] - dsum[qq]);
+                }
+
+        // dQ^T += K^T dS^T: K^T by transpose reads of the K tile; source lane s
+        // of a 16-lane group addresses key row k0 + s / 4, columns 16u + 4 (s % 4)
+#pragma unroll
+        for (int pp = 0; pp < NT / 2; ++pp) {
+            u32x4 sb[NQW];
+#pragma unroll
+            for (int qq = 0; qq < NQW; ++qq)
+                sb[qq] = u32x4{pack_bf16x2(pacc[2 * pp][qq][0], pacc[2 * pp][qq][1]),
+                               pack_bf16x2(pacc[2 * pp][qq][2], pacc[2 * pp][qq][3]),
+                               pack_bf16x2(pacc[2 * pp + 1][qq][0], pacc[2 * pp + 1][qq][1]),
+                               pack_bf16x2(pacc[2 * pp + 1][qq][2], pacc[2 * pp + 1][qq][3])};
+            const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
+#pragma unroll
+            for (int u = 0; u < D / 16; ++u) {
+                const int ch = 2 * u + ((li & 3) >> 1);
+                const int o0 = r0 * ROWB + 16 * (ch ^ C::swz(r0)) + 8 * (li & 1);
+                const int o1 = r1 * ROWB + 16 * (ch ^ C::swz(r1)) + 8 * (li & 1);
+                const u32x2 lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(kt + o0));
+                const u32x2 hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(kt + o1));
+                const u32x4 ka = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int qq = 0; qq < NQW; ++qq) dqT[u][qq] = mfma_bf16(ka, sb[qq], dqT[u][qq]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
+        __syncthreads();
+        stage ^= 1;
+    }
+
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        if (row_pos[qq] >= Sq) continue;
+        const size_t off = (((size_t)b * Sq + row_pos[qq]) * p.Hq + hq) * D + 4 * lg;
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+            const f32x4 v = dqT[u][qq] * p.scale;
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.dq) + off + 16 * u) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers and the variant table
 // ---------------------------------------------------------------------------
 template <class T, int D>
@@ -791,6 +1005,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, int NQW, int OCC>
+hipError_t launch_bwd_dq_dma(const BwdParams& p, hipStream_t stream) {
+    const int num_m = ceil_div(p.Sq, BwdDqDmaTile<D, NQW>::BM);
+    if (num_m == 0 || p.B == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<D, NQW, OCC>), dim3(num_m, p.Hq, p.B), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <class T, int D, int NQW, int OCC>
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
     const int num_m = ceil_div(p.Sq, BwdDqTile<T, D, NQW>::BM);
@@ -804,19 +1026,27 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
 #define TPA_BWD_ATOMIC(T, DT, D, NKW, OCC)                                                       \
     {DT, D, BwdTile<T, D, NKW, true>::BN, BwdTile<T, D, NKW, true>::BM,                          \
      BwdTile<T, D, NKW, true>::LDS_BYTES, 1, &launch_bwd<T, D, NKW, OCC, true>,                  \
-     &launch_bwd_pre<T, D>, &launch_bwd_post<T, D>, nullptr, 0}
+     &launch_bwd_pre<T, D>, &launch_bwd_post<T, D>, nullptr, 0, 0}
 #define TPA_BWD_TWO_PASS(T, DT, D, NKW, OCC, NQW, QOCC)                                          \
     {DT, D, BwdTile<T, D, NKW>::BN, BwdTile<T, D, NKW>::BM, BwdTile<T, D, NKW>::LDS_BYTES, 0,    \
      &launch_bwd<T, D, NKW, OCC, false>, &launch_bwd_pre<T, D>, nullptr,                        \
-     &launch_bwd_dq<T, D, NQW, QOCC>, BwdDqTile<T, D, NQW>::BM}
+     &launch_bwd_dq<T, D, NQW, QOCC>, BwdDqTile<T, D, NQW>::BM, 0}
+
+#define TPA_BWD_TWO_PASS_DMA(D, NKW, OCC, NQW, QOCC)                                                  \
+    {DT_BF16, D, BwdTile<bf16_t, D, NKW>::BN, BwdTile<bf16_t, D, NKW>::BM,                          \
+     BwdTile<bf16_t, D, NKW>::LDS_BYTES, 0, &launch_bwd<bf16_t, D, NKW, OCC, false>,               \
+     &launch_bwd_pre<bf16_t, D>, nullptr, &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 1}
 
 static const BwdVariant kBwdVariants[] = {
-    // two passes (default): 64-key blocks for dK/dV, 64-row blocks for dQ
-    // (measured faster than 128-row blocks, which hold one workgroup per CU)
+    // two passes (default): 64-key blocks for dK/dV; bf16 dQ on DMA'd K/V tiles,
+    // 64-row blocks (16 rows per wave, two workgroups per CU)
+    TPA_BWD_TWO_PASS_DMA(128, 16, 2, 1, 2),
+    TPA_BWD_TWO_PASS_DMA(64, 16, 2, 1, 2),
+    TPA_BWD_TWO_PASS_DMA(128, 16, 2, 2, 1),  // 128-row dQ blocks, one workgroup per CU
+    TPA_BWD_TWO_PASS_DMA(64, 16, 2, 2, 2),
+    // register-staged dQ kernel (the fp32 path's kernel), as an ablation for bf16
     TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 16, 2, 1, 2),
     TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 16, 2, 1, 2),
-    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 16, 2, 2, 1),  // 128-row dQ blocks
-    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 16, 2, 2, 2),
     TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 32, 1, 2, 1),  // 128-key blocks
     TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 32, 1, 2, 2),
     TPA_BWD_TWO_PASS(float, DT_FP32, 128, 16, 1, 1, 1),
@@ -828,7 +1058,7 @@ static const BwdVariant kBwdVariants[] = {
     TPA_BWD_ATOMIC(bf16_t, DT_BF16, 64, 32, 1),
     TPA_BWD_ATOMIC(float, DT_FP32, 128, 16, 1),
     TPA_BWD_ATOMIC(float, DT_FP32, 64, 16, 1),
-    {0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, 0},
+    {0, 0, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, 0, 0},
 };
 
 const BwdVariant* bwd_variants() { return kBwdVariants; }
