@@ -195,4 +195,12 @@ def test_bwd_plan_visits_the_printed_block_count_and_the_forward_pairs():
         assert p["visited_blocks"] == pairs * w.Hq * w.B
         assert p["grid_x"] == p["num_n_blocks"] * w.Hkv * w.B
         rows = w.B * w.Sq * w.Hq
-        assert p["workspace_bytes"] >= rows * (w.d + 2) * 4
+        assert p["workspace_bytes"] >= rows * 2 * 4  # lse2 and the row sums
+
+
+def test_bwd_plan_atomic_form_needs_the_accumulator(monkeypatch):
+    w = WORKLOADS["causal_prefill_bf16"]
+    monkeypatch.setenv("TPATTN_BWD_ATOMIC", "1")
+    p = tpa.plan_bwd(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, w.dtype)
+    assert p["dq_block_m"] == 0
+    assert p["workspace_bytes"] >= w.B * w.Sq * w.Hq * (w.d + 2) * 4
