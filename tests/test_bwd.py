@@ -92,7 +92,8 @@ def test_bwd_small_shapes(case):
 @pytest.mark.parametrize("env", [
     {"TPATTN_BWD_BN": "128"},                              # 32 keys per wave
     {"TPATTN_BWD_DQ_ROWS": "128"},                         # 128-row dQ blocks
-    {"TPATTN_BWD_DQ_DMA": "0"},                            # register-staged dQ kernel
+    {"TPATTN_BWD_DMA": "1"},                               # register-staged query tiles
+    {"TPATTN_BWD_DMA": "0"},                               # register-staged tiles in both
     {"TPATTN_BWD_ATOMIC": "1"},                            # dQ by fp32 atomics
     {"TPATTN_BWD_ATOMIC": "1", "TPATTN_BWD_BN": "128"},
 ])

@@ -496,12 +496,13 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
     const int want_bn = env_int("TPATTN_BWD_BN", 64);
     const int want_atomic = env_int("TPATTN_BWD_ATOMIC", 0) ? 1 : 0;
     const int want_dq_rows = env_int("TPATTN_BWD_DQ_ROWS", 0);  // 0: first listed
-    const int want_dq_dma = env_int("TPATTN_BWD_DQ_DMA", 1);     // 0: register-staged dQ kernel
+    // 2: both kernels DMA their tiles; 1: only the dQ kernel; 0: neither
+    const int want_dq_dma = env_int("TPATTN_BWD_DMA", 2);
     const BwdVariant* var = nullptr;
     for (int pass = 0; pass < 2 && !var; ++pass)
         for (const BwdVariant* v = bwd_variants(); v->launch; ++v)
             if (v->dtype == p.dtype && v->d == p.d && v->atomic_dq == want_atomic &&
-                (pass == 1 || (v->block_n == want_bn && (want_dq_dma || !v->dq_dma) &&
+                (pass == 1 || (v->block_n == want_bn && v->dq_dma <= want_dq_dma &&
                                (want_dq_rows == 0 || v->atomic_dq || v->dq_block_m == want_dq_rows)))) {
                 var = v;
                 break;

@@ -976,6 +976,215 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
+// Key-block kernel, bf16, with the query-block tiles (Q, dO, and the rows'
+// lse2 and D) DMA'd into double-buffered LDS one block ahead. Q and dO serve
+// both as 16-byte row reads (the A operands of S and dP) and, by transpose
+// reads, as the column operands of dV^T and dK^T; chunk c of LDS row r sits in
+// slot c ^ swz(r). Query rows past Sq read as zeros (their Q and dO rows are 0,
+// so they add nothing whatever their P).
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdKvDmaTile {
+    static constexpr int NW = 4, NTHR = 64 * NW, NKW = 16;
+    static constexpr int BM = 64, BN = NW * NKW;
+    static constexpr int NQB = BM / 16;
+    static constexpr int CPR = D / 8, ROWB = 2 * D;
+    static constexpr int TILEB = BM * ROWB;
+    static constexpr int STAGEB = 2 * TILEB + 2 * BM * 4;   // Q, dO, lse2, D
+    static constexpr int LDS_BYTES = 2 * STAGEB;
+    static constexpr int KROWS = 1024 / ROWB, KDMA = BM / KROWS, KDMA_PER_WAVE = KDMA / NW;
+    static constexpr int KC = D / 32;
+    static_assert(KDMA % NW == 0, "tile DMAs must split evenly over the waves");
+    static __host__ __device__ __forceinline__ int swz(int r) {
+        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    }
+};
+
+template <int D, int OCC>
+__global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p) {
+    using C = BwdKvDmaTile<D>;
+    constexpr int BM = C::BM, BN = C::BN, NQB = C::NQB, KC = C::KC, NKW = C::NKW;
+    constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int bid = blockIdx.x;
+    const int hkv = bid % p.Hkv;
+    const int b = (bid / p.Hkv) % p.B;
+    const int nb = bid / (p.Hkv * p.B);
+    const int G = p.G, Sq = p.Sq, Sk = p.Sk;
+    const int delta = Sk - Sq;
+    const int key0 = nb * BN;
+    const int kw0 = wave * NKW;
+
+    int m_lo, m_hi;
+    m_block_range(Sq, Sk, p.causal, p.window_left, BM, BN, nb, &m_lo, &m_hi);
+    const int nm = imax(0, m_hi - m_lo);
+    const int total = G * nm;
+
+    // this wave's K and V rows as MFMA B fragments: key kw0 + li, d = 32c + 8lg..
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * Sk * p.Hkv + hkv) * D;
+    u32x4 kf[KC], vf[KC];
+    {
+        const int key = key0 + kw0 + li;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            kf[c] = z;
+            vf[c] = z;
+            if (key < Sk && total > 0) {
+                kf[c] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + 32 * c + 8 * lg);
+                vf[c] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + 32 * c + 8 * lg);
+            }
+        }
+    }
+    f32x4 dvT[D / 16], dkT[D / 16];
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+        dvT[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dkT[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const uint32_t row_bytes = (uint32_t)((size_t)p.Hq * D * 2);
+    // DMA of query block it into stage st: Q and dO rows (KDMA_PER_WAVE per wave
+    // each), then lse2 and D (one 4-byte-per-lane DMA each, waves 0 and 1)
+    auto load_block = [&](int it, int st) {
+        const int g = it / nm, m = m_lo + it % nm;
+        const int hq = hkv * G + g;
+        const int valid = imin(BM, Sq - m * BM);
+        const size_t row0 = ((size_t)b * Sq + m * BM) * p.Hq + hq;
+        const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16_t*>(p.q) + row0 * D, (uint32_t)valid * row_bytes);
+        const rsrc_t rg = make_rsrc(reinterpret_cast<const bf16_t*>(p.dout) + row0 * D, (uint32_t)valid * row_bytes);
+        char* dq_ = smem + st * STAGEB;
+        char* dg_ = dq_ + TILEB;
+#pragma unroll
+        for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
+            const int i = wave * C::KDMA_PER_WAVE + j;
+            const int rr = C::KROWS * i + lane / CPR;
+            const uint32_t voff = rr * row_bytes + 16 * ((lane % CPR) ^ C::swz(rr));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rq, (__attribute__((address_space(3))) void*)(dq_ + 1024 * i), 16, voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rg, (__attribute__((address_space(3))) void*)(dg_ + 1024 * i), 16, voff, 0, 0, 0);
+        }
+        if (wave < 2) {
+            const float* src = (wave == 0 ? p.lse2 : p.dsum) + ((size_t)b * p.Hq + hq) * Sq + m * BM;
+            const rsrc_t rl = make_rsrc(src, (uint32_t)valid * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rl, (__attribute__((address_space(3))) void*)(dg_ + TILEB + wave * BM * 4), 4,
+                4 * lane, 0, 0, 0);
+        }
+    };
+
+    if (total > 0) {
+        load_block(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __syncthreads();
+
+    const float sl2 = p.scale_log2;
+    int st = 0;
+    for (int it = 0; it < total; ++it) {
+        const int m = m_lo + it % nm;
+        if (it + 1 < total) load_block(it + 1, st ^ 1);
+        const char* qt = smem + st * STAGEB;
+        const char* gt = qt + TILEB;
+        const float* ls2 = reinterpret_cast<const float*>(gt + TILEB);
+        const float* lds_dsum = ls2 + BM;
+
+        // S = Q K^T and dP = dO V^T (contraction slot (lg, e) = d 32c + 8lg + e)
+        f32x4 sacc[NQB], pacc[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                const int row = 16 * qb + li;
+                const int off = row * ROWB + 16 * ((4 * c + lg) ^ C::swz(row));
+                const u32x4 qa = *reinterpret_cast<const u32x4*>(qt + off);
+                const u32x4 ga = *reinterpret_cast<const u32x4*>(gt + off);
+                sacc[qb] = mfma_bf16(qa, kf[c], sacc[qb]);
+                pacc[qb] = mfma_bf16(ga, vf[c], pacc[qb]);
+            }
+
+        // P and dS: lane holds key kw0 + li, query rows 16 qb + 4 lg .. +3
+        const int kk0 = key0 + kw0;
+        const int row0 = m * BM;
+        const int row1 = imin(row0 + BM, Sq) - 1;
+        const bool full = kk0 + NKW <= Sk && (!p.causal || kk0 + NKW - 1 <= row0 + delta) &&
+                          (p.window_left < 0 || kk0 >= row1 + delta - p.window_left);
+        const int key = kk0 + li;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(ls2 + 16 * qb + 4 * lg);
+            const f32x4 dsv = *reinterpret_cast<const f32x4*>(lds_dsum + 16 * qb + 4 * lg);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float pv = fast_exp2(fmaf(sacc[qb][r], sl2, -lv[r]));
+                if (!full) {
+                    const int pos = row0 + 16 * qb + 4 * lg + r;
+                    const bool vis = key < Sk && (!p.causal || key <= pos + delta) &&
+                                     (p.window_left < 0 || key >= pos + delta - p.window_left);
+                    pv = vis ? pv : 0.f;
+                }
+                sacc[qb][r] = pv;
+                pacc[qb][r] = pv * (pacc[qb][r] - dsv[r]);
+            }
+        }
+
+        // dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the dO and Q tiles)
+#pragma unroll
+        for (int pp = 0; pp < BM / 32; ++pp) {
+            const u32x4 pb = {pack_bf16x2(sacc[2 * pp][0], sacc[2 * pp][1]),
+                              pack_bf16x2(sacc[2 * pp][2], sacc[2 * pp][3]),
+                              pack_bf16x2(sacc[2 * pp + 1][0], sacc[2 * pp + 1][1]),
+                              pack_bf16x2(sacc[2 * pp + 1][2], sacc[2 * pp + 1][3])};
+            const u32x4 sb = {pack_bf16x2(pacc[2 * pp][0], pacc[2 * pp][1]),
+                              pack_bf16x2(pacc[2 * pp][2], pacc[2 * pp][3]),
+                              pack_bf16x2(pacc[2 * pp + 1][0], pacc[2 * pp + 1][1]),
+                              pack_bf16x2(pacc[2 * pp + 1][2], pacc[2 * pp + 1][3])};
+            const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
+#pragma unroll
+            for (int u = 0; u < D / 16; ++u) {
+                const int ch = 2 * u + ((li & 3) >> 1);
+                const int o0 = r0 * ROWB + 16 * (ch ^ C::swz(r0)) + 8 * (li & 1);
+                const int o1 = r1 * ROWB + 16 * (ch ^ C::swz(r1)) + 8 * (li & 1);
+                const u32x2 d0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(gt + o0));
+                const u32x2 d1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(gt + o1));
+                const u32x2 q0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(qt + o0));
+                const u32x2 q1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(qt + o1));
+                dvT[u] = mfma_bf16(u32x4{d0[0], d0[1], d1[0], d1[1]}, pb, dvT[u]);
+                dkT[u] = mfma_bf16(u32x4{q0[0], q0[1], q1[0], q1[1]}, sb, dkT[u]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next block has landed
+        __syncthreads();
+        st ^= 1;
+    }
+
+    // dK = scale (dK^T)^T, dV: lane holds d = 16u + 4lg .. +3 of key kw0 + li
+    const int key = key0 + kw0 + li;
+    if (key < Sk) {
+        const size_t off = (((size_t)b * Sk + key) * p.Hkv + hkv) * D + 4 * lg;
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) {
+            const f32x4 kv = dkT[u] * p.scale;
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.dk) + off + 16 * u) =
+                u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.dv) + off + 16 * u) =
+                u32x2{pack_bf16x2(dvT[u][0], dvT[u][1]), pack_bf16x2(dvT[u][2], dvT[u][3])};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers and the variant table
 // ---------------------------------------------------------------------------
 template <class T, int D>
@@ -1002,6 +1211,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const long long grid = (long long)p.num_n_blocks * p.Hkv * p.B;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((attn_bwd_kernel<T, D, NKW, OCC, ATOMIC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int OCC>
+hipError_t launch_bwd_dkdv_dma(const BwdParams& p, hipStream_t stream) {
+    const long long grid = (long long)p.num_n_blocks * p.Hkv * p.B;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1036,10 +1253,18 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
     {DT_BF16, D, BwdTile<bf16_t, D, NKW>::BN, BwdTile<bf16_t, D, NKW>::BM,                          \
      BwdTile<bf16_t, D, NKW>::LDS_BYTES, 0, &launch_bwd<bf16_t, D, NKW, OCC, false>,               \
      &launch_bwd_pre<bf16_t, D>, nullptr, &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 1}
+// both kernels on DMA'd tiles
+#define TPA_BWD_DMA(D, OCC, NQW, QOCC)                                                               \
+    {DT_BF16, D, BwdKvDmaTile<D>::BN, BwdKvDmaTile<D>::BM, BwdKvDmaTile<D>::LDS_BYTES, 0,          \
+     &launch_bwd_dkdv_dma<D, OCC>, &launch_bwd_pre<bf16_t, D>, nullptr,                           \
+     &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 2}
 
 static const BwdVariant kBwdVariants[] = {
-    // two passes (default): 64-key blocks for dK/dV; bf16 dQ on DMA'd K/V tiles,
-    // 64-row blocks (16 rows per wave, two workgroups per CU)
+    // two passes (default): both kernels on DMA'd tiles; 64-key blocks for dK/dV,
+    // 64-row blocks for dQ (16 rows per wave, two workgroups per CU)
+    TPA_BWD_DMA(128, 2, 1, 2),
+    TPA_BWD_DMA(64, 2, 1, 2),
+    // dK/dV with register-staged query tiles
     TPA_BWD_TWO_PASS_DMA(128, 16, 2, 1, 2),
     TPA_BWD_TWO_PASS_DMA(64, 16, 2, 1, 2),
     TPA_BWD_TWO_PASS_DMA(128, 16, 2, 2, 1),  // 128-row dQ blocks, one workgroup per CU

@@ -49,7 +49,7 @@ struct BwdVariant {
     hipError_t (*launch_post)(const BwdParams&, hipStream_t stream);  // atomic_dq: dQ = scale * acc
     hipError_t (*launch_dq)(const BwdParams&, hipStream_t stream);    // else: the dQ kernel
     int dq_block_m;         // query rows per workgroup of the dQ kernel
-    int dq_dma;             // 1: the dQ kernel DMAs K/V tiles into LDS (bf16)
+    int dq_dma;             // 1: the dQ kernel DMAs K/V tiles into LDS (bf16); 2: both kernels DMA their tiles
 };
 const BwdVariant* bwd_variants();  // null-terminated by launch == nullptr
 
