@@ -983,9 +983,10 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
 // slot c ^ swz(r). Query rows past Sq read as zeros (their Q and dO rows are 0,
 // so they add nothing whatever their P).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NKW_ = 16>
 struct BwdKvDmaTile {
-    static constexpr int NW = 4, NTHR = 64 * NW, NKW = 16;
+    static constexpr int NW = 4, NTHR = 64 * NW, NKW = NKW_;
+    static constexpr int NT = NKW / 16;           // 16-key blocks per wave
     static constexpr int BM = 64, BN = NW * NKW;
     static constexpr int NQB = BM / 16;
     static constexpr int CPR = D / 8, ROWB = 2 * D;
@@ -1000,10 +1001,10 @@ struct BwdKvDmaTile {
     }
 };
 
-template <int D, int OCC>
+template <int D, int NKW_, int OCC>
 __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p) {
-    using C = BwdKvDmaTile<D>;
-    constexpr int BM = C::BM, BN = C::BN, NQB = C::NQB, KC = C::KC, NKW = C::NKW;
+    using C = BwdKvDmaTile<D, NKW_>;
+    constexpr int BM = C::BM, BN = C::BN, NQB = C::NQB, KC = C::KC, NKW = C::NKW, NT = C::NT;
     constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
@@ -1023,30 +1024,33 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
     const int nm = imax(0, m_hi - m_lo);
     const int total = G * nm;
 
-    // this wave's K and V rows as MFMA B fragments: key kw0 + li, d = 32c + 8lg..
+    // this wave's K and V rows as MFMA B fragments: key kw0 + 16t + li, d = 32c + 8lg..
     const size_t kv_stride = (size_t)p.Hkv * D;
     const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * Sk * p.Hkv + hkv) * D;
     const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * Sk * p.Hkv + hkv) * D;
-    u32x4 kf[KC], vf[KC];
-    {
-        const int key = key0 + kw0 + li;
+    u32x4 kf[NT][KC], vf[NT][KC];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int key = key0 + kw0 + 16 * t + li;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             u32x4 z = {0u, 0u, 0u, 0u};
-            kf[c] = z;
-            vf[c] = z;
+            kf[t][c] = z;
+            vf[t][c] = z;
             if (key < Sk && total > 0) {
-                kf[c] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + 32 * c + 8 * lg);
-                vf[c] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + 32 * c + 8 * lg);
+                kf[t][c] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + 32 * c + 8 * lg);
+                vf[t][c] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + 32 * c + 8 * lg);
             }
         }
     }
-    f32x4 dvT[D / 16], dkT[D / 16];
+    f32x4 dvT[D / 16][NT], dkT[D / 16][NT];
 #pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-        dvT[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dkT[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int u = 0; u < D / 16; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            dvT[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dkT[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
     const uint32_t row_bytes = (uint32_t)((size_t)p.Hq * D * 2);
     // DMA of query block it into stage st: Q and dO rows (KDMA_PER_WAVE per wave
@@ -1096,12 +1100,14 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         const float* lds_dsum = ls2 + BM;
 
         // S = Q K^T and dP = dO V^T (contraction slot (lg, e) = d 32c + 8lg + e)
-        f32x4 sacc[NQB], pacc[NQB];
+        f32x4 sacc[NQB][NT], pacc[NQB][NT];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            pacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                sacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
         for (int c = 0; c < KC; ++c)
 #pragma unroll
@@ -1110,8 +1116,11 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
                 const int off = row * ROWB + 16 * ((4 * c + lg) ^ C::swz(row));
                 const u32x4 qa = *reinterpret_cast<const u32x4*>(qt + off);
                 const u32x4 ga = *reinterpret_cast<const u32x4*>(gt + off);
-                sacc[qb] = mfma_bf16(qa, kf[c], sacc[qb]);
-                pacc[qb] = mfma_bf16(ga, vf[c], pacc[qb]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    sacc[qb][t] = mfma_bf16(qa, kf[t][c], sacc[qb][t]);
+                    pacc[qb][t] = mfma_bf16(ga, vf[t][c], pacc[qb][t]);
+                }
             }
 
         // P and dS: lane holds key kw0 + li, query rows 16 qb + 4 lg .. +3
@@ -1120,36 +1129,43 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         const int row1 = imin(row0 + BM, Sq) - 1;
         const bool full = kk0 + NKW <= Sk && (!p.causal || kk0 + NKW - 1 <= row0 + delta) &&
                           (p.window_left < 0 || kk0 >= row1 + delta - p.window_left);
-        const int key = kk0 + li;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             const f32x4 lv = *reinterpret_cast<const f32x4*>(ls2 + 16 * qb + 4 * lg);
             const f32x4 dsv = *reinterpret_cast<const f32x4*>(lds_dsum + 16 * qb + 4 * lg);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float pv = fast_exp2(fmaf(sacc[qb][r], sl2, -lv[r]));
-                if (!full) {
-                    const int pos = row0 + 16 * qb + 4 * lg + r;
-                    const bool vis = key < Sk && (!p.causal || key <= pos + delta) &&
-                                     (p.window_left < 0 || key >= pos + delta - p.window_left);
-                    pv = vis ? pv : 0.f;
+            for (int t = 0; t < NT; ++t) {
+                const int key = kk0 + 16 * t + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float pv = fast_exp2(fmaf(sacc[qb][t][r], sl2, -lv[r]));
+                    if (!full) {
+                        const int pos = row0 + 16 * qb + 4 * lg + r;
+                        const bool vis = key < Sk && (!p.causal || key <= pos + delta) &&
+                                         (p.window_left < 0 || key >= pos + delta - p.window_left);
+                        pv = vis ? pv : 0.f;
+                    }
+                    sacc[qb][t][r] = pv;
+                    pacc[qb][t][r] = pv * (pacc[qb][t][r] - dsv[r]);
                 }
-                sacc[qb][r] = pv;
-                pacc[qb][r] = pv * (pacc[qb][r] - dsv[r]);
             }
         }
 
         // dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the dO and Q tiles)
 #pragma unroll
         for (int pp = 0; pp < BM / 32; ++pp) {
-            const u32x4 pb = {pack_bf16x2(sacc[2 * pp][0], sacc[2 * pp][1]),
-                              pack_bf16x2(sacc[2 * pp][2], sacc[2 * pp][3]),
-                              pack_bf16x2(sacc[2 * pp + 1][0], sacc[2 * pp + 1][1]),
-                              pack_bf16x2(sacc[2 * pp + 1][2], sacc[2 * pp + 1][3])};
-            const u32x4 sb = {pack_bf16x2(pacc[2 * pp][0], pacc[2 * pp][1]),
-                              pack_bf16x2(pacc[2 * pp][2], pacc[2 * pp][3]),
-                              pack_bf16x2(pacc[2 * pp + 1][0], pacc[2 * pp + 1][1]),
-                              pack_bf16x2(pacc[2 * pp + 1][2], pacc[2 * pp + 1][3])};
+            u32x4 pb[NT], sb[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                pb[t] = u32x4{pack_bf16x2(sacc[2 * pp][t][0], sacc[2 * pp][t][1]),
+                              pack_bf16x2(sacc[2 * pp][t][2], sacc[2 * pp][t][3]),
+                              pack_bf16x2(sacc[2 * pp + 1][t][0], sacc[2 * pp + 1][t][1]),
+                              pack_bf16x2(sacc[2 * pp + 1][t][2], sacc[2 * pp + 1][t][3])};
+                sb[t] = u32x4{pack_bf16x2(pacc[2 * pp][t][0], pacc[2 * pp][t][1]),
+                              pack_bf16x2(pacc[2 * pp][t][2], pacc[2 * pp][t][3]),
+                              pack_bf16x2(pacc[2 * pp + 1][t][0], pacc[2 * pp + 1][t][1]),
+                              pack_bf16x2(pacc[2 * pp + 1][t][2], pacc[2 * pp + 1][t][3])};
+            }
             const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
 #pragma unroll
             for (int u = 0; u < D / 16; ++u) {
@@ -1160,8 +1176,13 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
                 const u32x2 d1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(gt + o1));
                 const u32x2 q0 = lds_read_tr16(reinterpret_cast<const bf16_t*>(qt + o0));
                 const u32x2 q1 = lds_read_tr16(reinterpret_cast<const bf16_t*>(qt + o1));
-                dvT[u] = mfma_bf16(u32x4{d0[0], d0[1], d1[0], d1[1]}, pb, dvT[u]);
-                dkT[u] = mfma_bf16(u32x4{q0[0], q0[1], q1[0], q1[1]}, sb, dkT[u]);
+                const u32x4 da = {d0[0], d0[1], d1[0], d1[1]};
+                const u32x4 qa = {q0[0], q0[1], q1[0], q1[1]};
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    dvT[u][t] = mfma_bf16(da, pb[t], dvT[u][t]);
+                    dkT[u][t] = mfma_bf16(qa, sb[t], dkT[u][t]);
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next block has landed
@@ -1169,17 +1190,20 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         st ^= 1;
     }
 
-    // dK = scale (dK^T)^T, dV: lane holds d = 16u + 4lg .. +3 of key kw0 + li
-    const int key = key0 + kw0 + li;
-    if (key < Sk) {
+    // dK = scale (dK^T)^T, dV: lane holds d = 16u + 4lg .. +3 of key kw0 + 16t + li
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int key = key0 + kw0 + 16 * t + li;
+        if (key >= Sk) continue;
         const size_t off = (((size_t)b * Sk + key) * p.Hkv + hkv) * D + 4 * lg;
 #pragma unroll
         for (int u = 0; u < D / 16; ++u) {
-            const f32x4 kv = dkT[u] * p.scale;
+            const f32x4 kv = dkT[u][t] * p.scale;
+            const f32x4 vv = dvT[u][t];
             *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.dk) + off + 16 * u) =
                 u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
             *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.dv) + off + 16 * u) =
-                u32x2{pack_bf16x2(dvT[u][0], dvT[u][1]), pack_bf16x2(dvT[u][2], dvT[u][3])};
+                u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
         }
     }
 }
@@ -1214,11 +1238,11 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int OCC>
+template <int D, int NKW, int OCC>
 hipError_t launch_bwd_dkdv_dma(const BwdParams& p, hipStream_t stream) {
     const long long grid = (long long)p.num_n_blocks * p.Hkv * p.B;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<D, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<D, NKW, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1254,16 +1278,19 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
      BwdTile<bf16_t, D, NKW>::LDS_BYTES, 0, &launch_bwd<bf16_t, D, NKW, OCC, false>,               \
      &launch_bwd_pre<bf16_t, D>, nullptr, &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 1}
 // both kernels on DMA'd tiles
-#define TPA_BWD_DMA(D, OCC, NQW, QOCC)                                                               \
-    {DT_BF16, D, BwdKvDmaTile<D>::BN, BwdKvDmaTile<D>::BM, BwdKvDmaTile<D>::LDS_BYTES, 0,          \
-     &launch_bwd_dkdv_dma<D, OCC>, &launch_bwd_pre<bf16_t, D>, nullptr,                           \
+#define TPA_BWD_DMA(D, NKW, OCC, NQW, QOCC)                                                          \
+    {DT_BF16, D, BwdKvDmaTile<D, NKW>::BN, BwdKvDmaTile<D, NKW>::BM,                               \
+     BwdKvDmaTile<D, NKW>::LDS_BYTES, 0, &launch_bwd_dkdv_dma<D, NKW, OCC>,                       \
+     &launch_bwd_pre<bf16_t, D>, nullptr,                                                         \
      &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 2}
 
 static const BwdVariant kBwdVariants[] = {
     // two passes (default): both kernels on DMA'd tiles; 64-key blocks for dK/dV,
     // 64-row blocks for dQ (16 rows per wave, two workgroups per CU)
-    TPA_BWD_DMA(128, 2, 1, 2),
-    TPA_BWD_DMA(64, 2, 1, 2),
+    TPA_BWD_DMA(128, 16, 2, 1, 2),
+    TPA_BWD_DMA(64, 16, 2, 1, 2),
+    TPA_BWD_DMA(128, 32, 1, 1, 2),  // 128-key blocks (32 keys per wave)
+    TPA_BWD_DMA(64, 32, 1, 1, 2),
     // dK/dV with register-staged query tiles
     TPA_BWD_TWO_PASS_DMA(128, 16, 2, 1, 2),
     TPA_BWD_TWO_PASS_DMA(64, 16, 2, 1, 2),
