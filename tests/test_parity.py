@@ -294,6 +294,15 @@ ABLATIONS = [
 ]
 
 
+@pytest.mark.parametrize("S", [2, 15, 16, 17, 31, 64, 200, 256])
+def test_decode_forced_split_counts(S):
+    # forced split counts on both sides of the combine kernels' switch (16);
+    # 2100 keys make 33 key blocks, so S > 33 leaves empty splits
+    for seed in (13, 14):
+        run_case("bf16", 2, 16, 2, 1, 2100, 128, False, -1, S, seed=seed)
+        run_case("bf16", 1, 8, 8, 1, 700, 64, False, 100, S, seed=seed)
+
+
 @pytest.mark.parametrize("env", ABLATIONS, ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
 def test_ablation_paths(env, monkeypatch):
     for k_, v_ in env.items():
