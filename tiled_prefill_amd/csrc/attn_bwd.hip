@@ -892,58 +892,57 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
         const char* kt = smem + stage * STAGEB;
         const char* vt = kt + TILEB;
 
-        // S^T = K Q^T and dP^T = V dO^T (lane group lg contracts d in [lg DL, (lg+1) DL))
-        f32x4 sacc[NT][NQW], pacc[NT][NQW];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int qq = 0; qq < NQW; ++qq) {
-                sacc[t][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pacc[t][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int c = 0; c < QV; ++c) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int row = 16 * t + li;
-                const int off = row * ROWB + 16 * ((lg * QV + c) ^ C::swz(row));
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + off);
-                const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + off);
-#pragma unroll
-                for (int qq = 0; qq < NQW; ++qq) {
-                    sacc[t][qq] = mfma_bf16(kf, qf[qq][c], sacc[t][qq]);
-                    pacc[t][qq] = mfma_bf16(vf, gf[qq][c], pacc[t][qq]);
-                }
-            }
-        }
-
+        // per 32-key half of the tile: S^T = K Q^T and dP^T = V dO^T (lane group lg
+        // contracts d in [lg DL, (lg+1) DL)), then P^T, dS^T and dQ^T += K^T dS^T
         const int key0 = n * BN;
         const bool full = key0 >= wlo && key0 + BN - 1 <= whi;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int qq = 0; qq < NQW; ++qq)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float pv = fast_exp2(fmaf(sacc[t][qq][r], sl2, -l2[qq]));
-                    if (!full) {
-                        const int key = key0 + 16 * t + 4 * lg + r;
-                        pv = (key < row_lo[qq] || key > row_hi[qq]) ? 0.f : pv;
-                    }
-                    pacc[t][qq][r] = pv * (pacc[t][qq][r] - dsum[qq]);
-                }
-
-        // dQ^T += K^T dS^T: K^T by transpose reads of the K tile; source lane s
-        // of a 16-lane group addresses key row k0 + s / 4, columns 16u + 4 (s % 4)
-#pragma unroll
         for (int pp = 0; pp < NT / 2; ++pp) {
+            f32x4 sacc[2][NQW], pacc[2][NQW];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int qq = 0; qq < NQW; ++qq) {
+                    sacc[h][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pacc[h][qq] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int c = 0; c < QV; ++c) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * (2 * pp + h) + li;
+                    const int off = row * ROWB + 16 * ((lg * QV + c) ^ C::swz(row));
+                    const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + off);
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vt + off);
+#pragma unroll
+                    for (int qq = 0; qq < NQW; ++qq) {
+                        sacc[h][qq] = mfma_bf16(kf, qf[qq][c], sacc[h][qq]);
+                        pacc[h][qq] = mfma_bf16(vf, gf[qq][c], pacc[h][qq]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int qq = 0; qq < NQW; ++qq)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float pv = fast_exp2(fmaf(sacc[h][qq][r], sl2, -l2[qq]));
+                        if (!full) {
+                            const int key = key0 + 16 * (2 * pp + h) + 4 * lg + r;
+                            pv = (key < row_lo[qq] || key > row_hi[qq]) ? 0.f : pv;
+                        }
+                        pacc[h][qq][r] = pv * (pacc[h][qq][r] - dsum[qq]);
+                    }
+            // K^T by transpose reads of the K tile; source lane s of a 16-lane
+            // group addresses key row k0 + s / 4, columns 16u + 4 (s % 4)
             u32x4 sb[NQW];
 #pragma unroll
             for (int qq = 0; qq < NQW; ++qq)
-                sb[qq] = u32x4{pack_bf16x2(pacc[2 * pp][qq][0], pacc[2 * pp][qq][1]),
-                               pack_bf16x2(pacc[2 * pp][qq][2], pacc[2 * pp][qq][3]),
-                               pack_bf16x2(pacc[2 * pp + 1][qq][0], pacc[2 * pp + 1][qq][1]),
-                               pack_bf16x2(pacc[2 * pp + 1][qq][2], pacc[2 * pp + 1][qq][3])};
+                sb[qq] = u32x4{pack_bf16x2(pacc[0][qq][0], pacc[0][qq][1]),
+                               pack_bf16x2(pacc[0][qq][2], pacc[0][qq][3]),
+                               pack_bf16x2(pacc[1][qq][0], pacc[1][qq][1]),
+                               pack_bf16x2(pacc[1][qq][2], pacc[1][qq][3])};
             const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
 #pragma unroll
             for (int u = 0; u < D / 16; ++u) {
@@ -1004,7 +1003,7 @@ struct BwdKvDmaTile {
 template <int D, int NKW_, int OCC>
 __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p) {
     using C = BwdKvDmaTile<D, NKW_>;
-    constexpr int BM = C::BM, BN = C::BN, NQB = C::NQB, KC = C::KC, NKW = C::NKW, NT = C::NT;
+    constexpr int BM = C::BM, BN = C::BN, KC = C::KC, NKW = C::NKW, NT = C::NT;
     constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
@@ -1099,72 +1098,68 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         const float* ls2 = reinterpret_cast<const float*>(gt + TILEB);
         const float* lds_dsum = ls2 + BM;
 
-        // S = Q K^T and dP = dO V^T (contraction slot (lg, e) = d 32c + 8lg + e)
-        f32x4 sacc[NQB][NT], pacc[NQB][NT];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                sacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pacc[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                const int row = 16 * qb + li;
-                const int off = row * ROWB + 16 * ((4 * c + lg) ^ C::swz(row));
-                const u32x4 qa = *reinterpret_cast<const u32x4*>(qt + off);
-                const u32x4 ga = *reinterpret_cast<const u32x4*>(gt + off);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    sacc[qb][t] = mfma_bf16(qa, kf[t][c], sacc[qb][t]);
-                    pacc[qb][t] = mfma_bf16(ga, vf[t][c], pacc[qb][t]);
-                }
-            }
-
-        // P and dS: lane holds key kw0 + li, query rows 16 qb + 4 lg .. +3
+        // per 32-row half of the query block: S = Q K^T and dP = dO V^T (contraction
+        // slot (lg, e) = d 32c + 8lg + e), P and dS (lane holds key kw0 + 16t + li,
+        // query rows 16 qb + 4 lg .. +3), then dV^T += dO^T P and dK^T += Q^T dS
+        // with dO and Q read as columns (transpose reads)
         const int kk0 = key0 + kw0;
         const int row0 = m * BM;
         const int row1 = imin(row0 + BM, Sq) - 1;
         const bool full = kk0 + NKW <= Sk && (!p.causal || kk0 + NKW - 1 <= row0 + delta) &&
                           (p.window_left < 0 || kk0 >= row1 + delta - p.window_left);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(ls2 + 16 * qb + 4 * lg);
-            const f32x4 dsv = *reinterpret_cast<const f32x4*>(lds_dsum + 16 * qb + 4 * lg);
+        for (int pp = 0; pp < BM / 32; ++pp) {
+            f32x4 sacc[2][NT], pacc[2][NT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int key = kk0 + 16 * t + li;
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float pv = fast_exp2(fmaf(sacc[qb][t][r], sl2, -lv[r]));
-                    if (!full) {
-                        const int pos = row0 + 16 * qb + 4 * lg + r;
-                        const bool vis = key < Sk && (!p.causal || key <= pos + delta) &&
-                                         (p.window_left < 0 || key >= pos + delta - p.window_left);
-                        pv = vis ? pv : 0.f;
+                for (int t = 0; t < NT; ++t) {
+                    sacc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pacc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * (2 * pp + h) + li;
+                    const int off = row * ROWB + 16 * ((4 * c + lg) ^ C::swz(row));
+                    const u32x4 qa = *reinterpret_cast<const u32x4*>(qt + off);
+                    const u32x4 ga = *reinterpret_cast<const u32x4*>(gt + off);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        sacc[h][t] = mfma_bf16(qa, kf[t][c], sacc[h][t]);
+                        pacc[h][t] = mfma_bf16(ga, vf[t][c], pacc[h][t]);
                     }
-                    sacc[qb][t][r] = pv;
-                    pacc[qb][t][r] = pv * (pacc[qb][t][r] - dsv[r]);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int qb = 2 * pp + h;
+                const f32x4 lv = *reinterpret_cast<const f32x4*>(ls2 + 16 * qb + 4 * lg);
+                const f32x4 dsv = *reinterpret_cast<const f32x4*>(lds_dsum + 16 * qb + 4 * lg);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int key = kk0 + 16 * t + li;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float pv = fast_exp2(fmaf(sacc[h][t][r], sl2, -lv[r]));
+                        if (!full) {
+                            const int pos = row0 + 16 * qb + 4 * lg + r;
+                            const bool vis = key < Sk && (!p.causal || key <= pos + delta) &&
+                                             (p.window_left < 0 || key >= pos + delta - p.window_left);
+                            pv = vis ? pv : 0.f;
+                        }
+                        sacc[h][t][r] = pv;
+                        pacc[h][t][r] = pv * (pacc[h][t][r] - dsv[r]);
+                    }
                 }
             }
-        }
-
-        // dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the dO and Q tiles)
-#pragma unroll
-        for (int pp = 0; pp < BM / 32; ++pp) {
             u32x4 pb[NT], sb[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                pb[t] = u32x4{pack_bf16x2(sacc[2 * pp][t][0], sacc[2 * pp][t][1]),
-                              pack_bf16x2(sacc[2 * pp][t][2], sacc[2 * pp][t][3]),
-                              pack_bf16x2(sacc[2 * pp + 1][t][0], sacc[2 * pp + 1][t][1]),
-                              pack_bf16x2(sacc[2 * pp + 1][t][2], sacc[2 * pp + 1][t][3])};
-                sb[t] = u32x4{pack_bf16x2(pacc[2 * pp][t][0], pacc[2 * pp][t][1]),
-                              pack_bf16x2(pacc[2 * pp][t][2], pacc[2 * pp][t][3]),
-                              pack_bf16x2(pacc[2 * pp + 1][t][0], pacc[2 * pp + 1][t][1]),
-                              pack_bf16x2(pacc[2 * pp + 1][t][2], pacc[2 * pp + 1][t][3])};
+                pb[t] = u32x4{pack_bf16x2(sacc[0][t][0], sacc[0][t][1]), pack_bf16x2(sacc[0][t][2], sacc[0][t][3]),
+                              pack_bf16x2(sacc[1][t][0], sacc[1][t][1]), pack_bf16x2(sacc[1][t][2], sacc[1][t][3])};
+                sb[t] = u32x4{pack_bf16x2(pacc[0][t][0], pacc[0][t][1]), pack_bf16x2(pacc[0][t][2], pacc[0][t][3]),
+                              pack_bf16x2(pacc[1][t][0], pacc[1][t][1]), pack_bf16x2(pacc[1][t][2], pacc[1][t][3])};
             }
             const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
 #pragma unroll
@@ -1286,15 +1281,17 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
 
 static const BwdVariant kBwdVariants[] = {
     // two passes (default): both kernels on DMA'd tiles; 64-key blocks for dK/dV,
-    // 64-row blocks for dQ (16 rows per wave, two workgroups per CU)
-    TPA_BWD_DMA(128, 16, 2, 1, 2),
+    // 128-row blocks for dQ (32 rows per wave, two workgroups per CU)
+    TPA_BWD_DMA(128, 16, 2, 2, 2),
+    TPA_BWD_DMA(64, 16, 2, 2, 2),
+    TPA_BWD_DMA(128, 16, 2, 1, 2),  // 64-row dQ blocks (16 rows per wave)
     TPA_BWD_DMA(64, 16, 2, 1, 2),
-    TPA_BWD_DMA(128, 32, 1, 1, 2),  // 128-key blocks (32 keys per wave)
-    TPA_BWD_DMA(64, 32, 1, 1, 2),
+    TPA_BWD_DMA(128, 32, 1, 2, 2),  // 128-key blocks (32 keys per wave)
+    TPA_BWD_DMA(64, 32, 1, 2, 2),
     // dK/dV with register-staged query tiles
     TPA_BWD_TWO_PASS_DMA(128, 16, 2, 1, 2),
     TPA_BWD_TWO_PASS_DMA(64, 16, 2, 1, 2),
-    TPA_BWD_TWO_PASS_DMA(128, 16, 2, 2, 1),  // 128-row dQ blocks, one workgroup per CU
+    TPA_BWD_TWO_PASS_DMA(128, 16, 2, 2, 2),  // 128-row dQ blocks
     TPA_BWD_TWO_PASS_DMA(64, 16, 2, 2, 2),
     // register-staged dQ kernel (the fp32 path's kernel), as an ablation for bf16
     TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 16, 2, 1, 2),
