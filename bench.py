@@ -40,9 +40,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "backward"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload (one JSON line each) instead of the headline line")
@@ -334,8 +335,19 @@ def main():
         comb_ms = prof["combine_ms"] / max(1, prof["combine_launches"])
         achieved = (kv_bytes + q_bytes) / (fwd_ms * 1e-3) / 1e9
         traffic = traffic_for("attn_decode_kernel", w.name)
+        # distribution of single steps, each bracketed by events on the launch stream
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(100)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            step(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1 in evs)
+        pct = {"p10": round(us[10], 2), "p50": round(us[50], 2), "p90": round(us[90], 2)}
         out["decode"] = dict(value=value, ms_per_step=ms, fwd_ms=fwd_ms, combine_ms=comb_ms,
-                             achieved=achieved, traffic=traffic, n_rot=n_rot)
+                             achieved=achieved, traffic=traffic, n_rot=n_rot, step_us=pct)
         del ks, vs, q, k, v
 
     # ----------------------------------------------------------------- prefill
@@ -365,6 +377,37 @@ def main():
         out["prefill"] = dict(value=flops / (pms * 1e-3) / 1e12, ms_per_step=pms, fwd_ms=pf_ms,
                               achieved=flops / (pf_ms * 1e-3) / 1e12)
         del q, k, v
+
+    # ---------------------------------------------------------------- backward
+    from workloads import BWD_WORKLOADS, output_grad
+    wb = BWD_WORKLOADS["causal_prefill_bwd_bf16"]
+    bflops = 10.0 * wb.d * pairs  # five products of 2 d flops per visible pair
+    if not args.no_backward and args.only in (None, "backward"):
+        q, k, v, _ = make_inputs(wb, seed=0, device=dev)
+        g = output_grad(0, q.shape, wb.dtype, device=dev)
+        o, lse = tpa.fwd(q, k, v, causal=True)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def bstep(i=0):
+            tpa.bwd(q, k, v, o, g, lse, causal=True, dq=dq, dk=dk, dv=dv)
+
+        warm(bstep, 3)
+        nb = max(5, args.prefill_steps)
+        t0 = time.perf_counter()
+        for _ in range(nb):
+            bstep()
+        torch.cuda.synchronize()
+        bms = (time.perf_counter() - t0) * 1e3 / nb
+        tpa.profile_begin(4 * nb + 8)
+        for _ in range(nb):
+            bstep()
+        prof = tpa.profile_end_kinds()
+        n = max(1, prof["bwd_launches"])
+        kv_ms, dq_ms = prof["bwd_ms"] / n, prof["bwd_dq_ms"] / n
+        out["backward"] = dict(value=bflops / (bms * 1e-3) / 1e12, ms_per_step=bms, dkdv_ms=kv_ms,
+                               dq_ms=dq_ms, pre_ms=prof["bwd_prepost_ms"] / n,
+                               achieved=bflops / ((kv_ms + dq_ms) * 1e-3) / 1e12)
+        del q, k, v, g, o, dq, dk, dv
 
     # ------------------------------------------------------------ cpu baseline
     cpu = None
@@ -397,6 +440,22 @@ def main():
         dtp = time.perf_counter() - t0
         cpu["prefill"] = {"value": pf / dtp / 1e12, "unit": "TFLOP/s",
                           "sample": f"{len(rows)} causal query rows x 32 heads, {dtp:.1f} s"}
+        if not args.no_backward:
+            # backward: the whole gradient of one of the 32 heads (full 8192 rows)
+            from workloads import output_grad
+            gp = output_grad(0, qp.shape, wp.dtype)
+            t0 = time.perf_counter()
+            oracle.attn_bwd_ref(qp[:, :, :1], kp[:, :, :1], vp[:, :, :1], gp[:, :, :1], True, -1,
+                                wp.scale, n_threads=threads)
+            dtb = time.perf_counter() - t0
+            cpu["backward"] = {"value": 10.0 * wp.d * (pairs / wp.Hq) / dtb / 1e12, "unit": "TFLOP/s",
+                               "sample": f"the backward of 1 of the 32 heads (8192 causal rows), {dtb:.1f} s"}
+        try:
+            model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                         if l.startswith("model name"))
+        except (OSError, StopIteration):
+            model = "unknown"
+        cpu["cpu_model"] = model
 
     dec = out.get("decode")
     pre = out.get("prefill")
@@ -427,6 +486,7 @@ def main():
                             "traffic": dec["traffic"],
                             "avg_launch_ms": round(dec["fwd_ms"], 5),
                             "combine_avg_launch_ms": round(dec["combine_ms"], 5)}
+        line["step_us"] = dec["step_us"]
     if pre:
         line["prefill"] = {
             "metric": "causal prefill TFLOP/s", "value": round(pre["value"], 2),
@@ -434,12 +494,28 @@ def main():
             "pct_of_mfma_peak": round(100 * pre["value"] / BF16_PEAK_TFLOPS, 2),
             "config": {"workload": "causal_prefill_bf16: B=1 H=32 S=8192 d=128, causal, "
                                    "visible pairs only", "flops_per_step": flops},
-            "roofline": {"bound": "mfma", "kernel": "attn_prefill_kernel<128, 8, 32, 0>",
+            "roofline": {"bound": "mfma", "kernel": "attn_prefill_kernel<128, 8, 32, 0, 0>",
                          "achieved": round(pre["achieved"], 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["achieved"] / BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic_for("attn_prefill_kernel", wp.name),
                          "avg_launch_ms": round(pre["fwd_ms"], 4)},
+        }
+    bwd = out.get("backward")
+    if bwd:
+        line["backward"] = {
+            "metric": "causal backward TFLOP/s", "value": round(bwd["value"], 2),
+            "unit": "TFLOP/s", "ms_per_step": round(bwd["ms_per_step"], 4),
+            "pct_of_mfma_peak": round(100 * bwd["value"] / BF16_PEAK_TFLOPS, 2),
+            "config": {"workload": "causal_prefill_bwd_bf16: B=1 H=32 S=8192 d=128, causal, "
+                                   "dq/dk/dv, 10 d flops per visible pair", "flops_per_step": bflops},
+            "roofline": {"bound": "mfma",
+                         "kernel": "attn_bwd_dkdv_dma_kernel<128, 16, 2> + attn_bwd_dq_dma_kernel<128, 2, 2>",
+                         "achieved": round(bwd["achieved"], 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(bwd["achieved"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "avg_launch_ms": {"dkdv": round(bwd["dkdv_ms"], 4), "dq": round(bwd["dq_ms"], 4),
+                                           "row_sums": round(bwd["pre_ms"], 4)}},
         }
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
