@@ -783,8 +783,11 @@ struct BwdDqDmaTile {
     static constexpr int KDMA_PER_WAVE = KDMA / NW;
     static constexpr int DL = D / 4, QV = DL / 8;
     static_assert(KDMA % NW == 0, "tile DMAs must split evenly over the waves");
+    // XOR swizzle of the 16-byte chunk slots of row r: 16 consecutive rows read
+    // at one chunk (16-byte row reads) hit distinct banks, and so do the two
+    // chunks of 4 consecutive rows that one 16-lane transpose read touches
     static __host__ __device__ __forceinline__ int swz(int r) {
-        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+        return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
     }
 };
 
@@ -995,8 +998,11 @@ struct BwdKvDmaTile {
     static constexpr int KROWS = 1024 / ROWB, KDMA = BM / KROWS, KDMA_PER_WAVE = KDMA / NW;
     static constexpr int KC = D / 32;
     static_assert(KDMA % NW == 0, "tile DMAs must split evenly over the waves");
+    // XOR swizzle of the 16-byte chunk slots of row r: 16 consecutive rows read
+    // at one chunk (16-byte row reads) hit distinct banks, and so do the two
+    // chunks of 4 consecutive rows that one 16-lane transpose read touches
     static __host__ __device__ __forceinline__ int swz(int r) {
-        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+        return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
     }
 };
 
@@ -1023,7 +1029,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
     const int nm = imax(0, m_hi - m_lo);
     const int total = G * nm;
 
-    // this wave's K and V rows as MFMA B fragments: key kw0 + 16t + li, d = 32c + 8lg..
+    // this wave's K and V rows as MFMA B fragments: key kw0 + 16t + li, d = (D/4) lg + 8c..
     const size_t kv_stride = (size_t)p.Hkv * D;
     const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * Sk * p.Hkv + hkv) * D;
     const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * Sk * p.Hkv + hkv) * D;
@@ -1037,8 +1043,8 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
             kf[t][c] = z;
             vf[t][c] = z;
             if (key < Sk && total > 0) {
-                kf[t][c] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + 32 * c + 8 * lg);
-                vf[t][c] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + 32 * c + 8 * lg);
+                kf[t][c] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + (D / 4) * lg + 8 * c);
+                vf[t][c] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + (D / 4) * lg + 8 * c);
             }
         }
     }
@@ -1099,7 +1105,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         const float* lds_dsum = ls2 + BM;
 
         // per 32-row half of the query block: S = Q K^T and dP = dO V^T (contraction
-        // slot (lg, e) = d 32c + 8lg + e), P and dS (lane holds key kw0 + 16t + li,
+        // slot (lg, e) of step c = d (D/4) lg + 8c + e), P and dS (lane holds key kw0 + 16t + li,
         // query rows 16 qb + 4 lg .. +3), then dV^T += dO^T P and dK^T += Q^T dS
         // with dO and Q read as columns (transpose reads)
         const int kk0 = key0 + kw0;
@@ -1122,7 +1128,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int row = 16 * (2 * pp + h) + li;
-                    const int off = row * ROWB + 16 * ((4 * c + lg) ^ C::swz(row));
+                    const int off = row * ROWB + 16 * ((KC * lg + c) ^ C::swz(row));
                     const u32x4 qa = *reinterpret_cast<const u32x4*>(qt + off);
                     const u32x4 ga = *reinterpret_cast<const u32x4*>(gt + off);
 #pragma unroll
