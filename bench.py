@@ -30,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tiled_prefill_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # kernel -> source file it is compiled from
-KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_prefill_kernel": "attn_prefill.hip"}
+KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_prefill_kernel": "attn_prefill.hip",
+                  "attn_bwd_dkdv_dma_kernel": "attn_bwd.hip", "attn_bwd_dq_dma_kernel": "attn_bwd.hip"}
 
 
 def parse():
@@ -503,6 +504,10 @@ def main():
         }
     bwd = out.get("backward")
     if bwd:
+        # counter bytes of the two matrix kernels together, when both are recorded
+        t_kv = traffic_for("attn_bwd_dkdv_dma_kernel", wb.name)
+        t_dq = traffic_for("attn_bwd_dq_dma_kernel", wb.name)
+        bwd_traffic = t_kv + t_dq if t_kv is not None and t_dq is not None else None
         line["backward"] = {
             "metric": "causal backward TFLOP/s", "value": round(bwd["value"], 2),
             "unit": "TFLOP/s", "ms_per_step": round(bwd["ms_per_step"], 4),
@@ -513,7 +518,7 @@ def main():
                          "kernel": "attn_bwd_dkdv_dma_kernel<128, 16, 2> + attn_bwd_dq_dma_kernel<128, 2, 2>",
                          "achieved": round(bwd["achieved"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(bwd["achieved"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": bwd_traffic,
                          "avg_launch_ms": {"dkdv": round(bwd["dkdv_ms"], 4), "dq": round(bwd["dq_ms"], 4),
                                            "row_sums": round(bwd["pre_ms"], 4)}},
         }

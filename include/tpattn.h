@@ -156,7 +156,7 @@ typedef struct tpattn_bwd_plan {
     int block_m;         /* query rows per inner block                                     */
     int block_n;         /* keys per workgroup                                             */
     int num_n_blocks;    /* key blocks per (batch, KV head)                                */
-    int grid_x;          /* workgroups of the main kernel: num_n_blocks * Hkv * B          */
+    int grid_x;          /* key-block tiles: num_n_blocks * Hkv * B (launch padded to 8s)   */
     int threads;         /* threads per workgroup                                          */
     int lds_bytes;       /* LDS per workgroup                                              */
     int dq_block_m;      /* query rows per workgroup of the dQ kernel (0: atomic form)     */

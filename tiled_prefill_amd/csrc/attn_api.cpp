@@ -517,7 +517,9 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
     q.lds_bytes = var->lds_bytes;
     q.num_n_blocks = ceil_div(imax(p.Sk, 0), var->block_n);
     const long long grid = (long long)q.num_n_blocks * p.Hkv * p.B;
-    if (grid > 0x7fffffffLL) return fail(TPATTN_EINVAL, "too many key blocks");
+    const long long dq_tiles = (long long)ceil_div(imax(p.Sq, 0), imax(1, var->dq_block_m)) * p.Hq * p.B;
+    if (grid > 0x7fffffffLL - 8 || dq_tiles > 0x7fffffffLL - 8)
+        return fail(TPATTN_EINVAL, "too many key or query blocks");
     q.grid_x = (int)grid;
     long long visited = 0;
     for (int n = 0; n < q.num_n_blocks; ++n) {

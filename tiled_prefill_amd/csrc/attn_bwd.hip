@@ -800,9 +800,18 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
+    // XCD-aware one-dimensional grid: tile t = (batch, head, query block), query
+    // blocks fastest and heaviest first; XCD x (workgroup i runs on XCD i % 8)
+    // owns tiles [x per_xcd, (x + 1) per_xcd), so the query blocks of a head run
+    // together on one XCD and share its 4 MB L2 for the head's K and V
     const int num_m = ceil_div(p.Sq, BM);
-    const int m_block = p.causal ? num_m - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    const int hq = blockIdx.y, b = blockIdx.z;
+    const int total = num_m * p.Hq * p.B;
+    const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
+    const int t = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
+    if (t >= total) return;
+    const int m_rev = t % num_m;
+    const int m_block = p.causal ? num_m - 1 - m_rev : m_rev;
+    const int hq = (t / num_m) % p.Hq, b = t / (num_m * p.Hq);
     const int hkv = hq / p.G;
     const int Sq = p.Sq, Sk = p.Sk, delta = Sk - Sq;
 
@@ -1015,10 +1024,18 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int bid = blockIdx.x;
-    const int hkv = bid % p.Hkv;
-    const int b = (bid / p.Hkv) % p.B;
-    const int nb = bid / (p.Hkv * p.B);
+    // XCD-aware one-dimensional grid: tile t = (batch, KV head, key block), key
+    // blocks fastest (heaviest causal blocks first); XCD x owns tiles
+    // [x per_xcd, (x + 1) per_xcd), so the key blocks of a head run together on
+    // one XCD and share its L2 for the head's Q and dO ([FA-tiling] §4.6: Q and dO
+    // are what the backward keeps in L2)
+    const int tiles = p.num_n_blocks * p.Hkv * p.B;
+    const int per_xcd = (tiles + NUM_XCD - 1) / NUM_XCD;
+    const int tile = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
+    if (tile >= tiles) return;
+    const int nb = tile % p.num_n_blocks;
+    const int hkv = (tile / p.num_n_blocks) % p.Hkv;
+    const int b = tile / (p.num_n_blocks * p.Hkv);
     const int G = p.G, Sq = p.Sq, Sk = p.Sk;
     const int delta = Sk - Sq;
     const int key0 = nb * BN;
@@ -1241,17 +1258,19 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
 
 template <int D, int NKW, int OCC>
 hipError_t launch_bwd_dkdv_dma(const BwdParams& p, hipStream_t stream) {
-    const long long grid = (long long)p.num_n_blocks * p.Hkv * p.B;
-    if (grid == 0) return hipSuccess;
+    const long long tiles = (long long)p.num_n_blocks * p.Hkv * p.B;
+    if (tiles == 0) return hipSuccess;
+    const long long grid = (tiles + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<D, NKW, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D, int NQW, int OCC>
 hipError_t launch_bwd_dq_dma(const BwdParams& p, hipStream_t stream) {
-    const int num_m = ceil_div(p.Sq, BwdDqDmaTile<D, NQW>::BM);
-    if (num_m == 0 || p.B == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<D, NQW, OCC>), dim3(num_m, p.Hq, p.B), dim3(256), 0, stream, p);
+    const long long tiles = (long long)ceil_div(p.Sq, BwdDqDmaTile<D, NQW>::BM) * p.Hq * p.B;
+    if (tiles == 0) return hipSuccess;
+    const long long grid = (tiles + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<D, NQW, OCC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
