@@ -892,15 +892,18 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
         }
     };
 
+    // key blocks in ascending order: the query blocks of a head, which run
+    // together on one XCD, then walk the head's K and V tiles roughly in step
+    // and share them in L2
     if (has_work) {
-        load_kv(n_hi - 1, 0);
+        load_kv(n_lo, 0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
     }
     __syncthreads();
 
     int stage = 0;
-    for (int n = n_hi - 1; n >= n_lo; --n) {
-        if (n > n_lo) load_kv(n - 1, stage ^ 1);
+    for (int n = n_lo; n < n_hi; ++n) {
+        if (n + 1 < n_hi) load_kv(n + 1, stage ^ 1);
         const char* kt = smem + stage * STAGEB;
         const char* vt = kt + TILEB;
 
