@@ -278,11 +278,13 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             S = imax(1, imin(TPATTN_MAX_SPLITS, ceil_div(imax(max_blocks, 1), cb)));
             if (S == 1) chunk = 0;
         } else if (var->dv) {
-            // 512-wide fp32 partials are costly: split only as far as both the
-            // workgroup target and a minimum chunk of 512 keys allow
-            const int mc = imax(1, ceil_div(env_int("TPATTN_MLA_MIN_CHUNK", 512), BN));
-            const int target = wg_per_cu * num_cus;
-            S = imin(ceil_div(target, t), imax(1, max_blocks / mc));
+            // The latent kernel holds one workgroup per CU (136 KB of LDS): split as
+            // far as one wave of workgroups allows (tiles * S <= CUs; a second,
+            // partial wave costs more than the splits save: 65,536 keys, 5 query
+            // blocks, 51 splits 161 us vs 64 splits 236 us) and every split keeps
+            // a minimum chunk of 128 keys.
+            const int mc = imax(1, ceil_div(env_int("TPATTN_MLA_MIN_CHUNK", 128), BN));
+            S = imin(imax(1, num_cus / t), imax(1, max_blocks / mc));
         } else {
             S = occupancy_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
         }
