@@ -104,9 +104,10 @@ int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * v [B][Sk][Hkv][d_v], o [B][Sq][Hq][d_v] (dtype of q), lse as tpattn_fwd.
  * d_v == d behaves as tpattn_fwd; otherwise only bf16 with d = 576, d_v = 512
  * is built (TPATTN_EUNSUPPORTED else). The query heads of a KV head are always
- * packed into the row dimension ([FA-tiling] §6.3); num_splits <= 0 takes the
- * smaller of the workgroup target and a 512-key minimum chunk (the fp32 split
- * partials are d_v wide). Other arguments as tpattn_fwd. */
+ * packed into the row dimension ([FA-tiling] §6.3); num_splits <= 0 splits as far
+ * as one workgroup per CU allows (the kernel holds one per CU), with at least 128
+ * keys per split (the fp32 split partials are d_v wide). Other arguments as
+ * tpattn_fwd. */
 int tpattn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v,
                   int causal, int window_left, float scale, int num_splits,
