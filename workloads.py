@@ -51,9 +51,10 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The six workloads. Shapes come from the pages' discussion of decode,
-# speculative verification and long-context prefill (see the design doc for the
-# mapping to the pages).
+# The six forward workloads. Shapes follow the pages' discussion of decode
+# ("分块策略与调度" §5: long KV with few heads, split-KV), speculative verification
+# (the occupancy blog's verify-attention shapes) and long-context prefill
+# ("分块策略与调度" §3: causal and sliding-window block skipping).
 WORKLOADS = {
     "decode_fp32": Workload(
         "decode_fp32", "fp32", B=1, Hq=4, Hkv=4, Sq=1, Sk=256, d=64, causal=False,
