@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the attention forward pass.
+"""Seeded synthetic workloads for the attention forward and backward passes.
 
 This module only draws random tensors with the shapes, dtypes and value
 distributions of the workloads the pages discuss; it contains none of the
