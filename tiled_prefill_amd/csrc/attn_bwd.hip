@@ -13,6 +13,13 @@
 //   attn_bwd_dq_kernel  one workgroup per (query block, query head, batch),
 //                       looping over the key blocks that query block sees:
 //                       recomputes S and dP and forms dQ = dS K on MFMA.
+//   attn_bwd_dkdv_dma_kernel, attn_bwd_dq_dma_kernel
+//                       the bf16 forms of the two kernels above (the default):
+//                       their tiles (Q, dO, lse2, D; or K, V) are DMA'd into
+//                       double-buffered LDS one block ahead, work proceeds in
+//                       32-row / 32-key halves, and both run on XCD-aware
+//                       one-dimensional grids so that the blocks of a head share
+//                       one XCD's L2.
 //   (atomic form)       the pages' single pass ([FA-tiling] §4.6: Q, dO and an
 //                       fp32 dQ accumulator are the backward's working set):
 //                       attn_bwd_kernel<.., ATOMIC> also forms dQ = dS K per
