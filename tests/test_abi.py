@@ -111,3 +111,27 @@ def _bwd(**kw):
 def test_bwd_bad_arguments_are_rejected_without_launch(kw, code):
     assert _bwd(**kw) == code
     assert tpa.load().tpattn_last_error().decode() != ""
+
+
+def test_python_binding_refuses_cpu_tensors_in_every_entry_point():
+    # no CPU fallback anywhere: every compute call raises on host tensors
+    import torch
+    q = torch.zeros(1, 2, 4, 64)
+    k = torch.zeros(1, 3, 2, 64)
+    lse = torch.zeros(1, 4, 2)
+    with pytest.raises(ValueError):
+        tpa.fwd_varlen(q, k, k, torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        tpa.fwd_dv(q, k, torch.zeros(1, 3, 2, 32))
+    with pytest.raises(ValueError):
+        tpa.bwd(q, k, k, q, q, lse)
+
+
+def test_host_block_range_mirrors_reject_bad_arguments():
+    with pytest.raises(tpa.TpAttnError):
+        tpa.m_block_range(8, 8, True, -2, 64, 64, 0)
+    with pytest.raises(tpa.TpAttnError):
+        tpa.m_block_range(8, 8, True, -1, 0, 64, 0)
+    with pytest.raises(tpa.TpAttnError):
+        tpa.plan_bwd(1, 6, 4, 8, 8, 64)
+    assert tpa.m_block_range(0, 8, True, -1, 64, 64, 0)[1] == 0   # no query rows: empty
