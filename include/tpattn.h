@@ -176,10 +176,11 @@ size_t tpattn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits);
  * over rows r = (b, i, h) in o's order (B*Sq*Hq rows). o_part [S][rows][d] fp32,
  * lse_part [S][rows] fp32 (-inf marks an empty split, whose o_part is not
  * read), o in `dtype`, lse [B][Hq][Sq] fp32 or NULL. 1 <= num_splits <= 256,
- * d in {64, 128, 512} (512: the value width of tpattn_fwd_dv). Two kernels:
- * one parallel over splits (many splits, few rows: decode) and one parallel
- * over output elements (few splits or many rows); TPATTN_COMBINE_COLS=0/1
- * forces either. */
+ * d in {64, 128, 512} (512: the value width of tpattn_fwd_dv). Three kernels:
+ * one parallel over splits (many splits, few rows: decode), one parallel over
+ * output elements (few splits or many rows; TPATTN_COMBINE_COLS=0/1 forces
+ * either of these two), and for 512-wide rows one workgroup per row
+ * (TPATTN_COMBINE_ROWS=0 turns it off). */
 int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                        int B, int Sq, int Hq, int d, int num_splits, int dtype, void* stream);
 

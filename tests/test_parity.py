@@ -177,12 +177,20 @@ def test_non_default_stream():
     assert_parity(o, lse, ro, rl, "bf16", "stream")
 
 
-@pytest.mark.parametrize("cols", ["0", "1"], ids=["split_groups", "columns"])
+@pytest.mark.parametrize("cols", ["0", "1", "rows"], ids=["split_groups", "columns", "rows"])
 @pytest.mark.parametrize("S,d,dtype", [(1, 128, "fp32"), (2, 64, "bf16"), (5, 128, "bf16"),
                                        (64, 128, "fp32"), (256, 64, "fp32"), (128, 128, "bf16"),
-                                       (7, 512, "bf16")])
+                                       (7, 512, "bf16"), (51, 512, "bf16"), (256, 512, "fp32"),
+                                       (1, 512, "fp32")])
 def test_combine_kernel_parity(S, d, dtype, cols, monkeypatch):
-    monkeypatch.setenv("TPATTN_COMBINE_COLS", cols)
+    # three kernels: split groups, columns, and (512-wide rows only) one workgroup per row
+    if cols == "rows":
+        if d != 512:
+            pytest.skip("the row-parallel combine serves 512-wide rows")
+        monkeypatch.setenv("TPATTN_COMBINE_ROWS", "1")
+    else:
+        monkeypatch.setenv("TPATTN_COMBINE_ROWS", "0")
+        monkeypatch.setenv("TPATTN_COMBINE_COLS", cols)
     B, Sq, Hq = 2, 3, 5
     rows = B * Sq * Hq
     o_part, lse_part = random_partials(10 + S, S, rows, d, p_empty=0.3)

@@ -486,6 +486,64 @@ __global__ void __launch_bounds__(256) lse_combine_cols_kernel(CombineParams p, 
     }
 }
 
+// Row-parallel combine for wide rows (the 512-wide values of the latent path):
+// one 512-thread workgroup per output row; thread (c4 = tid % C4, sq = tid / C4)
+// merges splits sq, sq + SQ, ... of its 4 columns online, eight partials in
+// flight, and the SQ partial states of each column quad are merged through LDS.
+// A row is read once by one workgroup, with every load of a thread issued in
+// batches instead of one dependent round per split.
+template <bool OUT_BF16, int D>
+__global__ void __launch_bounds__(512) lse_combine_rows_kernel(CombineParams p) {
+    constexpr int C4 = D / 4, SQ = 512 / C4;
+    static_assert(512 % C4 == 0, "column quads must divide the workgroup");
+    __shared__ float red_m[SQ][C4], red_l[SQ][C4];
+    __shared__ f32x4 red_a[SQ][C4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int c4 = tid % C4, sq = tid / C4;
+    const size_t rows = (size_t)p.rows;
+    const int S = p.num_splits;
+    LseState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int s0 = sq; s0 < S; s0 += 8 * SQ) {
+        float ls[8];
+        f32x4 ov[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int s = s0 + j * SQ;
+            ls[j] = -INFINITY;
+            if (s < S) {
+                ls[j] = p.lse_part[(size_t)s * rows + row];
+                ov[j] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + 4 * c4);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (ls[j] != -INFINITY) st = lse_merge(st, LseState{ls[j], 1.f, ov[j]});
+    }
+    red_m[sq][c4] = st.m;
+    red_l[sq][c4] = st.l;
+    red_a[sq][c4] = st.acc;
+    __syncthreads();
+    if (sq != 0) return;
+#pragma unroll
+    for (int g = 1; g < SQ; ++g) st = lse_merge(st, LseState{red_m[g][c4], red_l[g][c4], red_a[g][c4]});
+    const bool any = st.m != -INFINITY && st.l > 0.f;
+    const f32x4 o = st.acc * (any ? 1.f / st.l : 0.f);
+    if constexpr (OUT_BF16) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + 4 * c4) = w;
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + 4 * c4) = o;
+    }
+    if (c4 == 0 && p.lse) {
+        const int h = row % p.Hq;
+        const int pos = (row / p.Hq) % p.Sq;
+        const int bb = row / (p.Hq * p.Sq);
+        p.lse[((size_t)bb * p.Hq + h) * p.Sq + pos] = any ? st.m + logf(st.l) : -INFINITY;
+    }
+}
+
 template <int D, int NW>
 hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((attn_decode_kernel<D, NW>), grid, dim3(64 * NW), 0, stream, p);
@@ -517,6 +575,14 @@ bool combine_by_columns(int rows, int d, int num_splits) {
 }
 
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream) {
+    // 512-wide rows (latent values): one workgroup per row (measured on the latent
+    // verify shape, 16 splits x 544 rows: the column kernel took 11.1 us; on the
+    // 65,536-key prefix, 51 splits x 272 rows: 24 us with either other kernel)
+    if (d == 512 && env_flag("TPATTN_COMBINE_ROWS", 1) != 0) {
+        if (out_bf16) hipLaunchKernelGGL((lse_combine_rows_kernel<true, 512>), dim3(p.rows), dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL((lse_combine_rows_kernel<false, 512>), dim3(p.rows), dim3(512), 0, stream, p);
+        return hipGetLastError();
+    }
     if (combine_by_columns(p.rows, d, p.num_splits)) {
         const long long n = (long long)p.rows * (d / 4);
         dim3 grid((unsigned)((n + 255) / 256)), block(256);
