@@ -223,6 +223,26 @@ def test_varlen_small():
         assert_parity(o, lse, ro, rl, "bf16", f"varlen S={S}")
 
 
+@pytest.mark.parametrize("factor,causal,wl,d", [(8.0, True, -1, 128), (4.0, True, -1, 128),
+                                                (8.0, False, -1, 128), (8.0, True, 1000, 128),
+                                                (16.0, False, 300, 64), (2.0, True, -1, 64)])
+def test_prefill_score_jumps(factor, causal, wl, d):
+    # Keys are walked from the last block to the first. Scaling the first 64 keys
+    # (exact in bf16: a power of two) makes their scores jump far above the
+    # reference max the later keys set: x8 and x16 overflow the fp16 P of the
+    # steady-tile form (that tile runs again with the exact max), x4 and x2 stay
+    # inside fp16 with large P. The result must not depend on either.
+    B, H, S = 1, 4, 600
+    q, k, v = small_case(15, "bf16", B, H, H, S, S, d)
+    k[:, :64] = (k[:, :64].float() * factor).to(k.dtype)
+    scale = 1.0 / math.sqrt(d)
+    print(f"score jumps factor={factor} causal={causal} wl={wl} d={d}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window_left=wl, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_ref(q, k, v, causal, wl, scale)
+    assert_parity(o, lse, ro, rl, "bf16", f"jumps x{factor} c={causal} wl={wl} d={d}")
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads in the benchmark's launch configuration
 # ---------------------------------------------------------------------------

@@ -15,7 +15,10 @@
 //     v_permlane16/32_swap) with a lazily moved reference max: O is rescaled
 //     only when a score exceeds the reference by more than 2^8, which after the
 //     first tile of a row almost never happens; the row sums of P come from an
-//     extra MFMA with an all-ones operand instead of VALU adds;
+//     extra MFMA with an all-ones operand instead of VALU adds. Once every row
+//     of a wave has a reference, tiles skip the row max: P is formed against
+//     the reference and its row sums, which bound every element, detect an fp16
+//     overflow, after which the tile runs again with the exact max;
 //   * O^T += V^T P^T on 16x16x32 fp16 MFMA: P is rounded to fp16 (11 significant
 //     bits: one bf16 rounding of P would cost up to 2^-9 per term) and V^T comes
 //     from ds_read_b64_tr_b16 of the row-major fp16 tile.
@@ -53,6 +56,7 @@ struct PrefillTile {
     static constexpr int TILEB = BN * ROWB;    // bytes of one K (or V) tile
     static constexpr int STAGEB = 2 * TILEB;   // K + V
     static constexpr int LDS_BYTES = 2 * STAGEB;
+    static constexpr int QBYTES = BM * ROWB;   // the workgroup's Q rows (attn_prefill_kernel)
     static constexpr int KROWS_PER_DMA = 1024 / ROWB;              // rows per wave-wide DMA
     static constexpr int KDMA = BN / KROWS_PER_DMA;                // DMA instructions per tile
     static constexpr int KDMA_PER_WAVE = (KDMA + NWV - 1) / NWV;
@@ -132,10 +136,17 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     }
     wlo = row16_imax(wlo);
     whi = row16_imin(whi);
+    int row_span[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const bool none = row_hi[q] < row_lo[q];
+        row_span[q] = none ? 0 : row_hi[q] - row_lo[q];
+        if (none) row_lo[q] = 0x40000000;
+    }
 
     // ---- Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
-    u32x4 qf[NQ][NSLAB];
+    u32x4 qreg[NQ][NSLAB];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const bf16_t* qrow = qp + (((size_t)b * p.Sq + row_pos[q]) * p.Hq + row_head[q]) * D + 8 * lg;
@@ -144,28 +155,36 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
         for (int c = 0; c < NSLAB; ++c) {
             const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c);
             const u32x4 z = {0u, 0u, 0u, 0u};
-            qf[q][c] = use ? x : z;
+            qreg[q][c] = use ? x : z;
         }
     }
+    auto q_frag = [&](const int q, const int c) { return qreg[q][c]; };
 
     // O^T accumulators, and the row sums of P computed on the matrix core: an
-    // all-ones A operand turns the PV MFMA into sum_j P[j][i] for every lane of
-    // query column i, which also keeps l consistent with the fp16-rounded P.
-    f32x4 oacc[DT][NQ], lacc[NQ];
-    float m_run[NQ];
+    // all-ones A operand turns a PV-shaped MFMA into sum_j P[j][i] for every lane
+    // of query column i, which also keeps l consistent with the fp16-rounded P.
+    f32x4 oacc[DT][NQ];
+    float m_run[NQ], l_run[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         m_run[q] = -INFINITY;
-        lacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_run[q] = 0.f;
 #pragma unroll
         for (int u = 0; u < DT; ++u) oacc[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
     const float sl2 = p.scale_log2;
-    // Lazy max: the reference max of a row moves only when a new score exceeds
-    // it by more than 2^LAZY (log2 units), so P <= 2^LAZY stays well inside fp16
-    // and the O rescale (and its exponential) is skipped on most tiles.
+    // Lazy max: when the exact row max is taken, the reference max of a row moves
+    // only if a new score exceeds it by more than 2^LAZY (log2 units), so the O
+    // rescale (and its exponential) is skipped on most tiles.
     constexpr float LAZY = 8.f;
+    // Once every row of the wave has a finite reference max ("steady"), a tile
+    // skips the row max altogether: P = exp2(S - m_ref) is formed directly and
+    // its fp16 row sums (the matrix-core sums above, which l needs anyway) bound
+    // every element, since P >= 0. A sum at most P_MAX means no element overflowed
+    // fp16; otherwise (a score that jumped far above the reference, or an inf)
+    // the tile is recomputed from the K tile still in LDS with the exact max.
+    constexpr float P_MAX = 65504.f;
 
     // ---- K/V tile loads
     const size_t kv_stride = (size_t)p.Hkv * D;
@@ -222,52 +241,52 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     }
     __syncthreads();
 
-    int stage = 0;
-    for (int n = s_hi - 1; n >= s_lo; --n) {
-        const bool more = n > s_lo;
-        if (more) {  // prefetch the next (lower) tile into the other stage
-            load_k(n - 1, stage ^ 1);
-            load_v(n - 1);
-        }
-        const char* kt = smem + stage * STAGEB;
-        const char* vt = kt + TILEB;
-
-        // S^T = K . Q^T (raised wave priority while feeding the matrix core, so the
-        // partner wave on the SIMD runs its VALU work in the gaps)
+    f32x4 sacc[NT][NQ];
+    // S^T = K . Q^T for the tile at kt (raised wave priority while feeding the
+    // matrix core, so the partner wave on the SIMD runs its VALU work in the
+    // gaps), then -inf on the elements a row cannot see
+    auto scores = [&](const char* kt, const int key0) {
         if (PRIO) __builtin_amdgcn_s_setprio(1);
-        f32x4 sacc[NT][NQ];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int q = 0; q < NQ; ++q) sacc[tt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NSLAB; ++c) {
+            u32x4 qf[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) qf[q] = q_frag(q, c);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 const int rr = 16 * tt + li;
                 const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + rr * ROWB + 16 * ((4 * c + lg) ^ C::swz_k(rr)));
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) sacc[tt][q] = mfma_bf16(kf, qf[q][c], sacc[tt][q]);
+                for (int q = 0; q < NQ; ++q) sacc[tt][q] = mfma_bf16(kf, qf[q], sacc[tt][q]);
             }
         }
-
         if (PRIO) __builtin_amdgcn_s_setprio(0);
-        const int key0 = n * BN;
         if (!(key0 >= wlo && key0 + BN - 1 <= whi)) {
+            // key visible iff 0 <= key - lo <= span (one unsigned compare; rows
+            // with no visible key carry lo far above every key and span 0)
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
+            for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-                for (int q = 0; q < NQ; ++q)
+                for (int q = 0; q < NQ; ++q) {
+                    const int base = key0 + 16 * tt + 4 * lg - row_lo[q];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int key = key0 + 16 * tt + 4 * lg + e;
-                        if (key < row_lo[q] || key > row_hi[q]) sacc[tt][q][e] = -INFINITY;
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if ((uint32_t)(base + e) > (uint32_t)row_span[q]) sacc[tt][q][e] = -INFINITY;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-
-        // online softmax with a lazily moved reference max
+    };
+    // exact row max of the tile; moves the reference max (and rescales O and l)
+    // of the rows whose max exceeds it by more than 2^LAZY
+    auto exact_max = [&]() {
         bool raise[NQ];
         bool any_raise = false;
+        float mxs[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             float mx = -INFINITY;
@@ -275,6 +294,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             for (int tt = 0; tt < NT; ++tt)
                 mx = vmax(vmax(vmax(vmax(mx, sacc[tt][q][0]), sacc[tt][q][1]), sacc[tt][q][2]), sacc[tt][q][3]);
             mx = xor_max(mx);
+            mxs[q] = mx;
             raise[q] = m_run[q] == -INFINITY ? mx != -INFINITY : (mx - m_run[q]) * sl2 > LAZY;
             any_raise |= raise[q];
         }
@@ -282,19 +302,18 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 if (!raise[q]) continue;
-                float mx = -INFINITY;
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) mx = vmax(mx, sacc[tt][q][e]);
-                mx = xor_max(mx);
-                const float alpha = m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mx) * sl2);
-                m_run[q] = mx;
-                lacc[q] *= alpha;
+                const float alpha = m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mxs[q]) * sl2);
+                m_run[q] = mxs[q];
+                l_run[q] *= alpha;
 #pragma unroll
                 for (int u = 0; u < DT; ++u) oacc[u][q] *= alpha;
             }
         }
+    };
+    // P = exp2(S * scale * log2e - m_ref) as fp16 pairs, and the tile's row sums
+    u32x4 pf[NT / 2][NQ];
+    f32x4 tsum[NQ];
+    auto exps = [&]() {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const float neg = m_run[q] == -INFINITY ? 0.f : -m_run[q] * sl2;
@@ -303,23 +322,66 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sacc[tt][q][e] = fast_exp2(fmaf(sacc[tt][q][e], sl2, neg));
         }
+#pragma unroll
+        for (int pp = 0; pp < NT / 2; ++pp)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                pf[pp][q][0] = pack_f16x2(sacc[2 * pp][q][0], sacc[2 * pp][q][1]);
+                pf[pp][q][1] = pack_f16x2(sacc[2 * pp][q][2], sacc[2 * pp][q][3]);
+                pf[pp][q][2] = pack_f16x2(sacc[2 * pp + 1][q][0], sacc[2 * pp + 1][q][1]);
+                pf[pp][q][3] = pack_f16x2(sacc[2 * pp + 1][q][2], sacc[2 * pp + 1][q][3]);
+            }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            tsum[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pp = 0; pp < NT / 2; ++pp) tsum[q] = mfma_f16(ones, pf[pp][q], tsum[q]);
+        }
+    };
+
+    bool steady = false;  // every row of the wave has a finite reference max
+    bool redo = false;    // this tile runs again with the exact max
+    int stage = 0;
+    for (int n = s_hi - 1; n >= s_lo;) {
+        const bool more = n > s_lo;
+        if (more && !redo) {  // prefetch the next (lower) tile into the other stage
+            load_k(n - 1, stage ^ 1);
+            load_v(n - 1);
+        }
+        const char* kt = smem + stage * STAGEB;
+        const char* vt = kt + TILEB;
+        const int key0 = n * BN;
+
+        // online softmax: exact max until steady, then the bounded fast form; a
+        // steady tile whose row sums show an fp16 overflow runs again, exactly
+        scores(kt, key0);
+        if (!steady || redo) exact_max();
+        exps();
+        if (steady && !redo) {
+            bool bad = false;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) bad |= !(tsum[q][0] <= P_MAX);
+            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                redo = true;
+                continue;
+            }
+        }
+        redo = false;
+        if (!steady) {
+            bool open = false;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) open |= m_run[q] == -INFINITY;
+            steady = __builtin_amdgcn_ballot_w64(open) == 0;
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) l_run[q] += tsum[q][0];
 
         // O^T += V^T . P^T (fp16)
         if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int pp = 0; pp < NT / 2; ++pp) {
-            u32x4 pf[NQ];
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                pf[q][0] = pack_f16x2(sacc[2 * pp][q][0], sacc[2 * pp][q][1]);
-                pf[q][1] = pack_f16x2(sacc[2 * pp][q][2], sacc[2 * pp][q][3]);
-                pf[q][2] = pack_f16x2(sacc[2 * pp + 1][q][0], sacc[2 * pp + 1][q][1]);
-                pf[q][3] = pack_f16x2(sacc[2 * pp + 1][q][2], sacc[2 * pp + 1][q][3]);
-            }
             const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
             const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) lacc[q] = mfma_f16(ones, pf[q], lacc[q]);
 #pragma unroll
             for (int u = 0; u < DT; ++u) {
                 const int ch = 2 * u + cb;
@@ -327,7 +389,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
                 const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
                 const u32x4 vf = {a[0], a[1], c[0], c[1]};
 #pragma unroll
-                for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f16(vf, pf[q], oacc[u][q]);
+                for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f16(vf, pf[pp][q], oacc[u][q]);
             }
         }
 
@@ -338,6 +400,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
         }
         __syncthreads();
         stage ^= 1;
+        --n;
     }
 
     // ---- epilogue
@@ -345,7 +408,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         if (!row_ok[q]) continue;
-        const float l = lacc[q][0];
+        const float l = l_run[q];
         const bool any = l > 0.f;
         const float inv = any ? 1.f / l : 0.f;
         const float lse = any ? m_run[q] * p.scale + logf(l) : -INFINITY;
