@@ -105,6 +105,8 @@ SMALL = [
     ("bf16", 2, 8, 8, 64, 64, 128, False, 10, 1),
     ("bf16", 1, 16, 16, 257, 1025, 128, True, 300, 4),
     ("bf16", 2, 4, 2, 16, 700, 128, True, -1, 0),
+    ("bf16", 1, 16, 2, 2, 333, 128, True, -1, 0),   # decode tile: 2 positions x 8 heads, ragged halves
+    ("bf16", 2, 8, 2, 4, 95, 64, True, 20, 3),      # decode tile: 16 packed rows, window, d 64
     ("fp32", 1, 4, 2, 33, 70, 64, True, 5, 0),
     ("fp32", 2, 2, 2, 20, 150, 128, False, -1, 4),
     ("fp32", 1, 8, 1, 2, 333, 128, False, -1, 0),
@@ -314,6 +316,7 @@ ABLATIONS = [
     {"TPATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
     {"TPATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
     {"TPATTN_DECODE_WAVES": "8"},             # 8-wave decode workgroups
+    {"TPATTN_DECODE_KDMA": "0"},              # decode with K straight into registers
     {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
     {"TPATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
     {"TPATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order

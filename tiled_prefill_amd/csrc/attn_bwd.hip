@@ -1092,8 +1092,8 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         const int hq = hkv * G + g;
         const int valid = imin(BM, Sq - m * BM);
         const size_t row0 = ((size_t)b * Sq + m * BM) * p.Hq + hq;
-        const rsrc_t rq = make_rsrc(reinterpret_cast<const bf16_t*>(p.q) + row0 * D, (uint32_t)valid * row_bytes);
-        const rsrc_t rg = make_rsrc(reinterpret_cast<const bf16_t*>(p.dout) + row0 * D, (uint32_t)valid * row_bytes);
+        const rsrc_t rq = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.q) + row0 * D, (uint32_t)valid * row_bytes);
+        const rsrc_t rg = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.dout) + row0 * D, (uint32_t)valid * row_bytes);
         char* dq_ = smem + st * STAGEB;
         char* dg_ = dq_ + TILEB;
 #pragma unroll
@@ -1108,7 +1108,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         }
         if (wave < 2) {
             const float* src = (wave == 0 ? p.lse2 : p.dsum) + ((size_t)b * p.Hq + hq) * Sq + m * BM;
-            const rsrc_t rl = make_rsrc(src, (uint32_t)valid * 4);
+            const rsrc_t rl = make_rsrc_u(src, (uint32_t)valid * 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rl, (__attribute__((address_space(3))) void*)(dg_ + TILEB + wave * BM * 4), 4,
                 4 * lane, 0, 0, 0);

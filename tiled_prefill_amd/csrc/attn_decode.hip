@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams 
     const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
     auto block_bytes = [&](int n) { return (uint32_t)imin(KB, Skb - n * KB) * row_bytes; };
     auto load_k = [&](int n) {
-        const rsrc_t rk = make_rsrc(kbase + (size_t)n * KB * kv_stride, block_bytes(n));
+        const rsrc_t rk = make_rsrc_u(kbase + (size_t)n * KB * kv_stride, block_bytes(n));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams 
     // i.e. row RPI*i + l / CPR, chunk slot l % CPR, which holds the row's chunk
     // (slot ^ swz(row)).
     auto load_v = [&](int n) {
-        const rsrc_t rv = make_rsrc(vbase + (size_t)n * KB * kv_stride, block_bytes(n));
+        const rsrc_t rv = make_rsrc_u(vbase + (size_t)n * KB * kv_stride, block_bytes(n));
         const int r0 = lane / CPR, slot = lane % CPR;
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
@@ -302,6 +302,292 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams 
             w[0] = pack_bf16x2(oacc[u][0] * inv, oacc[u][1] * inv);
             w[1] = pack_bf16x2(oacc[u][2] * inv, oacc[u][3] * inv);
             *reinterpret_cast<u32x2*>(orow + 16 * u) = w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode with K through LDS. The kernel above loads K straight into MFMA
+// operand registers, so each load instruction covers 16 key rows x 64 bytes:
+// every 128-byte line is fetched by two instructions, and 64 MiB of the decode
+// workload read that way take 12.7 us against 11.95 us when each instruction
+// covers 4 whole rows. Here K and V both stream into LDS by buffer_load ... lds
+// (4 whole rows per instruction for d = 128) in 32-key halves of each 64-key
+// block, single-buffered per wave (16 KB per wave: two 4-wave workgroups per
+// CU), each half refilled as soon as it has been read: K of the next half
+// after the QK product, V after the PV product. K fragments are read back with
+// 16-byte LDS reads, chunk slots XOR-swizzled by row so the 16 rows of a read
+// hit distinct banks. The online softmax rescales O only when a half's max
+// exceeds the reference by more than 2^8 (P <= 256 as bf16 hi + lo parts).
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+struct DecodeKdmaTile {
+    static constexpr int KB = 64;              // keys per block (the planner's block)
+    static constexpr int HB = 32;              // keys per half
+    static constexpr int NSLAB = D / 32;       // 32-d slabs of the QK contraction
+    static constexpr int DT = D / 16;          // 16-wide d tiles of the output
+    static constexpr int CPR = D / 8;          // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;         // bytes per K / V row in LDS
+    static constexpr int RPI = 1024 / ROWB;    // rows per wave-wide DMA
+    static constexpr int NL = HB / RPI;        // DMAs per half (K or V)
+    static constexpr int HALFB = HB * ROWB;    // bytes of one half tile
+    static constexpr int WAVEB = 2 * HALFB;    // K half + V half
+    static constexpr int RED_BYTES = NW * (DT * 4 * 64 + 2 * 64) * 4;
+    static constexpr int LDS_BYTES = NW * WAVEB > RED_BYTES ? NW * WAVEB : RED_BYTES;
+    static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1; }
+};
+
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdParams p) {
+    using C = DecodeKdmaTile<D, NW>;
+    constexpr int KB = C::KB, HB = C::HB, NSLAB = C::NSLAB, DT = C::DT;
+    constexpr int CPR = C::CPR, RPI = C::RPI, NL = C::NL, ROWB = C::ROWB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    char* kl = smem + wave * C::WAVEB;  // this wave's K half, swizzled rows
+    char* vl = kl + C::HALFB;           // and its V half
+
+    const int hg = p.split_major ? (int)blockIdx.y % p.grid_heads : (int)blockIdx.y / p.num_splits;
+    const int split = p.split_major ? (int)blockIdx.y / p.grid_heads : (int)blockIdx.y % p.num_splits;
+    const int b = blockIdx.z;
+    int Skb = p.Sk;
+    if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
+    const int G = p.G;
+    const int hkv = p.pack ? hg : hg / G;
+    const int nrows = p.pack ? p.Sq * G : p.Sq;
+    const int delta = Skb - p.Sq;
+
+    // key blocks of this split ([FA-tiling] §3.2, §5.3)
+    int n_lo, n_hi;
+    n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, 16, KB, 0, &n_lo, &n_hi);
+    const int S_b = splits_for(imax(0, n_hi - n_lo), p.num_splits, p.chunk_blocks);
+    int s_lo = 0, s_hi = 0;
+    if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+
+    // this lane's query row (column li of every S^T tile); visible keys are
+    // those with 0 <= key - lo <= span (rows that see none: lo above every key)
+    const int r = li;
+    const bool row_ok = r < nrows;
+    const int pos = row_ok ? (p.pack ? r / G : r) : 0;
+    const int head = p.pack ? hkv * G + (row_ok ? r % G : 0) : hg;
+    int row_lo = 0, row_hi = Skb - 1;
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+    if (row_ok) {
+        if (p.window_left >= 0) row_lo = pos + delta - p.window_left;
+        if (p.causal) row_hi = imin(row_hi, pos + delta);
+        wlo = row_lo;
+        whi = row_hi;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+    const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
+    if (row_hi < row_lo) row_lo = 0x40000000;
+
+    // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
+    u32x4 qf[NSLAB];
+    {
+        const bf16_t* qrow = qp + (((size_t)b * p.Sq + pos) * p.Hq + head) * D + 8 * lg;
+        const bool use = row_ok && s_hi > s_lo;
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c);  // row 0 when !row_ok
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qf[c] = use ? x : z;
+        }
+    }
+
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    // half u = 2 n + h of the key range: keys [32 u, 32 u + 32); buffer resources
+    // over the rows that exist (rows at or past Skb read as zeros)
+    auto half_bytes = [&](int u) { return (uint32_t)imax(0, imin(HB, Skb - u * HB)) * row_bytes; };
+    // lane l of DMA i fills bytes [1024 i + 16 l, +16) of the half: row RPI i +
+    // l / CPR, slot l % CPR, which holds chunk (slot ^ swz(row))
+    auto dma_half = [&](const bf16_t* base, int u, char* dst, const bool is_k) {
+        const rsrc_t rs = make_rsrc_u(base + (size_t)u * HB * kv_stride, half_bytes(u));
+        const int r0 = lane / CPR, slot = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int rr = RPI * i + r0;
+            const int sw = is_k ? C::swz_k(rr) : C::swz_v(rr);
+            // (offset computed outside the builtin's argument list: a call there
+            // makes this compiler drop the kernel's host launch stub)
+            const uint32_t off = rr * row_bytes + 16 * (slot ^ sw);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off, 0, 0, 0);
+        }
+    };
+
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
+    constexpr float LAZY = 8.f;
+
+    // s_waitcnt: vmcnt(NL) (the older half-group landed, the newer may be in flight)
+    // and vmcnt(0); expcnt and lgkmcnt left at their maximum
+    constexpr int WAIT_NL = (NL & 15) | ((NL >> 4) << 14) | 0x0F70;
+    constexpr int WAIT_0 = 0x0F70;
+    constexpr int WAIT_LDS = 0xC07F;  // lgkmcnt(0)
+
+    // halves of this wave: u = 2 n + h for its blocks n = s_lo + wave, +NW, ...
+    int n = s_lo + wave;
+    if (n < s_hi) {
+        dma_half(kbase, 2 * n, kl, true);
+        dma_half(vbase, 2 * n, vl, false);
+    }
+    for (; n < s_hi; n += NW) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int u = 2 * n + h;
+            // the half after this one (this block's second, or the next block's first)
+            const bool more = h == 0 || n + NW < s_hi;
+            const int u_next = h == 0 ? u + 1 : 2 * (n + NW);
+
+            // S^T = K . Q^T for the half's 32 keys (K half landed; V half may still stream)
+            __builtin_amdgcn_s_waitcnt(WAIT_NL);
+            f32x4 sacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NSLAB; ++c) {
+                    const int rr = 16 * t + li;
+                    const u32x4 kf = *reinterpret_cast<const u32x4*>(kl + rr * ROWB + 16 * ((4 * c + lg) ^ C::swz_k(rr)));
+                    sacc[t] = mfma_bf16(kf, qf[c], sacc[t]);
+                }
+            }
+            if (more) {  // refill the K half once this wave's reads of it are done
+                __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+                dma_half(kbase, u_next, kl, true);
+            }
+
+            const int key0 = u * HB;
+            if (!(key0 >= wlo && key0 + HB - 1 <= whi)) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int base = key0 + 16 * t + 4 * lg - row_lo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if ((uint32_t)(base + e) > (uint32_t)row_span) sacc[t][e] = -INFINITY;
+                }
+            }
+
+            // online softmax, reference max moved lazily
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                mx = vmax(vmax(vmax(vmax(mx, sacc[t][0]), sacc[t][1]), sacc[t][2]), sacc[t][3]);
+            mx = xor_max(mx);
+            const bool raise = m_run == -INFINITY ? mx != -INFINITY : (mx - m_run) * sl2 > LAZY;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+                const float alpha = !raise ? 1.f : (m_run == -INFINITY ? 0.f : fast_exp2((m_run - mx) * sl2));
+                if (raise) m_run = mx;
+                l_run *= alpha;
+#pragma unroll
+                for (int w = 0; w < DT; ++w) oacc[w] *= alpha;
+            }
+            const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pv = fast_exp2(fmaf(sacc[t][e], sl2, neg));
+                    sacc[t][e] = pv;
+                    l_run += pv;
+                }
+
+            // O^T += V^T . P^T with P as bf16 hi + lo parts (V half landed)
+            if (more) __builtin_amdgcn_s_waitcnt(WAIT_NL);
+            else __builtin_amdgcn_s_waitcnt(WAIT_0);
+            const u32x2 s0 = split_bf16x2(sacc[0][0], sacc[0][1]);
+            const u32x2 s1 = split_bf16x2(sacc[0][2], sacc[0][3]);
+            const u32x2 s2 = split_bf16x2(sacc[1][0], sacc[1][1]);
+            const u32x2 s3 = split_bf16x2(sacc[1][2], sacc[1][3]);
+            const u32x4 ph = {s0[0], s1[0], s2[0], s3[0]};
+            const u32x4 pl = {s0[1], s1[1], s2[1], s3[1]};
+            const int ra = 4 * lg + (li >> 2), rb = ra + 16;
+            const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+#pragma unroll
+            for (int w = 0; w < DT; ++w) {
+                const int ch = 2 * w + cb;
+                const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vl + ra * ROWB + 16 * (ch ^ C::swz_v(ra)) + hb));
+                const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vl + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
+                const u32x4 vf = {a[0], a[1], c[0], c[1]};
+                oacc[w] = mfma_bf16(vf, ph, oacc[w]);
+                oacc[w] = mfma_bf16(vf, pl, oacc[w]);
+            }
+            if (more) {  // refill the V half once this wave's reads of it are done
+                __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+                dma_half(vbase, u_next, vl, false);
+            }
+        }
+    }
+    l_run = xor_sum(l_run);
+
+    // merge the waves' softmax states
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    float* red_o = red;                          // [NW][DT*4][64]
+    float* red_ml = red + NW * DT * 4 * 64;      // [NW][2][64]
+#pragma unroll
+    for (int w = 0; w < DT; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red_o[(wave * DT * 4 + w * 4 + e) * 64 + lane] = oacc[w][e];
+    red_ml[(wave * 2 + 0) * 64 + lane] = m_run;
+    red_ml[(wave * 2 + 1) * 64 + lane] = l_run;
+    __syncthreads();
+    if (wave != 0) return;
+    float mw[NW], mstar = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        mw[w] = red_ml[(w * 2 + 0) * 64 + lane];
+        mstar = vmax(mstar, mw[w]);
+    }
+    const float muse = mstar == -INFINITY ? 0.f : mstar;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < DT; ++w) oacc[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float a = fast_exp2((mw[w] - muse) * sl2);
+        l += a * red_ml[(w * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int x = 0; x < DT; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[x][e] += a * red_o[(w * DT * 4 + x * 4 + e) * 64 + lane];
+    }
+
+    // epilogue: the split partial (O_s normalised, lse_s) or the final O and lse
+    if (!row_ok) return;
+    const bool any = l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const float lse = any ? mstar * p.scale + logf(l) : -INFINITY;
+    const size_t row = ((size_t)b * p.Sq + pos) * p.Hq + head;
+    if (p.num_splits > 1) {
+        const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
+        if (lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+        if (any) {
+            float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
+#pragma unroll
+            for (int w = 0; w < DT; ++w) *reinterpret_cast<f32x4*>(orow + 16 * w) = oacc[w] * inv;
+        }
+    } else {
+        if (lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + head) * p.Sq + pos] = lse;
+        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * D + 4 * lg;
+#pragma unroll
+        for (int w = 0; w < DT; ++w) {
+            u32x2 wv;
+            wv[0] = pack_bf16x2(oacc[w][0] * inv, oacc[w][1] * inv);
+            wv[1] = pack_bf16x2(oacc[w][2] * inv, oacc[w][3] * inv);
+            *reinterpret_cast<u32x2*>(orow + 16 * w) = wv;
         }
     }
 }
@@ -550,8 +836,17 @@ hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, int NW>
+hipError_t launch_decode_kdma(const FwdParams& p, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_decode_kdma_kernel<D, NW>), grid, dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
 const FwdVariant* decode_variants() {
     static const FwdVariant v[] = {
+        // K through LDS in 32-key halves (see attn_decode_kdma_kernel)
+        {DT_BF16, 128, 16, 64, 1, 4, DecodeKdmaTile<128, 4>::LDS_BYTES, &launch_decode_kdma<128, 4>, 0, 0, 0, 0, 1},
+        {DT_BF16, 64, 16, 64, 1, 4, DecodeKdmaTile<64, 4>::LDS_BYTES, &launch_decode_kdma<64, 4>, 0, 0, 0, 0, 1},
         {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>, 0},
         {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>, 0},
         // 8 waves (512 keys per workgroup at one block per wave), one workgroup per CU

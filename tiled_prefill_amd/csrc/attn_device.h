@@ -126,6 +126,16 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// The same for a base and size the caller knows to be wave-uniform but the
+// compiler may hold in VGPRs (e.g. after v_med3 / v_min): read from the first
+// lane, so buffer instructions get scalar operands instead of a waterfall loop.
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                     __builtin_amdgcn_readfirstlane(bytes));
+}
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }

@@ -22,6 +22,7 @@ struct FwdVariant {
                             // keys permuted in blocks of this many (16 or 32)
     int persistent;         // > 0: persistent workgroups (this many per CU) over tile queues
     int dv;                 // value / output width when it differs from d (0: equal to d)
+    int kdma;               // decode kernels: 1 = K through LDS in 32-key halves, 0 = K into registers
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
