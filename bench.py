@@ -30,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tiled_prefill_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # kernel -> source file it is compiled from
-KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_prefill_kernel": "attn_prefill.hip",
+KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_decode_kdma_kernel": "attn_decode.hip",
+                  "attn_prefill_kernel": "attn_prefill.hip",
                   "attn_bwd_dkdv_dma_kernel": "attn_bwd.hip", "attn_bwd_dq_dma_kernel": "attn_bwd.hip"}
 
 
@@ -53,6 +54,11 @@ def parse():
                     help="first copy a buffer of this many MiB three times (a plain copy "
                          "of known size, to calibrate HBM byte counters)")
     return ap.parse_args()
+
+
+# the decode kernel the planner selects (TPATTN_DECODE_KDMA=0: the register-K form)
+DECODE_KERNEL = "attn_decode_kernel" if os.environ.get("TPATTN_DECODE_KDMA", "").strip() == "0" \
+    else "attn_decode_kdma_kernel"
 
 
 def source_hash(kernel: str) -> str:
@@ -335,7 +341,7 @@ def main():
         fwd_ms = prof["fwd_ms"] / max(1, prof["fwd_launches"])
         comb_ms = prof["combine_ms"] / max(1, prof["combine_launches"])
         achieved = (kv_bytes + q_bytes) / (fwd_ms * 1e-3) / 1e9
-        traffic = traffic_for("attn_decode_kernel", w.name)
+        traffic = traffic_for(DECODE_KERNEL, w.name)
         # distribution of single steps, each bracketed by events on the launch stream
         stream = torch.cuda.current_stream()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -481,7 +487,7 @@ def main():
     }
     if dec:
         line["pct_of_hbm_peak"] = round(100 * dec["value"] / HBM_PEAK_GBS, 2)
-        line["roofline"] = {"bound": "hbm", "kernel": "attn_decode_kernel<128, 4>",
+        line["roofline"] = {"bound": "hbm", "kernel": DECODE_KERNEL + "<128, 4>",
                             "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": dec["traffic"],
