@@ -211,10 +211,10 @@ int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, i
 
 /* Default split rule, a reading of [llama.cpp] for 256 CUs: 1 split when
  * tiles >= wg_per_cu * num_cus or there are fewer than 2 key blocks; else
- * max(s_occ, s_chunk) with s_occ = min(ceil(wg_per_cu * num_cus / tiles),
- * n_blocks) (reach wg_per_cu workgroups per CU) and s_chunk = n_blocks /
- * ceil(min_chunk_rows / block_n) (more splits only while each keeps
- * min_chunk_rows keys), at most 256. */
+ * min(s_occ, s_chunk), at least 1 and at most 256, with s_occ =
+ * min(ceil(wg_per_cu * num_cus / tiles), n_blocks) (toward wg_per_cu
+ * workgroups per CU) and s_chunk = n_blocks / ceil(min_chunk_rows / block_n)
+ * (every split keeps min_chunk_rows keys). */
 int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
                                 int min_chunk_rows, int wg_per_cu);
 

@@ -319,6 +319,7 @@ ABLATIONS = [
     {"TPATTN_DECODE_KDMA": "0"},              # decode with K straight into registers
     {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
     {"TPATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
+    {"TPATTN_SPLIT_RULE": "3"},               # occupancy first, below the 256-key chunk
     {"TPATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order
     {"TPATTN_COMBINE_COLS": "0"},             # split-group combine kernel everywhere
     {"TPATTN_COMBINE_COLS": "1"},             # column-parallel combine kernel everywhere

@@ -102,13 +102,17 @@ def test_splits_partition_the_block_range(S):
 
 
 def test_occupancy_rule():
-    # reach 2 workgroups per CU, then split further only while chunks keep 256 keys
+    # toward 2 workgroups per CU, but every split keeps 256 keys
     assert tpa.num_splits_occupancy(4, 256, 256, 128) == 128     # 32K keys, 4 tiles
-    assert tpa.num_splits_occupancy(32, 256, 65, 32) == 16       # below the chunk, for occupancy
+    assert tpa.num_splits_occupancy(4, 256, 512, 64) == 128      # the same keys in 64-key blocks
+    assert tpa.num_splits_occupancy(32, 256, 65, 32) == 8        # the chunk bounds it (65 / 8)
+    assert tpa.num_splits_occupancy(32, 256, 33, 64) == 8        # fp32 verify: 2065 keys, 32 tiles
+    assert tpa.num_splits_occupancy(4, 256, 4, 64) == 1          # 256 keys: one chunk
     assert tpa.num_splits_occupancy(2048, 256, 128, 64) == 1     # grid already full
     assert tpa.num_splits_occupancy(4, 256, 1, 64) == 1          # one key block
     assert tpa.num_splits_occupancy(1, 256, 4096, 64) == 256     # capped at 256 splits
-    assert tpa.num_splits_occupancy(4, 256, 4, 64) == 4          # never more splits than blocks
+    assert tpa.num_splits_occupancy(300, 256, 4096, 64) == 2     # occupancy bounds it: ceil(512 / 300)
+    assert tpa.num_splits_occupancy(4, 256, 4096, 64, min_chunk_rows=64) == 128  # 1-block chunks
 
 
 def _plan(name, **kw):
@@ -127,7 +131,9 @@ def test_workload_plans():
     p = _plan("window_prefill_bf16")
     assert p["num_splits"] == 1
     p = _plan("spec_verify_fp32")
-    assert p["num_splits"] > 1 and p["grid_x"] * p["grid_y"] * p["grid_z"] >= 2 * 256
+    assert p["num_splits"] == 8 and p["grid_x"] * p["grid_y"] * p["grid_z"] == 256  # 258-key splits
+    p = _plan("decode_fp32")
+    assert p["num_splits"] == 1  # 256 keys: a single chunk
     p = _plan("varlen_decode_bf16", sum_seqlens_k=16 * 8448)
     assert p["pack_gqa"] == 1 and p["chunk_blocks"] * p["block_n"] >= 256
     p = _plan("decode_fp32", num_splits=8)

@@ -49,12 +49,27 @@ int env_int(const char* name, int dflt) {
 // split-count rules
 // ---------------------------------------------------------------------------
 
-// Default rule, a reading of the [llama.cpp] thread for 256 CUs: first reach
-// wg_per_cu (2) workgroups per CU so a CU stays busy while one workgroup waits
-// at a barrier; beyond that, split further only while every split keeps at
-// least min_chunk_rows keys. Never more splits than key blocks, at most 256.
+// Default rule, a reading of the [llama.cpp] thread for 256 CUs: split toward
+// wg_per_cu (2) workgroups per CU, so a CU stays busy while one workgroup waits
+// at a barrier, but only as far as every split keeps at least min_chunk_rows
+// keys: S = min(ceil(target / tiles), n_blocks / chunk_blocks), at least 1, at
+// most 256. (Splits below the chunk cost more in partials to merge than they
+// gain: fp32 decode over 256 keys, 4 splits 12.6 us vs 1 split 9.9 us; fp32
+// verify, 2 x 16 heads x 17 rows over 2065 keys, 16 splits 36.5 us vs 8 35.2.)
 int occupancy_rule(int tiles, int num_cus, int n_blocks, int block_n, int min_chunk_rows,
                    int wg_per_cu) {
+    const int target = wg_per_cu * num_cus;
+    if (tiles >= target || n_blocks < 2) return 1;
+    const int min_chunk_blocks = imax(1, ceil_div(min_chunk_rows, block_n));
+    const int s_occ = imin(ceil_div(target, tiles), n_blocks);
+    const int s_chunk = n_blocks / min_chunk_blocks;
+    return imax(1, imin(TPATTN_MAX_SPLITS, imin(s_occ, s_chunk)));
+}
+
+// The other reading of the same text, as an ablation: reach the workgroup target
+// even below the minimum chunk, then split further while chunks keep it.
+int occupancy_first_rule(int tiles, int num_cus, int n_blocks, int block_n, int min_chunk_rows,
+                         int wg_per_cu) {
     const int target = wg_per_cu * num_cus;
     if (tiles >= target || n_blocks < 2) return 1;
     const int min_chunk_blocks = imax(1, ceil_div(min_chunk_rows, block_n));
@@ -255,7 +270,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     const long long tiles = (long long)p.B * q.grid_heads * q.num_m_blocks;
     const int min_chunk = env_int("TPATTN_MIN_CHUNK", 256);
     const int wg_per_cu = imax(1, env_int("TPATTN_WG_PER_CU", 2));
-    const int rule = env_int("TPATTN_SPLIT_RULE", 0);  // 0 occupancy, 1 fa3, 2 blog
+    const int rule = env_int("TPATTN_SPLIT_RULE", 0);  // 0 occupancy, 1 fa3, 2 blog, 3 occupancy first
     int S = 1;
     int chunk = 0;
     if (p.num_splits >= 1) {
@@ -268,6 +283,8 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                          p.causal || p.window_left >= 0, 128);
         } else if (rule == 2) {
             S = blog_rule(p.Sk);
+        } else if (rule == 3) {
+            S = occupancy_first_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
         } else if (p.varlen) {
             // per-sequence chunk: as many splits as keep >= 512 keys each (fewer
             // partials for the combine; measured on 16 sequences of 512..16384 keys:
