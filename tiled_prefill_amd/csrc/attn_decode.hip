@@ -532,7 +532,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     }
     l_run = xor_sum(l_run);
 
-    // merge the waves' softmax states
+    // merge the waves' softmax states: every wave merges a quarter of the d
+    // tiles (DT / NW of them) from all waves and writes that part of the output
+    static_assert(DT % NW == 0, "d tiles split evenly over the waves");
+    constexpr int DW = DT / NW;
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
     float* red_o = red;                          // [NW][DT*4][64]
@@ -544,7 +547,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     red_ml[(wave * 2 + 0) * 64 + lane] = m_run;
     red_ml[(wave * 2 + 1) * 64 + lane] = l_run;
     __syncthreads();
-    if (wave != 0) return;
     float mw[NW], mstar = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -553,19 +555,21 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     }
     const float muse = mstar == -INFINITY ? 0.f : mstar;
     float l = 0.f;
+    f32x4 om[DW];
 #pragma unroll
-    for (int w = 0; w < DT; ++w) oacc[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < DW; ++x) om[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         const float a = fast_exp2((mw[w] - muse) * sl2);
         l += a * red_ml[(w * 2 + 1) * 64 + lane];
 #pragma unroll
-        for (int x = 0; x < DT; ++x)
+        for (int x = 0; x < DW; ++x)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[x][e] += a * red_o[(w * DT * 4 + x * 4 + e) * 64 + lane];
+            for (int e = 0; e < 4; ++e) om[x][e] += a * red_o[(w * DT * 4 + (wave * DW + x) * 4 + e) * 64 + lane];
     }
 
-    // epilogue: the split partial (O_s normalised, lse_s) or the final O and lse
+    // epilogue: the split partial (O_s normalised, lse_s) or the final O and lse,
+    // d tiles wave * DW .. wave * DW + DW - 1 of it
     if (!row_ok) return;
     const bool any = l > 0.f;
     const float inv = any ? 1.f / l : 0.f;
@@ -573,21 +577,21 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     const size_t row = ((size_t)b * p.Sq + pos) * p.Hq + head;
     if (p.num_splits > 1) {
         const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
-        if (lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+        if (wave == 0 && lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
         if (any) {
             float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
 #pragma unroll
-            for (int w = 0; w < DT; ++w) *reinterpret_cast<f32x4*>(orow + 16 * w) = oacc[w] * inv;
+            for (int x = 0; x < DW; ++x) *reinterpret_cast<f32x4*>(orow + 16 * (wave * DW + x)) = om[x] * inv;
         }
     } else {
-        if (lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + head) * p.Sq + pos] = lse;
+        if (wave == 0 && lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + head) * p.Sq + pos] = lse;
         bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * D + 4 * lg;
 #pragma unroll
-        for (int w = 0; w < DT; ++w) {
+        for (int x = 0; x < DW; ++x) {
             u32x2 wv;
-            wv[0] = pack_bf16x2(oacc[w][0] * inv, oacc[w][1] * inv);
-            wv[1] = pack_bf16x2(oacc[w][2] * inv, oacc[w][3] * inv);
-            *reinterpret_cast<u32x2*>(orow + 16 * w) = wv;
+            wv[0] = pack_bf16x2(om[x][0] * inv, om[x][1] * inv);
+            wv[1] = pack_bf16x2(om[x][2] * inv, om[x][3] * inv);
+            *reinterpret_cast<u32x2*>(orow + 16 * (wave * DW + x)) = wv;
         }
     }
 }
