@@ -367,39 +367,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     int s_lo = 0, s_hi = 0;
     if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
 
-    // this lane's query row (column li of every S^T tile); visible keys are
-    // those with 0 <= key - lo <= span (rows that see none: lo above every key)
-    const int r = li;
-    const bool row_ok = r < nrows;
-    const int pos = row_ok ? (p.pack ? r / G : r) : 0;
-    const int head = p.pack ? hkv * G + (row_ok ? r % G : 0) : hg;
-    int row_lo = 0, row_hi = Skb - 1;
-    int wlo = -0x7fffffff, whi = 0x7fffffff;
-    if (row_ok) {
-        if (p.window_left >= 0) row_lo = pos + delta - p.window_left;
-        if (p.causal) row_hi = imin(row_hi, pos + delta);
-        wlo = row_lo;
-        whi = row_hi;
-    }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
-    const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
-    if (row_hi < row_lo) row_lo = 0x40000000;
-
-    // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
-    u32x4 qf[NSLAB];
-    {
-        const bf16_t* qrow = qp + (((size_t)b * p.Sq + pos) * p.Hq + head) * D + 8 * lg;
-        const bool use = row_ok && s_hi > s_lo;
-#pragma unroll
-        for (int c = 0; c < NSLAB; ++c) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * c);  // row 0 when !row_ok
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qf[c] = use ? x : z;
-        }
-    }
-
     const size_t kv_stride = (size_t)p.Hkv * D;
     const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
     const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
@@ -424,6 +391,46 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
         }
     };
 
+    // the first K half goes out before anything else, the Q rows next, then the
+    // first V half (the loop's waits count on that order: K, Q, V)
+    int n = s_lo + wave;
+    if (n < s_hi) dma_half(kbase, 2 * n, kl, true);
+
+    // this lane's query row (column li of every S^T tile); visible keys are
+    // those with 0 <= key - lo <= span (rows that see none: lo above every key)
+    const int r = li;
+    const bool row_ok = r < nrows;
+    const int pos = row_ok ? (p.pack ? r / G : r) : 0;
+    const int head = p.pack ? hkv * G + (row_ok ? r % G : 0) : hg;
+    int row_lo = 0, row_hi = Skb - 1;
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+    if (row_ok) {
+        if (p.window_left >= 0) row_lo = pos + delta - p.window_left;
+        if (p.causal) row_hi = imin(row_hi, pos + delta);
+        wlo = row_lo;
+        whi = row_hi;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+    const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
+    if (row_hi < row_lo) row_lo = 0x40000000;
+
+    // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]. Buffer loads
+    // over this batch's Q rows; a row the tile does not own reads zeros through
+    // an offset past the resource (no select, so nothing waits on Q before the
+    // first V half is issued)
+    u32x4 qf[NSLAB];
+    {
+        const rsrc_t rq = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.q) + (size_t)b * p.Sq * p.Hq * D,
+                                      (uint32_t)p.Sq * p.Hq * D * 2);
+        const bool use = row_ok && s_hi > s_lo;
+        const uint32_t qoff = use ? (uint32_t)(((pos * p.Hq + head) * D + 8 * lg) * 2) : 0x80000000u;
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) qf[c] = buf_load16(rq, qoff + 64 * c);
+    }
+
+    if (n < s_hi) dma_half(vbase, 2 * n, vl, false);
+
     f32x4 oacc[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -438,11 +445,6 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     constexpr int WAIT_LDS = 0xC07F;  // lgkmcnt(0)
 
     // halves of this wave: u = 2 n + h for its blocks n = s_lo + wave, +NW, ...
-    int n = s_lo + wave;
-    if (n < s_hi) {
-        dma_half(kbase, 2 * n, kl, true);
-        dma_half(vbase, 2 * n, vl, false);
-    }
     for (; n < s_hi; n += NW) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
