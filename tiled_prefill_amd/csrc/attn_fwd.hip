@@ -162,22 +162,22 @@ attn_fwd_kernel(FwdParams p) {
     const size_t kv_stride = (size_t)p.Hkv * D;
     u32x4 kst[ITEMS][4], vst[ITEMS][4];
 
+    // buffer loads over the tile's rows that exist: rows at or past Skb read as
+    // zeros, with no branch per load
+    const uint32_t row_bytes = (uint32_t)(kv_stride * C::ESZ);
     auto load_tile = [&](int n) {
+        const uint32_t valid = (uint32_t)imax(0, imin(BN, Skb - n * BN));
+        const rsrc_t rk = make_rsrc_u(kbase + (size_t)n * BN * kv_stride, valid * row_bytes);
+        const rsrc_t rv = make_rsrc_u(vbase + (size_t)n * BN * kv_stride, valid * row_bytes);
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
             const int item = tid + it * C::NTHR;
             const int c = item % CPR, rg = item / CPR;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = n * BN + 4 * rg + r;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (key < Skb) {
-                    kst[it][r] = *reinterpret_cast<const u32x4*>(kbase + key * kv_stride + c * CE);
-                    vst[it][r] = *reinterpret_cast<const u32x4*>(vbase + key * kv_stride + c * CE);
-                } else {
-                    kst[it][r] = z;
-                    vst[it][r] = z;
-                }
+                const uint32_t off = (uint32_t)(4 * rg + r) * row_bytes + 16 * c;
+                kst[it][r] = buf_load16(rk, off);
+                vst[it][r] = buf_load16(rv, off);
             }
         }
     };
