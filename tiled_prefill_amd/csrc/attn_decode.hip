@@ -376,18 +376,19 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     auto half_bytes = [&](int u) { return (uint32_t)imax(0, imin(HB, Skb - u * HB)) * row_bytes; };
     // lane l of DMA i fills bytes [1024 i + 16 l, +16) of the half: row RPI i +
     // l / CPR, slot l % CPR, which holds chunk (slot ^ swz(row))
+    // Issued untracked (dma16_untracked): every read of a half is preceded by
+    // the explicit vmcnt wait below, and every refill by an lgkmcnt(0) wait, so
+    // the V reads of one half do not also wait for the K refill issued after it.
     auto dma_half = [&](const bf16_t* base, int u, char* dst, const bool is_k) {
-        const rsrc_t rs = make_rsrc_u(base + (size_t)u * HB * kv_stride, half_bytes(u));
+        const u32x4 rs = rsrc_words_u(base + (size_t)u * HB * kv_stride, half_bytes(u));
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(dst));
         const int r0 = lane / CPR, slot = lane % CPR;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int rr = RPI * i + r0;
             const int sw = is_k ? C::swz_k(rr) : C::swz_v(rr);
-            // (offset computed outside the builtin's argument list: a call there
-            // makes this compiler drop the kernel's host launch stub)
             const uint32_t off = rr * row_bytes + 16 * (slot ^ sw);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, off, 0, 0, 0);
+            dma16_untracked(rs, off, l0 + 1024 * i);
         }
     };
 
@@ -438,11 +439,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     const float sl2 = p.scale_log2;
     constexpr float LAZY = 8.f;
 
-    // s_waitcnt: vmcnt(NL) (the older half-group landed, the newer may be in flight)
-    // and vmcnt(0); expcnt and lgkmcnt left at their maximum
-    constexpr int WAIT_NL = (NL & 15) | ((NL >> 4) << 14) | 0x0F70;
-    constexpr int WAIT_0 = 0x0F70;
-    constexpr int WAIT_LDS = 0xC07F;  // lgkmcnt(0)
+    // waits: vmcnt(NL) = the older half-group landed while the newer one (NL
+    // copies) may still be in flight; vmcnt(0) = everything landed
 
     // halves of this wave: u = 2 n + h for its blocks n = s_lo + wave, +NW, ...
     for (; n < s_hi; n += NW) {
@@ -454,7 +452,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
             const int u_next = h == 0 ? u + 1 : 2 * (n + NW);
 
             // S^T = K . Q^T for the half's 32 keys (K half landed; V half may still stream)
-            __builtin_amdgcn_s_waitcnt(WAIT_NL);
+            wait_vmcnt<NL>();
             f32x4 sacc[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -467,7 +465,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
                 }
             }
             if (more) {  // refill the K half once this wave's reads of it are done
-                __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+                wait_lgkmcnt0();
                 dma_half(kbase, u_next, kl, true);
             }
 
@@ -507,8 +505,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
                 }
 
             // O^T += V^T . P^T with P as bf16 hi + lo parts (V half landed)
-            if (more) __builtin_amdgcn_s_waitcnt(WAIT_NL);
-            else __builtin_amdgcn_s_waitcnt(WAIT_0);
+            if (more) wait_vmcnt<NL>();
+            else wait_vmcnt<0>();
             const u32x2 s0 = split_bf16x2(sacc[0][0], sacc[0][1]);
             const u32x2 s1 = split_bf16x2(sacc[0][2], sacc[0][3]);
             const u32x2 s2 = split_bf16x2(sacc[1][0], sacc[1][1]);
@@ -527,7 +525,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
                 oacc[w] = mfma_bf16(vf, pl, oacc[w]);
             }
             if (more) {  // refill the V half once this wave's reads of it are done
-                __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+                wait_lgkmcnt0();
                 dma_half(vbase, u_next, vl, false);
             }
         }

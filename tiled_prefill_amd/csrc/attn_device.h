@@ -140,6 +140,55 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// The same resource as four raw words (base, stride 0, size in bytes, the
+// format word make_rsrc uses), read from the first lane, for buffer
+// instructions issued by inline asm.
+__device__ __forceinline__ u32x4 rsrc_words_u(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 w;
+    w[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    w[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu;
+    w[2] = __builtin_amdgcn_readfirstlane(bytes);
+    w[3] = 0x00020000u;
+    return w;
+}
+
+// Global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
+// reads the buffer at byte voff and writes LDS bytes [lds + 16 l, +16); lds is
+// the wave-uniform LDS byte address. Issued from inline asm, so the compiler
+// does not track it. The compiler's own tracking of such copies is coarse: a
+// `ds_read_b64_tr_b16` (whose memory operand carries no alias information)
+// waits for every copy in flight, including one that fills a different buffer,
+// which serialises a prefetch with the reads of the buffer in use. Callers of
+// this form order everything themselves: an explicit s_waitcnt vmcnt before
+// the first LDS read of what a copy fills (vmcnt retires in issue order,
+// counting these copies with every other vector memory load), and an
+// lgkmcnt(0) wait before a copy overwrites LDS that reads may still use. The
+// compiler's own waits for its tracked loads stay correct (they only grow
+// stricter when these copies are in flight too). The LDS address goes in M0
+// (an operand the compiler sets); the s_nop covers the wait states between a
+// VALU write of an SGPR operand (v_readfirstlane) or of M0 and a vector memory
+// instruction that reads it.
+__device__ __forceinline__ void dma16_untracked(u32x4 rs, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rs), "{m0}"(lds)
+        : "memory");
+}
+// s_waitcnt written as a compiler memory barrier (no load or store moves across
+// it), for the copies above that the compiler does not track
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane s
 // supplies an 8-byte address; lane n receives element k = 0..3 from source lane
 // 4k + n/4, element n % 4. With source lane s pointing at row k0 + s/4, columns
