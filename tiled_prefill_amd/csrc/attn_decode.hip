@@ -331,7 +331,9 @@ struct DecodeKdmaTile {
     static constexpr int RPI = 1024 / ROWB;    // rows per wave-wide DMA
     static constexpr int NL = HB / RPI;        // DMAs per half (K or V)
     static constexpr int HALFB = HB * ROWB;    // bytes of one half tile
-    static constexpr int WAVEB = 2 * HALFB;    // K half + V half
+    static constexpr int QB = 16 * ROWB;       // the 16 (packed) query rows
+    static constexpr int NQL = QB / 1024;      // DMAs for the query rows
+    static constexpr int WAVEB = 2 * HALFB + QB;  // K half + V half + Q rows (80 KB per 4 waves at d = 128)
     static constexpr int RED_BYTES = NW * (DT * 4 * 64 + 2 * 64) * 4;
     static constexpr int LDS_BYTES = NW * WAVEB > RED_BYTES ? NW * WAVEB : RED_BYTES;
     static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -348,7 +350,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
     char* kl = smem + wave * C::WAVEB;  // this wave's K half, swizzled rows
-    char* vl = kl + C::HALFB;           // and its V half
+    char* vl = kl + C::HALFB;           // its V half
+    char* ql = vl + C::HALFB;           // and its copy of the query rows (K's swizzle)
 
     const int hg = p.split_major ? (int)blockIdx.y % p.grid_heads : (int)blockIdx.y / p.num_splits;
     const int split = p.split_major ? (int)blockIdx.y / p.grid_heads : (int)blockIdx.y % p.num_splits;
@@ -392,10 +395,31 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
         }
     };
 
-    // the first K half goes out before anything else, the Q rows next, then the
-    // first V half (the loop's waits count on that order: K, Q, V)
+    // A wave with a block sends, in this order, the first K half, its copy of
+    // the 16 query rows and the first V half, all into LDS (the waits count on
+    // that order: K, Q, V). The query rows take the copy path too, so nothing
+    // the compiler tracks is in flight: the first QK product waits for K and
+    // Q only, while the V half still streams. Row q of the copy is packed row
+    // q of this (batch, KV head); a row the tile does not own reads zeros
+    // through an offset past the buffer.
     int n = s_lo + wave;
-    if (n < s_hi) dma_half(kbase, 2 * n, kl, true);
+    if (n < s_hi) {
+        dma_half(kbase, 2 * n, kl, true);
+        const u32x4 rq = rsrc_words_u(reinterpret_cast<const bf16_t*>(p.q) + (size_t)b * p.Sq * p.Hq * D,
+                                      (uint32_t)p.Sq * p.Hq * D * 2);
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(ql));
+#pragma unroll
+        for (int i = 0; i < C::NQL; ++i) {
+            const int qr = RPI * i + lane / CPR, slot = lane % CPR;
+            const bool own = qr < nrows;
+            const int qpos = own ? (p.pack ? qr / G : qr) : 0;
+            const int qhead = p.pack ? hkv * G + (own ? qr % G : 0) : hg;
+            const uint32_t off = own ? (uint32_t)(((qpos * p.Hq + qhead) * D) * 2 + 16 * (slot ^ C::swz_k(qr)))
+                                     : 0x80000000u;
+            dma16_untracked(rq, off, l0 + 1024 * i);
+        }
+        dma_half(vbase, 2 * n, vl, false);
+    }
 
     // this lane's query row (column li of every S^T tile); visible keys are
     // those with 0 <= key - lo <= span (rows that see none: lo above every key)
@@ -416,21 +440,18 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
     if (row_hi < row_lo) row_lo = 0x40000000;
 
-    // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]. Buffer loads
-    // over this batch's Q rows; a row the tile does not own reads zeros through
-    // an offset past the resource (no select, so nothing waits on Q before the
-    // first V half is issued)
+    // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7], read from the
+    // wave's copy once K and Q have landed
     u32x4 qf[NSLAB];
-    {
-        const rsrc_t rq = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.q) + (size_t)b * p.Sq * p.Hq * D,
-                                      (uint32_t)p.Sq * p.Hq * D * 2);
-        const bool use = row_ok && s_hi > s_lo;
-        const uint32_t qoff = use ? (uint32_t)(((pos * p.Hq + head) * D + 8 * lg) * 2) : 0x80000000u;
+    if (n < s_hi) {
+        wait_vmcnt<NL>();
 #pragma unroll
-        for (int c = 0; c < NSLAB; ++c) qf[c] = buf_load16(rq, qoff + 64 * c);
+        for (int c = 0; c < NSLAB; ++c)
+            qf[c] = *reinterpret_cast<const u32x4*>(ql + li * ROWB + 16 * ((4 * c + lg) ^ C::swz_k(li)));
+    } else {
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) qf[c] = u32x4{0u, 0u, 0u, 0u};
     }
-
-    if (n < s_hi) dma_half(vbase, 2 * n, vl, false);
 
     f32x4 oacc[DT];
 #pragma unroll
