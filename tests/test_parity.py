@@ -90,6 +90,16 @@ def test_verify_page_shapes_fp32(B, H, q_len, kv_len):
     run_case("fp32", B, H, H, q_len, kv_len, 128, True, -1, 0, seed=2)
 
 
+@pytest.mark.parametrize("tile", ["0", "2"], ids=["widest_rows", "waves_2x4"])
+@pytest.mark.parametrize("case", [(2, 16, 16, 17, 2065, 128, True, -1, 0), (1, 8, 2, 9, 521, 128, True, -1, 3),
+                                  (2, 4, 4, 20, 300, 64, False, -1, 0), (1, 4, 1, 5, 77, 128, True, 2, 2),
+                                  (1, 2, 2, 32, 129, 64, True, 40, 1)])
+def test_verify_tile_choices_fp32(tile, case, monkeypatch):
+    # the other tiles the planner can pick for <= 32 query rows per KV head
+    monkeypatch.setenv("TPATTN_VERIFY_TILE", tile)
+    run_case("fp32", *case, seed=4)
+
+
 SMALL = [
     # dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl, S
     ("bf16", 2, 4, 4, 200, 200, 128, True, -1, 1),

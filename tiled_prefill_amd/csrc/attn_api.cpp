@@ -222,12 +222,17 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     }
     // general tile kernel: decode tiles (16 rows) for decode, 32-row tiles when a
     // KV head's query rows (packed) are at most 32, else the widest row tile
+    // (TPATTN_VERIFY_TILE: 0 = widest row tile, 1 = 32-row tile over 2 x 2 waves,
+    // 2 = 32-row tile over 2 x 4 waves with 128-key tiles)
     const int head_rows = G > 1 ? p.Sq * G : p.Sq;
-    const int want_bm = decode ? 16 : (head_rows <= 32 && env_int("TPATTN_VERIFY_TILE", 1) ? 32 : 0);
+    const int verify_tile = env_int("TPATTN_VERIFY_TILE", 1);
+    const int want_bm = decode ? 16 : (head_rows <= 32 && verify_tile ? 32 : 0);
+    const int want_wn = want_bm == 32 ? (verify_tile == 2 ? 4 : 2) : 0;
     for (int pass = 0; pass < 2 && !var; ++pass)
         for (const FwdVariant* v = fwd_variants(); v->launch; ++v) {
             if (v->dtype != p.dtype || v->d != p.d) continue;
-            const bool ok = pass == 0 ? (want_bm ? v->block_m == want_bm : v->block_m > 32)
+            const bool ok = pass == 0 ? (want_bm ? v->block_m == want_bm && (!want_wn || v->waves_n == want_wn)
+                                                 : v->block_m > 32)
                                       : (decode ? v->block_m <= 16 : v->block_m > 16);
             if (ok) {
                 var = v;

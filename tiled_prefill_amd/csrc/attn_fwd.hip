@@ -474,6 +474,9 @@ static const FwdVariant kVariants[] = {
     // (a 64-row tile would leave half its waves on padding rows)
     TPA_VARIANT(float, DT_FP32, 128, 32, 64, 2, 2),
     TPA_VARIANT(float, DT_FP32, 64, 32, 64, 2, 2),
+    // the same rows with 128-key tiles over 4 key waves (8 waves, two per SIMD)
+    TPA_VARIANT(float, DT_FP32, 128, 32, 128, 2, 4),
+    TPA_VARIANT(float, DT_FP32, 64, 32, 128, 2, 4),
     // fp32 decode: 16 rows, 64-key tiles split over 4 waves
     TPA_VARIANT(float, DT_FP32, 128, 16, 64, 1, 4),
     TPA_VARIANT(float, DT_FP32, 64, 16, 64, 1, 4),
