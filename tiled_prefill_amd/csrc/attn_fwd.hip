@@ -53,7 +53,9 @@ struct FwdTile {
     static constexpr int DL = D / 4;                  // d elements owned by one lane group
     static constexpr int CE = 16 / ESZ;               // elements per 16-byte chunk
     static constexpr int KST = D + CE;                // K tile row stride (elements)
-    static constexpr int VST = BN + CE;               // V^T tile row stride (elements)
+    // V^T tile row stride (elements): padded for bf16; for fp32 unpadded, with
+    // the 16-byte key slot of row d XOR-swizzled by vswz(d) instead
+    static constexpr int VST = BF ? BN + CE : BN;
     static constexpr int CPR = D / CE;                // 16-byte chunks per row
     static constexpr int ITEMS = (BN / 4) * CPR / NTHR;  // (4 rows x chunk) items per thread
     static constexpr int K_BYTES = BN * KST * ESZ;
@@ -65,6 +67,13 @@ struct FwdTile {
     static_assert(MW % 16 == 0, "rows per wave must be a multiple of 16");
     static_assert(NK % (BF ? 32 : 16) == 0, "keys per wave must fill the PV contraction");
     static_assert(ITEMS >= 1 && (BN / 4) * CPR % NTHR == 0, "tile load must divide evenly");
+    // fp32 V^T: slot of keys 4j..4j+3 in row d is j ^ vswz(d). The tile store
+    // writes rows d = 4c + e for 16 consecutive c (one key slot j) per 16 lanes,
+    // the P.V read rows d = 16u + i for 16 consecutive i: both see 16 distinct
+    // slots, i.e. distinct LDS banks (a row of 64 keys spans the 64 banks once).
+    // (masked to the row's BN / 4 slots when a row has fewer than 16)
+    static constexpr int VSLOTS = BN / 4 < 16 ? BN / 4 : 16;
+    static __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 4)) & (VSLOTS - 1); }
 };
 
 template <class T, int D, int BM, int BN, int WM, int WN>
@@ -211,7 +220,8 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     u32x4 col = {vst[it][0][e], vst[it][1][e], vst[it][2][e], vst[it][3][e]};
-                    *reinterpret_cast<u32x4*>(Vt + (4 * c + e) * VST + 4 * rg) = col;
+                    const int d = 4 * c + e;
+                    *reinterpret_cast<u32x4*>(Vt + d * VST + 4 * (rg ^ C::vswz(d))) = col;
                 }
             }
         }
@@ -336,8 +346,9 @@ attn_fwd_kernel(FwdParams p) {
             for (int t = 0; t < NT; ++t) {
 #pragma unroll
                 for (int u = 0; u < D / 16; ++u) {
+                    const int d = 16 * u + li;
                     const f32x4 vf = *reinterpret_cast<const f32x4*>(
-                        Vt + (16 * u + li) * VST + kw0 + 16 * t + 4 * lg);
+                        Vt + d * VST + 4 * (((kw0 + 16 * t + 4 * lg) >> 2) ^ C::vswz(d)));
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
 #pragma unroll
