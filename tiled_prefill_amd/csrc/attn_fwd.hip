@@ -280,7 +280,12 @@ attn_fwd_kernel(FwdParams p) {
                     }
         }
 
-        // online softmax (fp32): running max m, running sum l, rescale of O
+        // online softmax (fp32): running sum l and O against a reference max m
+        // that moves lazily, only when the tile's row max exceeds it by more than
+        // 2^LAZY (log2 units): P <= 2^LAZY then, and the rescale of O (a read,
+        // multiply and write of every accumulator) runs on few tiles. l and O
+        // share the reference, so O / l and lse = m * scale + ln l are exact.
+        constexpr float LAZY = 8.f;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             float mx = -INFINITY;
@@ -289,10 +294,15 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mx = vmax(mx, sacc[t][q][r]);
             mx = xor_max(mx);
-            const float m_new = vmax(m_run[q], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2((m_run[q] - m_use) * sl2);
-            const float neg = -m_use * sl2;
+            const bool raise = m_run[q] == -INFINITY ? mx != -INFINITY : (mx - m_run[q]) * sl2 > LAZY;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+                const float alpha = !raise ? 1.f : (m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mx) * sl2));
+                if (raise) m_run[q] = mx;
+                l_run[q] *= alpha;
+#pragma unroll
+                for (int u = 0; u < D / 16; ++u) oacc[u][q] *= alpha;
+            }
+            const float neg = m_run[q] == -INFINITY ? 0.f : -m_run[q] * sl2;
             float rs = 0.f;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -302,10 +312,7 @@ attn_fwd_kernel(FwdParams p) {
                     sacc[t][q][r] = pv;
                     rs += pv;
                 }
-            l_run[q] = l_run[q] * alpha + rs;
-            m_run[q] = m_new;
-#pragma unroll
-            for (int u = 0; u < D / 16; ++u) oacc[u][q] *= alpha;
+            l_run[q] += rs;
         }
 
         // O^T += V^T . P^T. On the bf16 path P enters the MFMA as two bf16
