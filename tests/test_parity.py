@@ -189,29 +189,36 @@ def test_non_default_stream():
     assert_parity(o, lse, ro, rl, "bf16", "stream")
 
 
-@pytest.mark.parametrize("cols", ["0", "1", "rows"], ids=["split_groups", "columns", "rows"])
+@pytest.mark.parametrize("cols", ["0", "1", "1l", "rows"],
+                         ids=["split_groups", "columns", "columns_looped", "rows"])
 @pytest.mark.parametrize("S,d,dtype", [(1, 128, "fp32"), (2, 64, "bf16"), (5, 128, "bf16"),
+                                       (8, 128, "fp32"), (9, 64, "bf16"), (16, 128, "fp32"),
                                        (64, 128, "fp32"), (256, 64, "fp32"), (128, 128, "bf16"),
                                        (7, 512, "bf16"), (51, 512, "bf16"), (256, 512, "fp32"),
                                        (1, 512, "fp32")])
 def test_combine_kernel_parity(S, d, dtype, cols, monkeypatch):
-    # three kernels: split groups, columns, and (512-wide rows only) one workgroup per row
+    # four kernels: split groups; columns, with every partial of a thread in flight
+    # at once (up to 16 splits) or looped; (512-wide rows only) one workgroup per row
     if cols == "rows":
         if d != 512:
             pytest.skip("the row-parallel combine serves 512-wide rows")
         monkeypatch.setenv("TPATTN_COMBINE_ROWS", "1")
     else:
         monkeypatch.setenv("TPATTN_COMBINE_ROWS", "0")
-        monkeypatch.setenv("TPATTN_COMBINE_COLS", cols)
+        monkeypatch.setenv("TPATTN_COMBINE_COLS", cols[0])
+        monkeypatch.setenv("TPATTN_COMBINE_SMALL", "0" if cols == "1l" else "1")
     B, Sq, Hq = 2, 3, 5
     rows = B * Sq * Hq
     o_part, lse_part = random_partials(10 + S, S, rows, d, p_empty=0.3)
     lse_part[:, 0] = float("-inf")  # a row with every split empty
     o_part[:, 0] = 0
+    # an empty split leaves its O_s unwritten: NaN there must never reach the output
+    o_dev = o_part.clone()
+    o_dev[torch.isneginf(lse_part)] = float("nan")
     out = torch.empty((B, Sq, Hq, d), dtype=torch.float32 if dtype == "fp32" else torch.bfloat16,
                       device=DEV)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=DEV)
-    tpa.lse_combine(o_part.to(DEV), lse_part.to(DEV), out, lse, B, Sq, Hq)
+    tpa.lse_combine(o_dev.to(DEV), lse_part.to(DEV), out, lse, B, Sq, Hq)
     ro, rl = oracle.lse_combine_ref(o_part, lse_part)
     ro = ro.reshape(B, Sq, Hq, d)
     rl = rl.reshape(B, Sq, Hq).transpose(0, 2, 1)

@@ -797,6 +797,64 @@ __global__ void __launch_bounds__(256) lse_combine_cols_kernel(CombineParams p, 
     }
 }
 
+// The same for at most SMAX splits: every lse_s and O_s load of the thread is
+// issued before any is used (one memory round trip instead of a max pass and
+// then groups of partials); split indices past S are clamped to S - 1 and
+// their weight forced to zero, so every load stays inside the workspace.
+template <bool OUT_BF16, int SMAX>
+__global__ void __launch_bounds__(256) lse_combine_cols_small_kernel(CombineParams p, int D) {
+    const int cpr = D / 4;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.rows * cpr) return;
+    const int row = (int)(idx / cpr), c4 = (int)(idx % cpr);
+    const size_t rows = (size_t)p.rows;
+    const int S = p.num_splits;
+    float ls[SMAX];
+    f32x4 ov[SMAX];
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int s = j < S ? j : S - 1;
+        ls[j] = p.lse_part[(size_t)s * rows + row];
+        ov[j] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + 4 * c4);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        if (j >= S) ls[j] = -INFINITY;
+        m = vmax(m, ls[j]);
+    }
+    float l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+            // an empty split (lse_s = -inf) may hold no O_s at all: select, never 0 * O_s
+            const bool live = ls[j] != -INFINITY;
+            const float w = live ? __expf(ls[j] - m) : 0.f;
+            l += w;
+            const f32x4 t = acc + w * ov[j];
+            acc = live ? t : acc;
+        }
+    }
+    const bool any = m != -INFINITY && l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const f32x4 o = acc * inv;
+    if constexpr (OUT_BF16) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(p.o) + (size_t)row * D + 4 * c4) = w;
+    } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + (size_t)row * D + 4 * c4) = o;
+    }
+    if (c4 == 0 && p.lse) {
+        const int h = row % p.Hq;
+        const int pos = (row / p.Hq) % p.Sq;
+        const int bb = row / (p.Hq * p.Sq);
+        p.lse[((size_t)bb * p.Hq + h) * p.Sq + pos] = any ? m + logf(l) : -INFINITY;
+    }
+}
+
 // Row-parallel combine for wide rows (the 512-wide values of the latent path):
 // one 512-thread workgroup per output row; thread (c4 = tid % C4, sq = tid / C4)
 // merges splits sq, sq + SQ, ... of its 4 columns online, eight partials in
@@ -906,8 +964,19 @@ hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream
     if (combine_by_columns(p.rows, d, p.num_splits)) {
         const long long n = (long long)p.rows * (d / 4);
         dim3 grid((unsigned)((n + 255) / 256)), block(256);
-        if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_kernel<true>), grid, block, 0, stream, p, d);
-        else hipLaunchKernelGGL((lse_combine_cols_kernel<false>), grid, block, 0, stream, p, d);
+        // every partial of a thread in flight at once for up to 8 / 16 splits
+        // (TPATTN_COMBINE_SMALL=0: the looped form for any count)
+        const int small = env_flag("TPATTN_COMBINE_SMALL", 1);
+        if (small && p.num_splits <= 8) {
+            if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_small_kernel<true, 8>), grid, block, 0, stream, p, d);
+            else hipLaunchKernelGGL((lse_combine_cols_small_kernel<false, 8>), grid, block, 0, stream, p, d);
+        } else if (small && p.num_splits <= 16) {
+            if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_small_kernel<true, 16>), grid, block, 0, stream, p, d);
+            else hipLaunchKernelGGL((lse_combine_cols_small_kernel<false, 16>), grid, block, 0, stream, p, d);
+        } else {
+            if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_kernel<true>), grid, block, 0, stream, p, d);
+            else hipLaunchKernelGGL((lse_combine_cols_kernel<false>), grid, block, 0, stream, p, d);
+        }
         return hipGetLastError();
     }
     dim3 grid(p.rows, d / 32), block(256);
