@@ -19,6 +19,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 #include "attn_plan.h"
@@ -665,10 +667,9 @@ __device__ __forceinline__ LseState lse_swap(const LseState& x, bool by32) {
     return y;
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int MAXI>
 __global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D) {
-    constexpr int SG = 32;                   // split groups
-    constexpr int MAXI = TPA_MAX_SPLITS / SG;
+    constexpr int SG = 32;                   // split groups (MAXI splits per thread: S <= SG * MAXI)
     __shared__ float red_m[4][8], red_l[4][8];
     __shared__ f32x4 red_a[4][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -678,29 +679,34 @@ __global__ void __launch_bounds__(256) lse_combine_kernel(CombineParams p, int D
     const int S = p.num_splits;
     const size_t rows = (size_t)p.rows;
 
+    // every load issued before any is used; a split index past S is clamped to
+    // S - 1 (the load stays inside the workspace) and its lse forced to -inf
+    // (a guarded load became a branch and a wait per split)
     f32x4 ov[MAXI];
     float ls[MAXI];
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
         const int s = sg + SG * i;
-        ls[i] = -INFINITY;
-        if (s < S) {
-            ls[i] = p.lse_part[(size_t)s * rows + row];
-            ov[i] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + d0 + 4 * c4);
-        }
+        const int sc = s < S ? s : S - 1;
+        ls[i] = p.lse_part[(size_t)sc * rows + row];
+        ov[i] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)sc * rows + row) * D + d0 + 4 * c4);
     }
-    // this thread's splits
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i)
+        if (sg + SG * i >= S) ls[i] = -INFINITY;
+    // this thread's splits (no branch around the sum, so the O_s loads are not
+    // sunk behind the max; an empty split contributes by select, never 0 * O_s)
     LseState st{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) st.m = vmax(st.m, ls[i]);
-    if (st.m != -INFINITY) {
+    const float mref = st.m == -INFINITY ? 0.f : st.m;
 #pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            if (ls[i] == -INFINITY) continue;
-            const float w = __expf(ls[i] - st.m);
-            st.l += w;
-            st.acc += w * ov[i];
-        }
+    for (int i = 0; i < MAXI; ++i) {
+        const bool live = ls[i] != -INFINITY;
+        const float w = live ? __expf(ls[i] - mref) : 0.f;
+        st.l += w;
+        const f32x4 t = st.acc + w * ov[i];
+        st.acc = live ? t : st.acc;
     }
     // merge the 8 split groups of the wave (lanes c4 + 8k): partner l ^ 8 is
     // row_mirror(half_mirror(.)), then the lane-bit swaps for l ^ 16 and l ^ 32
@@ -825,16 +831,16 @@ __global__ void __launch_bounds__(256) lse_combine_cols_small_kernel(CombinePara
     }
     float l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (m != -INFINITY) {
+    // no branch around the sum (the O_s loads stay ahead of the max); an empty
+    // split (lse_s = -inf) may hold no O_s at all: select, never 0 * O_s
+    const float mref = m == -INFINITY ? 0.f : m;
 #pragma unroll
-        for (int j = 0; j < SMAX; ++j) {
-            // an empty split (lse_s = -inf) may hold no O_s at all: select, never 0 * O_s
-            const bool live = ls[j] != -INFINITY;
-            const float w = live ? __expf(ls[j] - m) : 0.f;
-            l += w;
-            const f32x4 t = acc + w * ov[j];
-            acc = live ? t : acc;
-        }
+    for (int j = 0; j < SMAX; ++j) {
+        const bool live = ls[j] != -INFINITY;
+        const float w = live ? __expf(ls[j] - mref) : 0.f;
+        l += w;
+        const f32x4 t = acc + w * ov[j];
+        acc = live ? t : acc;
     }
     const bool any = m != -INFINITY && l > 0.f;
     const float inv = any ? 1.f / l : 0.f;
@@ -876,17 +882,15 @@ __global__ void __launch_bounds__(512) lse_combine_rows_kernel(CombineParams p) 
         float ls[8];
         f32x4 ov[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 8; ++j) {  // all eight loads first (indices past S clamped, then masked)
             const int s = s0 + j * SQ;
-            ls[j] = -INFINITY;
-            if (s < S) {
-                ls[j] = p.lse_part[(size_t)s * rows + row];
-                ov[j] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)s * rows + row) * D + 4 * c4);
-            }
+            const int sc = s < S ? s : S - 1;
+            ls[j] = p.lse_part[(size_t)sc * rows + row];
+            ov[j] = *reinterpret_cast<const f32x4*>(p.o_part + ((size_t)sc * rows + row) * D + 4 * c4);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if (ls[j] != -INFINITY) st = lse_merge(st, LseState{ls[j], 1.f, ov[j]});
+            if (s0 + j * SQ < S && ls[j] != -INFINITY) st = lse_merge(st, LseState{ls[j], 1.f, ov[j]});
     }
     red_m[sq][c4] = st.m;
     red_l[sq][c4] = st.l;
@@ -980,8 +984,18 @@ hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream
         return hipGetLastError();
     }
     dim3 grid(p.rows, d / 32), block(256);
-    if (out_bf16) hipLaunchKernelGGL((lse_combine_kernel<true>), grid, block, 0, stream, p, d);
-    else hipLaunchKernelGGL((lse_combine_kernel<false>), grid, block, 0, stream, p, d);
+    // splits per thread: the smallest of 1, 2, 4, 8 that covers S over 32 split groups
+    const int per = (p.num_splits + 31) / 32;
+    auto go = [&](auto maxi) {
+        constexpr int M = decltype(maxi)::value;
+        if (out_bf16) hipLaunchKernelGGL((lse_combine_kernel<true, M>), grid, block, 0, stream, p, d);
+        else hipLaunchKernelGGL((lse_combine_kernel<false, M>), grid, block, 0, stream, p, d);
+    };
+    static_assert(TPA_MAX_SPLITS <= 32 * 8, "split groups x splits per thread");
+    if (per <= 1) go(std::integral_constant<int, 1>{});
+    else if (per <= 2) go(std::integral_constant<int, 2>{});
+    else if (per <= 4) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, 8>{});
     return hipGetLastError();
 }
 
