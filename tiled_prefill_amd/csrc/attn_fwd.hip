@@ -141,15 +141,20 @@ attn_fwd_kernel(FwdParams p) {
 
     // ---- Q^T fragments: lane group g holds d in [g*DL, (g+1)*DL) of its row
     constexpr int QV = DL * (int)sizeof(T) / 16;  // 16-byte vectors per lane per row
+    // every load unconditional (a row the tile does not own points at row 0 of
+    // the batch, which exists, and is zeroed by a select afterwards): a load
+    // inside the condition compiled to a branch per load and a wait
     u32x4 qf[NQ][QV];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const T* qrow = reinterpret_cast<const T*>(p.q) +
                         (((size_t)b * p.Sq + row_pos[q]) * p.Hq + row_head[q]) * D + lg * DL;
+        const bool use = row_ok[q] && has_work;
 #pragma unroll
         for (int c = 0; c < QV; ++c) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qf[q][c] = (row_ok[q] && has_work) ? *reinterpret_cast<const u32x4*>(qrow + c * CE) : z;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + c * CE);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qf[q][c] = use ? x : z;
         }
     }
 
