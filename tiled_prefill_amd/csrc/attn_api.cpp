@@ -442,6 +442,19 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     // decode grids: the workgroups of one key range (all grid heads) are
     // dispatched together, so concurrent reads cover whole interleaved KV rows
     fp.split_major = env_int("TPATTN_SPLIT_MAJOR", plan.var->block_m <= 16 ? 1 : 0);
+    // decode tiles: block range and split share of fixed-length problems, and the
+    // grid-y divisor as a multiply-high
+    {
+        int lo = 0, hi = 0;
+        n_block_range(pr.Sq, pr.Sk, fp.G, fp.pack, fp.causal, fp.window_left, pl.block_m, pl.block_n, 0, &lo, &hi);
+        fp.dec_lo = lo;
+        fp.dec_hi = hi;
+        fp.dec_per = pl.num_splits > 1 ? ceil_div(imax(0, hi - lo), pl.num_splits) : imax(0, hi - lo);
+        fp.y_div = fp.split_major ? pl.grid_heads : pl.num_splits;
+        // (0: no exact multiplier for this grid; the kernel divides instead)
+        const bool exact = (unsigned long long)pl.grid_y * (unsigned long long)fp.y_div < (1ull << 32);
+        fp.y_magic = fp.y_div > 1 && exact ? (unsigned int)((1ull << 32) / (unsigned long long)fp.y_div + 1ull) : 0u;
+    }
 
     fp.d_head = pr.d;
     fp.skp = plan.skp;

@@ -355,22 +355,38 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     char* vl = kl + C::HALFB;           // its V half
     char* ql = vl + C::HALFB;           // and its copy of the query rows (K's swizzle)
 
-    const int hg = p.split_major ? (int)blockIdx.y % p.grid_heads : (int)blockIdx.y / p.num_splits;
-    const int split = p.split_major ? (int)blockIdx.y / p.grid_heads : (int)blockIdx.y % p.num_splits;
+    // (head, split) of this workgroup: blockIdx.y / y_div by a multiply-high
+    // with the host's magic number (no integer division before the first copy)
+    const unsigned int gy = blockIdx.y;
+    unsigned int qy = gy;
+    if (p.y_div > 1) qy = p.y_magic ? __umulhi(gy, p.y_magic) : gy / (unsigned int)p.y_div;
+    const int ry = (int)(gy - qy * (unsigned int)p.y_div);
+    const int hg = p.split_major ? ry : (int)qy;
+    const int split = p.split_major ? (int)qy : ry;
     const int b = blockIdx.z;
     int Skb = p.Sk;
     if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
     const int G = p.G;
-    const int hkv = p.pack ? hg : hg / G;
+    int hkv = hg;
+    if (!p.pack && G > 1) hkv = hg / G;
     const int nrows = p.pack ? p.Sq * G : p.Sq;
     const int delta = Skb - p.Sq;
 
-    // key blocks of this split ([FA-tiling] §3.2, §5.3)
-    int n_lo, n_hi;
-    n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, 16, KB, 0, &n_lo, &n_hi);
-    const int S_b = splits_for(imax(0, n_hi - n_lo), p.num_splits, p.chunk_blocks);
+    // key blocks of this split ([FA-tiling] §3.2, §5.3); a fixed-length problem
+    // takes the range and the blocks per split the host computed with the same
+    // functions (16-row tile, 64-key blocks)
     int s_lo = 0, s_hi = 0;
-    if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+    if (!p.seqlens_k && p.chunk_blocks <= 0) {
+        if (split < p.num_splits) {
+            s_lo = p.dec_lo + split * p.dec_per;
+            s_hi = imin(s_lo + p.dec_per, p.dec_hi);
+        }
+    } else {
+        int n_lo, n_hi;
+        n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, 16, KB, 0, &n_lo, &n_hi);
+        const int S_b = splits_for(imax(0, n_hi - n_lo), p.num_splits, p.chunk_blocks);
+        if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+    }
 
     const size_t kv_stride = (size_t)p.Hkv * D;
     const uint32_t row_bytes = (uint32_t)(kv_stride * 2);

@@ -144,6 +144,15 @@ struct FwdParams {
     int d_head;             // head dim (for launchers that dispatch on it)
     int vt_blk;             // key-permutation block of vt (16 or 32; see the V pre-pass)
     int* tile_counters;     // persistent kernels: one tile queue counter per XCD, zero at launch
+    // Decode tiles of fixed-length problems (seqlens_k null): the key-block
+    // range of the single query block and its blocks per split, computed once
+    // on the host, and y_magic = floor(2^32 / y_div) + 1 for y_div > 1 (y_div is
+    // grid_heads when split_major, else num_splits), so that blockIdx.y / y_div
+    // is one multiply-high: exact while blockIdx.y * y_div < 2^32 (else 0, and
+    // the kernel divides).
+    int dec_lo, dec_hi, dec_per;
+    int y_div;
+    unsigned int y_magic;
 };
 
 // Arguments of the log-sum-exp combine kernel. Every split writes its lse
