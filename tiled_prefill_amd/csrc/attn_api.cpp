@@ -450,10 +450,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         fp.dec_lo = lo;
         fp.dec_hi = hi;
         fp.dec_per = pl.num_splits > 1 ? ceil_div(imax(0, hi - lo), pl.num_splits) : imax(0, hi - lo);
-        fp.y_div = fp.split_major ? pl.grid_heads : pl.num_splits;
-        // (0: no exact multiplier for this grid; the kernel divides instead)
-        const bool exact = (unsigned long long)pl.grid_y * (unsigned long long)fp.y_div < (1ull << 32);
-        fp.y_magic = fp.y_div > 1 && exact ? (unsigned int)((1ull << 32) / (unsigned long long)fp.y_div + 1ull) : 0u;
+        fp.y_div = imax(1, fp.split_major ? pl.grid_heads : pl.num_splits);
+        div_magic((unsigned int)fp.y_div, &fp.y_mul, &fp.y_s1, &fp.y_s2);
     }
 
     fp.d_head = pr.d;

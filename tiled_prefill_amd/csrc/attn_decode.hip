@@ -355,11 +355,11 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     char* vl = kl + C::HALFB;           // its V half
     char* ql = vl + C::HALFB;           // and its copy of the query rows (K's swizzle)
 
-    // (head, split) of this workgroup: blockIdx.y / y_div by a multiply-high
-    // with the host's magic number (no integer division before the first copy)
+    // (head, split) of this workgroup: blockIdx.y / y_div by the host's
+    // multiplier (no branch and no integer division before the first copy)
     const unsigned int gy = blockIdx.y;
-    unsigned int qy = gy;
-    if (p.y_div > 1) qy = p.y_magic ? __umulhi(gy, p.y_magic) : gy / (unsigned int)p.y_div;
+    const unsigned int ty = __umulhi(gy, p.y_mul);
+    const unsigned int qy = (ty + ((gy - ty) >> p.y_s1)) >> p.y_s2;
     const int ry = (int)(gy - qy * (unsigned int)p.y_div);
     const int hg = p.split_major ? ry : (int)qy;
     const int split = p.split_major ? (int)qy : ry;
@@ -367,8 +367,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     int Skb = p.Sk;
     if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
     const int G = p.G;
-    int hkv = hg;
-    if (!p.pack && G > 1) hkv = hg / G;
+    const int hkv = hg;  // decode tiles always pack the G heads of a KV head (checked at launch)
     const int nrows = p.pack ? p.Sq * G : p.Sq;
     const int delta = Skb - p.Sq;
 
@@ -941,6 +940,7 @@ hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
 
 template <int D, int NW>
 hipError_t launch_decode_kdma(const FwdParams& p, dim3 grid, hipStream_t stream) {
+    if (!p.pack && p.G > 1) return hipErrorInvalidValue;  // the kernel takes grid head = KV head
     hipLaunchKernelGGL((attn_decode_kdma_kernel<D, NW>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }

@@ -146,14 +146,26 @@ struct FwdParams {
     int* tile_counters;     // persistent kernels: one tile queue counter per XCD, zero at launch
     // Decode tiles of fixed-length problems (seqlens_k null): the key-block
     // range of the single query block and its blocks per split, computed once
-    // on the host, and y_magic = floor(2^32 / y_div) + 1 for y_div > 1 (y_div is
-    // grid_heads when split_major, else num_splits), so that blockIdx.y / y_div
-    // is one multiply-high: exact while blockIdx.y * y_div < 2^32 (else 0, and
-    // the kernel divides).
+    // on the host. blockIdx.y / y_div (y_div = grid_heads when split_major, else
+    // num_splits) is t = umulhi(y_mul, y), (t + ((y - t) >> y_s1)) >> y_s2 with
+    // the host's round-up multiplier (Granlund and Montgomery, "Division by
+    // invariant integers using multiplication"): exact for every 32-bit y and
+    // any y_div >= 1, with no branch and no division on the device.
     int dec_lo, dec_hi, dec_per;
     int y_div;
-    unsigned int y_magic;
+    unsigned int y_mul;
+    int y_s1, y_s2;
 };
+
+// The multiplier and shifts above for divisor d >= 1: l = ceil(log2 d),
+// mul = floor(2^32 (2^l - d) / d) + 1, s1 = min(l, 1), s2 = max(l - 1, 0).
+inline void div_magic(unsigned int d, unsigned int* mul, int* s1, int* s2) {
+    int l = 0;
+    while (l < 32 && (1ull << l) < d) ++l;
+    *mul = (unsigned int)(((1ull << 32) * ((1ull << l) - d)) / d + 1ull);
+    *s1 = l < 1 ? l : 1;
+    *s2 = l - 1 > 0 ? l - 1 : 0;
+}
 
 // Arguments of the log-sum-exp combine kernel. Every split writes its lse
 // partial (-inf for an empty split), so the combine needs no block ranges.
