@@ -193,13 +193,16 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     }
     if (!var && decode && env_int("TPATTN_GENERIC_DECODE", 0) == 0) {
         const int want_waves = env_int("TPATTN_DECODE_WAVES", 4);  // waves per workgroup (4 or 8)
-        // 1: K through LDS in 32-key halves; 0: K straight into registers (ablation)
-        const int want_kdma = want_waves == 4 ? (env_int("TPATTN_DECODE_KDMA", 1) ? 1 : 0) : 0;
-        for (const FwdVariant* v = decode_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves && v->kdma == want_kdma) {
-                var = v;
-                break;
-            }
+        // 1: K through LDS in 32-key halves (else the register-K form where no
+        // such variant exists); 0: K straight into registers (ablation)
+        const int want_kdma = env_int("TPATTN_DECODE_KDMA", 1) ? 1 : 0;
+        for (int pass = 0; pass < 2 && !var; ++pass)
+            for (const FwdVariant* v = decode_variants(); v->launch; ++v)
+                if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves &&
+                    v->kdma == (pass == 0 ? want_kdma : 0)) {
+                    var = v;
+                    break;
+                }
     }
     if (!var && !decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
         // Tile rows ([FA-tiling] §2.5: smaller blocks where masking cuts tiles):

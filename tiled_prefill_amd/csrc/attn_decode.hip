@@ -953,6 +953,9 @@ const FwdVariant* decode_variants() {
         {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>, 0},
         {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>, 0},
         // 8 waves (512 keys per workgroup at one block per wave), one workgroup per CU
+        // (K through LDS: 8 x 20 KB, the whole 160 KB; d = 128 only, where the
+        // merge splits the 8 d tiles one per wave)
+        {DT_BF16, 128, 16, 64, 1, 8, DecodeKdmaTile<128, 8>::LDS_BYTES, &launch_decode_kdma<128, 8>, 0, 0, 0, 0, 1},
         {DT_BF16, 128, 16, 64, 1, 8, DecodeTile<128, 8>::LDS_BYTES, &launch_decode<128, 8>, 0},
         {DT_BF16, 64, 16, 64, 1, 8, DecodeTile<64, 8>::LDS_BYTES, &launch_decode<64, 8>, 0},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
