@@ -165,14 +165,16 @@ __device__ __forceinline__ u32x4 rsrc_words_u(const void* base, uint32_t bytes) 
 // counting these copies with every other vector memory load), and an
 // lgkmcnt(0) wait before a copy overwrites LDS that reads may still use. The
 // compiler's own waits for its tracked loads stay correct (they only grow
-// stricter when these copies are in flight too). The LDS address goes in M0
+// stricter when these copies are in flight too). The copies carry the
+// non-temporal hint (nt): decode streams K and V once, and without the hint
+// they displace lines that are read again soon. The LDS address goes in M0
 // (an operand the compiler sets); the s_nop covers the wait states between a
 // VALU write of an SGPR operand (v_readfirstlane) or of M0 and a vector memory
 // instruction that reads it.
 __device__ __forceinline__ void dma16_untracked(u32x4 rs, uint32_t voff, uint32_t lds) {
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
         :
         : "v"(voff), "s"(rs), "{m0}"(lds)
         : "memory");
