@@ -139,6 +139,10 @@ __device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t bytes) 
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+// The same with the non-temporal hint (cache policy bit 1: nt), for data read once.
+__device__ __forceinline__ u32x4 buf_load16_nt(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
 
 // The same resource as four raw words (base, stride 0, size in bytes, the
 // format word make_rsrc uses), read from the first lane, for buffer

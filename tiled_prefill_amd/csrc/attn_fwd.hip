@@ -190,8 +190,15 @@ attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t off = (uint32_t)(4 * rg + r) * row_bytes + 16 * c;
-                kst[it][r] = buf_load16(rk, off);
-                vst[it][r] = buf_load16(rv, off);
+                // decode and verify tiles (one query block per head) read each
+                // K/V row once: non-temporal; prefill tiles share them in L2
+                if constexpr (BM <= 32) {
+                    kst[it][r] = buf_load16_nt(rk, off);
+                    vst[it][r] = buf_load16_nt(rv, off);
+                } else {
+                    kst[it][r] = buf_load16(rk, off);
+                    vst[it][r] = buf_load16(rv, off);
+                }
             }
         }
     };
