@@ -61,9 +61,16 @@ DECODE_KERNEL = "attn_decode_kernel" if os.environ.get("TPATTN_DECODE_KDMA", "")
     else "attn_decode_kdma_kernel"
 
 
+# headers whose inline device code every kernel source compiles in
+SHARED_SOURCES = ("attn_device.h", "attn_plan.h")
+
+
 def source_hash(kernel: str) -> str:
-    path = os.path.join(CSRC, KERNEL_SOURCES[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over the kernel's source file and the shared device headers."""
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel],) + SHARED_SOURCES:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str):
