@@ -288,7 +288,7 @@ def run_latent_suite(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(every workload fits one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
