@@ -117,6 +117,7 @@ SMALL = [
     ("bf16", 2, 4, 2, 16, 700, 128, True, -1, 0),
     ("bf16", 1, 16, 2, 2, 333, 128, True, -1, 0),   # decode tile: 2 positions x 8 heads, ragged halves
     ("bf16", 2, 8, 2, 4, 95, 64, True, 20, 3),      # decode tile: 16 packed rows, window, d 64
+    ("bf16", 1, 8, 1, 2, 333, 128, False, -1, 0),   # decode tile: one KV head (grid-y divisor 1)
     ("fp32", 1, 4, 2, 33, 70, 64, True, 5, 0),
     ("fp32", 2, 2, 2, 20, 150, 128, False, -1, 4),
     ("fp32", 1, 8, 1, 2, 333, 128, False, -1, 0),
