@@ -315,12 +315,16 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams 
 // workload read that way take 12.7 us against 11.95 us when each instruction
 // covers 4 whole rows. Here K and V both stream into LDS by buffer_load ... lds
 // (4 whole rows per instruction for d = 128) in 32-key halves of each 64-key
-// block, single-buffered per wave (16 KB per wave: two 4-wave workgroups per
-// CU), each half refilled as soon as it has been read: K of the next half
-// after the QK product, V after the PV product. K fragments are read back with
+// block, single-buffered per wave (16 KB per wave, plus a 4 KB copy of the 16
+// query rows: two 4-wave workgroups fill a CU's 160 KB), each half refilled as
+// soon as it has been read: K of the next half after the QK product, V after
+// the PV product. The copies are untracked (explicit vmcnt waits order them)
+// and non-temporal (the cache is read once). K fragments are read back with
 // 16-byte LDS reads, chunk slots XOR-swizzled by row so the 16 rows of a read
 // hit distinct banks. The online softmax rescales O only when a half's max
 // exceeds the reference by more than 2^8 (P <= 256 as bf16 hi + lo parts).
+// Fixed-length problems take their key range and split share from the host,
+// so nothing is divided before the first copy.
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 struct DecodeKdmaTile {
