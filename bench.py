@@ -56,8 +56,8 @@ def parse():
     return ap.parse_args()
 
 
-# the decode kernel the planner selects (TPATTN_DECODE_KDMA=0: the register-K form)
-DECODE_KERNEL = "attn_decode_kernel" if os.environ.get("TPATTN_DECODE_KDMA", "").strip() == "0" \
+# the decode kernel the planner selects (ATTN_DECODE_KDMA=0: the register-K form)
+DECODE_KERNEL = "attn_decode_kernel" if os.environ.get("ATTN_DECODE_KDMA", "").strip() == "0" \
     else "attn_decode_kdma_kernel"
 
 
@@ -193,7 +193,7 @@ def run_suite(args):
 
 
 def run_bwd_suite(args):
-    """Backward workloads (tpattn_bwd) on the prefill shapes: TFLOP/s over the five
+    """Backward workloads (attn_bwd) on the prefill shapes: TFLOP/s over the five
     matrix products of the backward (10 d flops per visible pair)."""
     import torch
     import tiled_prefill_amd as tpa
@@ -238,7 +238,7 @@ def run_bwd_suite(args):
 
 
 def run_latent_suite(args):
-    """Latent-attention verify workloads (values of their own width, tpattn_fwd_dv)."""
+    """Latent-attention verify workloads (values of their own width, attn_fwd_dv)."""
     import torch
     import tiled_prefill_amd as tpa
     from workloads import LATENT_WORKLOADS, latent_case

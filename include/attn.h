@@ -1,12 +1,12 @@
 /*
- * tpattn.h -- C-ABI of the MI355X (gfx950) tiled flash-attention forward library
- * (libtpattn.so).
+ * attn.h -- C-ABI of the MI355X (gfx950) tiled flash-attention forward library
+ * (libattn.so).
  *
  * The library computes exact softmax attention
  *     O = softmax(scale * Q K^T + mask) V,     lse = log sum_j exp(scale q.k_j)
  * as a tiled flash-attention forward pass with online softmax, block skipping
  * for causal / sliding-window masks, GQA packing and split-KV with a separate
- * log-sum-exp combine kernel, and its gradients (tpattn_bwd) with the
+ * log-sum-exp combine kernel, and its gradients (attn_bwd) with the
  * key-block-outer backward loop.
  *
  * Sources (page title, section):
@@ -23,7 +23,7 @@
  *     q, o   [B][Sq][Hq][d]      element type `dtype`
  *     k, v   [B][Sk][Hkv][d]     element type `dtype`
  *     lse    [B][Hq][Sq]         fp32, natural log; may be NULL (not written)
- *   dtype: TPATTN_FP32 (0) or TPATTN_BF16 (1). o has q's dtype; softmax and
+ *   dtype: ATTN_FP32 (0) or ATTN_BF16 (1). o has q's dtype; softmax and
  *     accumulation are fp32 in both cases; bf16 outputs are rounded to nearest
  *     even.
  *   Heads: query head h reads key/value head h / (Hq / Hkv).
@@ -45,11 +45,11 @@
  *     library is thread-safe; on the GPU, calls on one device that use it must
  *     not overlap (issue them on one stream, or order the streams).
  *   Errors: a negative status code; nothing is launched and the message is
- *     available from tpattn_last_error() (thread-local). Argument checks never
+ *     available from attn_last_error() (thread-local). Argument checks never
  *     touch the GPU.
  */
-#ifndef TPATTN_H
-#define TPATTN_H
+#ifndef ATTN_H
+#define ATTN_H
 
 #include <stddef.h>
 
@@ -57,19 +57,19 @@
 extern "C" {
 #endif
 
-#define TPATTN_OK 0
-#define TPATTN_EINVAL (-1)       /* bad argument (null pointer, shape, range)   */
-#define TPATTN_EUNSUPPORTED (-2) /* valid but not built: d not in {64,128}, dtype */
-#define TPATTN_EHIP (-3)         /* a HIP runtime call or launch failed          */
-#define TPATTN_ENOMEM (-4)       /* the split workspace could not be allocated   */
+#define ATTN_OK 0
+#define ATTN_EINVAL (-1)       /* bad argument (null pointer, shape, range)   */
+#define ATTN_EUNSUPPORTED (-2) /* valid but not built: d not in {64,128}, dtype */
+#define ATTN_EHIP (-3)         /* a HIP runtime call or launch failed          */
+#define ATTN_ENOMEM (-4)       /* the split workspace could not be allocated   */
 
-#define TPATTN_FP32 0
-#define TPATTN_BF16 1
+#define ATTN_FP32 0
+#define ATTN_BF16 1
 
-#define TPATTN_MAX_SPLITS 256
+#define ATTN_MAX_SPLITS 256
 
 /* Execution plan of one call: what the host planner chose. */
-typedef struct tpattn_plan {
+typedef struct attn_plan_t {
     int pack_gqa;        /* 1: the G query heads of a KV head share a tile ([FA-tiling] §6) */
     int block_m;         /* query rows per tile (packed rows when pack_gqa)                 */
     int block_n;         /* key rows per tile                                              */
@@ -86,14 +86,14 @@ typedef struct tpattn_plan {
     int lpt;             /* 1: query blocks launched heaviest first ([FA-tiling] §4.4)      */
     long long visited_blocks;  /* key blocks all tiles visit (fixed-length problems)        */
     size_t workspace_bytes;    /* split partials needed (0 when num_splits == 1)           */
-} tpattn_plan;
+} attn_plan_t;
 
 /* Forward attention ([FA-tiling] §1-§6; [Occupancy] for the split path).
  * q, k, v, o: device pointers in the layouts above; lse: device fp32 or NULL.
  * B >= 0, Sq >= 0, Sk >= 0 (zero sizes are a no-op or give masked rows),
  * Hq, Hkv >= 1 with Hq % Hkv == 0, d in {64, 128}, scale finite and > 0,
  * window_left >= -1, num_splits <= 256. */
-int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Sq, int Sk, int d,
                int causal, int window_left, float scale, int num_splits,
                int dtype, void* stream);
@@ -101,14 +101,14 @@ int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /* Values of their own width: the latent-attention verify shape of [Occupancy]
  * (one KV head shared by every query head; keys 576 wide = 512 latent + 64
  * rotary, values 512 wide). q [B][Sq][Hq][d], k [B][Sk][Hkv][d],
- * v [B][Sk][Hkv][d_v], o [B][Sq][Hq][d_v] (dtype of q), lse as tpattn_fwd.
- * d_v == d behaves as tpattn_fwd; otherwise only bf16 with d = 576, d_v = 512
- * is built (TPATTN_EUNSUPPORTED else). The query heads of a KV head are always
+ * v [B][Sk][Hkv][d_v], o [B][Sq][Hq][d_v] (dtype of q), lse as attn_fwd.
+ * d_v == d behaves as attn_fwd; otherwise only bf16 with d = 576, d_v = 512
+ * is built (ATTN_EUNSUPPORTED else). The query heads of a KV head are always
  * packed into the row dimension ([FA-tiling] §6.3); num_splits <= 0 splits as far
  * as one workgroup per CU allows (the kernel holds one per CU), with at least 128
  * keys per split (the fp32 split partials are d_v wide). Other arguments as
- * tpattn_fwd. */
-int tpattn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
+ * attn_fwd. */
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v,
                   int causal, int window_left, float scale, int num_splits,
                   int dtype, void* stream);
@@ -119,41 +119,41 @@ int tpattn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* l
  * count of each sequence is ceil(its key blocks / chunk); the chunk follows the
  * occupancy rule from sum_seqlens_k (host: the sum of seqlens_k, or <= 0 if
  * unknown, then B * Sk is assumed). num_splits > 0 forces the maximum split
- * count instead. Other arguments as tpattn_fwd. */
-int tpattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+ * count instead. Other arguments as attn_fwd. */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int Sq, int Sk, int d,
                       int causal, int window_left, float scale, int num_splits,
                       int dtype, const int* seqlens_k, long long sum_seqlens_k,
                       void* stream);
 
-/* The plan tpattn_fwd / tpattn_fwd_varlen would use (varlen != 0 selects the
+/* The plan attn_fwd / attn_fwd_varlen would use (varlen != 0 selects the
  * latter). num_cus <= 0 reads the current device (256 when no device is
  * present). Pure host code: never touches the GPU beyond that query. */
-int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+int attn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
                     int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
-                    tpattn_plan* out);
+                    attn_plan_t* out);
 
 /* Backward pass: gradients of L = <dout, o> for o = attention(q, k, v) with the
- * mask of tpattn_fwd ([FA-tiling] §3.4: one workgroup per key block, looping
+ * mask of attn_fwd ([FA-tiling] §3.4: one workgroup per key block, looping
  * over the query blocks that see it -- get_m_block_min_max -- and the query
  * heads of its KV head; §4.6: Q, dO and an fp32 dQ accumulator are the working
- * set). Inputs: q, k, v as tpattn_fwd; o and lse the forward's outputs for
+ * set). Inputs: q, k, v as attn_fwd; o and lse the forward's outputs for
  * them (lse natural log, [B][Hq][Sq], -inf for rows that see no key); dout the
  * output gradient in o's layout. Outputs: dq in q's layout, dk and dv in k's
  * layout, all in `dtype` (dk, dv sum over the G query heads of a KV head).
  * Three kernels: row sums D = <dout, o>, the key-block kernel (dK, dV in
  * registers), and a query-block kernel for dQ that recomputes S and dP (no
- * atomics: the result is the same bits on every run). TPATTN_BWD_ATOMIC=1
+ * atomics: the result is the same bits on every run). ATTN_BWD_ATOMIC=1
  * selects the single-pass form of the pages instead (dQ added to an fp32
  * accumulator with atomics by the key-block kernel, then scaled; its last bits
- * depend on atomic timing). Sizes and errors as tpattn_fwd (d in {64, 128}; no
+ * depend on atomic timing). Sizes and errors as attn_fwd (d in {64, 128}; no
  * num_splits). */
-int tpattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
                int Sk, int d, int causal, int window_left, float scale, int dtype, void* stream);
 
-/* What tpattn_bwd would launch (host only). */
-typedef struct tpattn_bwd_plan {
+/* What attn_bwd would launch (host only). */
+typedef struct attn_bwd_plan_t {
     int block_m;         /* query rows per inner block                                     */
     int block_n;         /* keys per workgroup                                             */
     int num_n_blocks;    /* key blocks per (batch, KV head)                                */
@@ -163,51 +163,51 @@ typedef struct tpattn_bwd_plan {
     int dq_block_m;      /* query rows per workgroup of the dQ kernel (0: atomic form)     */
     long long visited_blocks;  /* (query block, key block) pairs of the key-block kernel   */
     size_t workspace_bytes;    /* lse2 + row sums (+ the fp32 dQ accumulator, atomic form) */
-} tpattn_bwd_plan;
-int tpattn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
-                    int dtype, tpattn_bwd_plan* out);
+} attn_bwd_plan_t;
+int attn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    int dtype, attn_bwd_plan_t* out);
 
 /* Split workspace bytes for B*Sq*Hq rows of head dim d and num_splits splits
  * (fp32 partial outputs plus fp32 partial lse). */
-size_t tpattn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits);
+size_t attn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits);
 
 /* Log-sum-exp combine of split partials ([FA-tiling] §5.1; [Occupancy]):
  *   lse[r] = log sum_s exp(lse_part[s][r]),  o[r] = sum_s exp(lse_part[s][r] - lse[r]) o_part[s][r]
  * over rows r = (b, i, h) in o's order (B*Sq*Hq rows). o_part [S][rows][d] fp32,
  * lse_part [S][rows] fp32 (-inf marks an empty split, whose o_part is not
  * read), o in `dtype`, lse [B][Hq][Sq] fp32 or NULL. 1 <= num_splits <= 256,
- * d in {64, 128, 512} (512: the value width of tpattn_fwd_dv). Three kernels:
+ * d in {64, 128, 512} (512: the value width of attn_fwd_dv). Three kernels:
  * one parallel over splits (many splits, few rows: decode), one parallel over
- * output elements (few splits or many rows; TPATTN_COMBINE_COLS=0/1 forces
+ * output elements (few splits or many rows; ATTN_COMBINE_COLS=0/1 forces
  * either of these two), and for 512-wide rows one workgroup per row
- * (TPATTN_COMBINE_ROWS=0 turns it off). */
-int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+ * (ATTN_COMBINE_ROWS=0 turns it off). */
+int attn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                        int B, int Sq, int Hq, int d, int num_splits, int dtype, void* stream);
 
 /* Host mirrors of the planner's integer rules, for tests and tooling. */
 /* Key-block range of query block m_block, then of split `split` of
  * `num_splits` ([FA-tiling] §3.2, §5.3); pack folds G heads into rows. */
-int tpattn_n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
+int attn_n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
                          int block_m, int block_n, int m_block, int split, int num_splits,
                          int* n_min, int* n_max);
 /* [FA-tiling] §6.2: pack iff varlen, or row efficiency without packing is
  * below 0.9 of the efficiency with packing. Returns 0 or 1. */
-int tpattn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int block_m);
+int attn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int block_m);
 /* [FA-tiling] §5.2 split heuristic (kept as an ablation of the default rule):
  * 1 split if tiles >= 0.8 * SMs (or ceil(KV/L2) splits for a long non-causal
  * KV), 1 if there are at most 4 key blocks, else the smallest split count
  * whose wave efficiency reaches 0.85 of the best. */
-int tpattn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
+int attn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
                           long long size_one_kv_head, int is_causal_or_local, int max_splits);
 /* [FA-tiling] §3.4 get_m_block_min_max: query-block range [m_min, m_max) whose
  * rows see a key of key block n_block (fixed key length Sk; empty if
  * m_max <= m_min). */
-int tpattn_m_block_range(int Sq, int Sk, int causal, int window_left, int block_m, int block_n,
+int attn_m_block_range(int Sq, int Sk, int causal, int window_left, int block_m, int block_n,
                          int n_block, int* m_min, int* m_max);
-/* The plan tpattn_fwd_dv would use (host only). */
-int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
+/* The plan attn_fwd_dv would use (host only). */
+int attn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
                        int window_left, int num_splits, int dtype, int num_cus,
-                       tpattn_plan* out);
+                       attn_plan_t* out);
 
 /* Default split rule, a reading of [llama.cpp] for 256 CUs: 1 split when
  * tiles >= wg_per_cu * num_cus or there are fewer than 2 key blocks; else
@@ -215,25 +215,25 @@ int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, i
  * min(ceil(wg_per_cu * num_cus / tiles), n_blocks) (toward wg_per_cu
  * workgroups per CU) and s_chunk = n_blocks / ceil(min_chunk_rows / block_n)
  * (every split keeps min_chunk_rows keys). */
-int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
+int attn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
                                 int min_chunk_rows, int wg_per_cu);
 
 /* Kernel timing for measurement tools: while enabled, every launch of the
  * forward kernel, the combine kernel and the V pre-pass (bf16 prefill kernels
  * that read V as fp16 V^T) is bracketed by HIP events on its stream.
- * tpattn_profile_end synchronises those events and returns the summed
+ * attn_profile_end synchronises those events and returns the summed
  * durations (ms) and launch counts per kind (any output pointer may be null),
  * then disables recording. */
-int tpattn_profile_begin(int max_launches);
-int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
+int attn_profile_begin(int max_launches);
+int attn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
                        int* combine_launches, double* prep_ms, int* prep_launches);
 /* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 6) with
  * kinds 0 forward, 1 combine, 2 V pre-pass / counter reset, 3 backward
  * key-block kernel, 4 backward pre- and post-passes, 5 backward dQ kernel. */
-int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds);
+int attn_profile_end_kinds(double* ms, int* launches, int n_kinds);
 
 /* Message of the last failure on this thread ("" if none). */
-const char* tpattn_last_error(void);
+const char* attn_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -13,13 +13,13 @@ FAKE = 0x1000  # never dereferenced: every call below fails argument checks firs
 def declared_functions():
     text = open(tpa.HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tpattn_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("tpattn_fwd", "tpattn_fwd_varlen", "tpattn_plan_fwd",
-                     "tpattn_workspace_bytes", "tpattn_lse_combine", "tpattn_last_error"):
+    for required in ("attn_fwd", "attn_fwd_varlen", "attn_plan_fwd",
+                     "attn_workspace_bytes", "attn_lse_combine", "attn_last_error"):
         assert required in names
 
 
@@ -34,7 +34,7 @@ def _fwd(**kw):
              causal=0, wl=-1, scale=0.125, splits=0, dtype=tpa.BF16)
     a.update(kw)
     lib = tpa.load()
-    return lib.tpattn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
                           a["Sq"], a["Sk"], a["d"], a["causal"], a["wl"], a["scale"],
                           a["splits"], a["dtype"], None)
 
@@ -57,28 +57,28 @@ def _fwd(**kw):
 ])
 def test_bad_arguments_are_rejected_without_launch(kw, code):
     assert _fwd(**kw) == code
-    assert tpa.load().tpattn_last_error().decode() != ""
+    assert tpa.load().attn_last_error().decode() != ""
 
 
 def test_varlen_requires_seqlens():
     lib = tpa.load()
-    rc = lib.tpattn_fwd_varlen(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 4, 1, 64, 64, 0, -1, 0.1, 0,
+    rc = lib.attn_fwd_varlen(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 4, 1, 64, 64, 0, -1, 0.1, 0,
                                tpa.BF16, None, -1, None)
     assert rc == -1
 
 
 def test_combine_rejects_bad_split_counts():
     lib = tpa.load()
-    assert lib.tpattn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 128, 0, 1, None) == -1
-    assert lib.tpattn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 128, 300, 1, None) == -1
-    assert lib.tpattn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 80, 4, 1, None) == -2
-    assert lib.tpattn_lse_combine(None, FAKE, FAKE, None, 1, 1, 4, 128, 4, 1, None) == -1
+    assert lib.attn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 128, 0, 1, None) == -1
+    assert lib.attn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 128, 300, 1, None) == -1
+    assert lib.attn_lse_combine(FAKE, FAKE, FAKE, None, 1, 1, 4, 80, 4, 1, None) == -2
+    assert lib.attn_lse_combine(None, FAKE, FAKE, None, 1, 1, 4, 128, 4, 1, None) == -1
 
 
 def test_plan_rejects_bad_arguments():
-    with pytest.raises(tpa.TpAttnError):
+    with pytest.raises(tpa.AttnError):
         tpa.plan(1, 3, 2, 4, 4, 64, num_cus=256)
-    with pytest.raises(tpa.TpAttnError):
+    with pytest.raises(tpa.AttnError):
         tpa.plan(1, 4, 4, 4, 4, 80, num_cus=256)
 
 
@@ -98,7 +98,7 @@ def _bwd(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
              Hq=4, Hkv=2, Sq=8, Sk=8, d=64, causal=0, wl=-1, scale=0.125, dtype=tpa.BF16)
     a.update(kw)
-    return tpa.load().tpattn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+    return tpa.load().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
                                  a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
                                  a["d"], a["causal"], a["wl"], a["scale"], a["dtype"], None)
 
@@ -110,7 +110,7 @@ def _bwd(**kw):
 ])
 def test_bwd_bad_arguments_are_rejected_without_launch(kw, code):
     assert _bwd(**kw) == code
-    assert tpa.load().tpattn_last_error().decode() != ""
+    assert tpa.load().attn_last_error().decode() != ""
 
 
 def test_python_binding_refuses_cpu_tensors_in_every_entry_point():
@@ -128,10 +128,10 @@ def test_python_binding_refuses_cpu_tensors_in_every_entry_point():
 
 
 def test_host_block_range_mirrors_reject_bad_arguments():
-    with pytest.raises(tpa.TpAttnError):
+    with pytest.raises(tpa.AttnError):
         tpa.m_block_range(8, 8, True, -2, 64, 64, 0)
-    with pytest.raises(tpa.TpAttnError):
+    with pytest.raises(tpa.AttnError):
         tpa.m_block_range(8, 8, True, -1, 0, 64, 0)
-    with pytest.raises(tpa.TpAttnError):
+    with pytest.raises(tpa.AttnError):
         tpa.plan_bwd(1, 6, 4, 8, 8, 64)
     assert tpa.m_block_range(0, 8, True, -1, 64, 64, 0)[1] == 0   # no query rows: empty

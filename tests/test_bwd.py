@@ -1,4 +1,4 @@
-"""GPU parity of the backward pass (tpattn_bwd) against the fp64 oracle.
+"""GPU parity of the backward pass (attn_bwd) against the fp64 oracle.
 
 The forward (o, lse) comes from the library's own forward kernels, as in
 training; the gradients are compared with attn_bwd_ref on the same seeded
@@ -90,12 +90,12 @@ def test_bwd_small_shapes(case):
 
 
 @pytest.mark.parametrize("env", [
-    {"TPATTN_BWD_BN": "128"},                              # 32 keys per wave
-    {"TPATTN_BWD_DQ_ROWS": "128"},                         # 128-row dQ blocks
-    {"TPATTN_BWD_DMA": "1"},                               # register-staged query tiles
-    {"TPATTN_BWD_DMA": "0"},                               # register-staged tiles in both
-    {"TPATTN_BWD_ATOMIC": "1"},                            # dQ by fp32 atomics
-    {"TPATTN_BWD_ATOMIC": "1", "TPATTN_BWD_BN": "128"},
+    {"ATTN_BWD_BN": "128"},                              # 32 keys per wave
+    {"ATTN_BWD_DQ_ROWS": "128"},                         # 128-row dQ blocks
+    {"ATTN_BWD_DMA": "1"},                               # register-staged query tiles
+    {"ATTN_BWD_DMA": "0"},                               # register-staged tiles in both
+    {"ATTN_BWD_ATOMIC": "1"},                            # dQ by fp32 atomics
+    {"ATTN_BWD_ATOMIC": "1", "ATTN_BWD_BN": "128"},
 ])
 def test_bwd_variants(env, monkeypatch):
     # the selectable variants (ablations) on ragged, masked, GQA shapes

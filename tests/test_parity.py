@@ -96,7 +96,7 @@ def test_verify_page_shapes_fp32(B, H, q_len, kv_len):
                                   (1, 2, 2, 32, 129, 64, True, 40, 1)])
 def test_verify_tile_choices_fp32(tile, case, monkeypatch):
     # the other tiles the planner can pick for <= 32 query rows per KV head
-    monkeypatch.setenv("TPATTN_VERIFY_TILE", tile)
+    monkeypatch.setenv("ATTN_VERIFY_TILE", tile)
     run_case("fp32", *case, seed=4)
 
 
@@ -203,11 +203,11 @@ def test_combine_kernel_parity(S, d, dtype, cols, monkeypatch):
     if cols == "rows":
         if d != 512:
             pytest.skip("the row-parallel combine serves 512-wide rows")
-        monkeypatch.setenv("TPATTN_COMBINE_ROWS", "1")
+        monkeypatch.setenv("ATTN_COMBINE_ROWS", "1")
     else:
-        monkeypatch.setenv("TPATTN_COMBINE_ROWS", "0")
-        monkeypatch.setenv("TPATTN_COMBINE_COLS", cols[0])
-        monkeypatch.setenv("TPATTN_COMBINE_SMALL", "0" if cols == "1l" else "1")
+        monkeypatch.setenv("ATTN_COMBINE_ROWS", "0")
+        monkeypatch.setenv("ATTN_COMBINE_COLS", cols[0])
+        monkeypatch.setenv("ATTN_COMBINE_SMALL", "0" if cols == "1l" else "1")
     B, Sq, Hq = 2, 3, 5
     rows = B * Sq * Hq
     o_part, lse_part = random_partials(10 + S, S, rows, d, p_empty=0.3)
@@ -322,25 +322,25 @@ def test_prefill_full_sampled(name):
 # every kernel path a planner switch can select (ablations included)
 # ---------------------------------------------------------------------------
 ABLATIONS = [
-    {"TPATTN_PREFILL_SKIP": "1"},             # prefill with raised wave priority
-    {"TPATTN_PREFILL_SKIP": "2"},             # software-pipelined prefill
-    {"TPATTN_PREFILL_WAVES": "4"},            # 128-row tiles (default with a window)
-    {"TPATTN_PREFILL_WAVES": "8"},            # 256-row tiles (default without one)
-    {"TPATTN_PREFILL_PERSIST": "1"},          # persistent workgroups, per-XCD tile queues
-    {"TPATTN_PREFILL_PERSIST": "1", "TPATTN_PREFILL_WAVES": "8"},
-    {"TPATTN_PREFILL_VT": "16"},              # 32x32 MFMA kernel on fp16 V^T
-    {"TPATTN_PREFILL_VT": "16", "TPATTN_PREFILL_WAVES": "8"},
-    {"TPATTN_PREFILL_VT": "16", "TPATTN_PREFILL_WAVES": "4"},
-    {"TPATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
-    {"TPATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
-    {"TPATTN_DECODE_WAVES": "8"},             # 8-wave decode workgroups
-    {"TPATTN_DECODE_KDMA": "0"},              # decode with K straight into registers
-    {"TPATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
-    {"TPATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
-    {"TPATTN_SPLIT_RULE": "3"},               # occupancy first, below the 256-key chunk
-    {"TPATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order
-    {"TPATTN_COMBINE_COLS": "0"},             # split-group combine kernel everywhere
-    {"TPATTN_COMBINE_COLS": "1"},             # column-parallel combine kernel everywhere
+    {"ATTN_PREFILL_SKIP": "1"},             # prefill with raised wave priority
+    {"ATTN_PREFILL_SKIP": "2"},             # software-pipelined prefill
+    {"ATTN_PREFILL_WAVES": "4"},            # 128-row tiles (default with a window)
+    {"ATTN_PREFILL_WAVES": "8"},            # 256-row tiles (default without one)
+    {"ATTN_PREFILL_PERSIST": "1"},          # persistent workgroups, per-XCD tile queues
+    {"ATTN_PREFILL_PERSIST": "1", "ATTN_PREFILL_WAVES": "8"},
+    {"ATTN_PREFILL_VT": "16"},              # 32x32 MFMA kernel on fp16 V^T
+    {"ATTN_PREFILL_VT": "16", "ATTN_PREFILL_WAVES": "8"},
+    {"ATTN_PREFILL_VT": "16", "ATTN_PREFILL_WAVES": "4"},
+    {"ATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
+    {"ATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
+    {"ATTN_DECODE_WAVES": "8"},             # 8-wave decode workgroups
+    {"ATTN_DECODE_KDMA": "0"},              # decode with K straight into registers
+    {"ATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
+    {"ATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
+    {"ATTN_SPLIT_RULE": "3"},               # occupancy first, below the 256-key chunk
+    {"ATTN_SPLIT_MAJOR": "0"},              # head-major decode grid order
+    {"ATTN_COMBINE_COLS": "0"},             # split-group combine kernel everywhere
+    {"ATTN_COMBINE_COLS": "1"},             # column-parallel combine kernel everywhere
 ]
 
 

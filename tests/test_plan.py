@@ -149,7 +149,7 @@ def test_causal_visited_blocks_about_half():
 def test_persistent_grid_is_resident_workgroups(monkeypatch):
     """Persistent prefill: one workgroup per resident slot (8-wave: 1 per CU, 4-wave: 2), a
     multiple of the 8 XCDs, never more than the tiles; the workspace holds the 8 queue counters."""
-    monkeypatch.setenv("TPATTN_PREFILL_PERSIST", "1")
+    monkeypatch.setenv("ATTN_PREFILL_PERSIST", "1")
     p = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
     assert p["block_m"] == 256 and p["grid_x"] == 256
     assert p["workspace_bytes"] >= 8 * 4
@@ -158,7 +158,7 @@ def test_persistent_grid_is_resident_workgroups(monkeypatch):
     p = tpa.plan(1, 2, 2, 300, 300, 128, causal=True, num_cus=256)  # few tiles: all of them, rounded to 8
     tiles = p["grid_heads"] * p["num_m_blocks"] * p["num_splits"]
     assert tiles < 256 and p["grid_x"] == -(-tiles // 8) * 8
-    monkeypatch.setenv("TPATTN_PREFILL_PERSIST", "0")
+    monkeypatch.setenv("ATTN_PREFILL_PERSIST", "0")
     p = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
     assert p["grid_x"] == 1024 and p["workspace_bytes"] == 0
 
@@ -206,7 +206,7 @@ def test_bwd_plan_visits_the_printed_block_count_and_the_forward_pairs():
 
 def test_bwd_plan_atomic_form_needs_the_accumulator(monkeypatch):
     w = WORKLOADS["causal_prefill_bf16"]
-    monkeypatch.setenv("TPATTN_BWD_ATOMIC", "1")
+    monkeypatch.setenv("ATTN_BWD_ATOMIC", "1")
     p = tpa.plan_bwd(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, w.dtype)
     assert p["dq_block_m"] == 0
     assert p["workspace_bytes"] >= w.B * w.Sq * w.Hq * (w.d + 2) * 4

@@ -1,8 +1,8 @@
-"""Python binding of libtpattn.so, the MI355X tiled flash-attention library
+"""Python binding of libattn.so, the MI355X tiled flash-attention library
 (forward pass, split-KV combine, and backward pass).
 
 Argument marshalling only: every step of the computation runs in the HIP
-kernels behind the C-ABI declared in include/tpattn.h. PyTorch provides
+kernels behind the C-ABI declared in include/attn.h. PyTorch provides
 device memory and the current stream. There is no fallback path: if the
 library is not built, or a tensor is not on a GPU, the call raises.
 
@@ -18,19 +18,19 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# TPATTN_LIB may name another build of the same library (same ABI), e.g. one
+# ATTN_LIB may name another build of the same library (same ABI), e.g. one
 # compiled with different flags, to compare two builds in one process tree.
-LIB_PATH = os.environ.get("TPATTN_LIB") or os.path.join(_PKG, "libtpattn.so")
-HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "tpattn.h")
+LIB_PATH = os.environ.get("ATTN_LIB") or os.path.join(_PKG, "libattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
 
 FP32, BF16 = 0, 1
 MAX_SPLITS = 256
 ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EHIP", -4: "ENOMEM"}
 
 
-class TpAttnError(RuntimeError):
+class AttnError(RuntimeError):
     def __init__(self, code: int, msg: str):
-        super().__init__(f"tpattn error {code} ({ERRORS.get(code, '?')}): {msg}")
+        super().__init__(f"attn error {code} ({ERRORS.get(code, '?')}): {msg}")
         self.code = code
 
 
@@ -65,7 +65,7 @@ _lib = None
 
 
 def load():
-    """Load libtpattn.so (raises if it has not been built)."""
+    """Load libattn.so (raises if it has not been built)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -76,50 +76,50 @@ def load():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     ll = ctypes.c_longlong
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.tpattn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
-    lib.tpattn_fwd.restype = i
-    lib.tpattn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp, ll, vp]
-    lib.tpattn_fwd_varlen.restype = i
-    lib.tpattn_plan_fwd.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ll, i, ctypes.POINTER(Plan)]
-    lib.tpattn_plan_fwd.restype = i
-    lib.tpattn_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp]
-    lib.tpattn_fwd_dv.restype = i
-    lib.tpattn_plan_fwd_dv.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
-    lib.tpattn_plan_fwd_dv.restype = i
-    lib.tpattn_workspace_bytes.argtypes = [i, i, i, i, i]
-    lib.tpattn_workspace_bytes.restype = ctypes.c_size_t
-    lib.tpattn_lse_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
-    lib.tpattn_lse_combine.restype = i
-    lib.tpattn_n_block_range.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ip, ip]
-    lib.tpattn_n_block_range.restype = i
-    lib.tpattn_should_pack_gqa.argtypes = [i, i, i, i]
-    lib.tpattn_should_pack_gqa.restype = i
-    lib.tpattn_num_splits_fa3.argtypes = [i, i, i, i, ll, i, i]
-    lib.tpattn_num_splits_fa3.restype = i
-    lib.tpattn_num_splits_occupancy.argtypes = [i, i, i, i, i, i]
-    lib.tpattn_num_splits_occupancy.restype = i
-    lib.tpattn_profile_begin.argtypes = [i]
-    lib.tpattn_profile_begin.restype = i
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp, ll, vp]
+    lib.attn_fwd_varlen.restype = i
+    lib.attn_plan_fwd.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ll, i, ctypes.POINTER(Plan)]
+    lib.attn_plan_fwd.restype = i
+    lib.attn_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd_dv.restype = i
+    lib.attn_plan_fwd_dv.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.attn_plan_fwd_dv.restype = i
+    lib.attn_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_lse_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.attn_lse_combine.restype = i
+    lib.attn_n_block_range.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ip, ip]
+    lib.attn_n_block_range.restype = i
+    lib.attn_should_pack_gqa.argtypes = [i, i, i, i]
+    lib.attn_should_pack_gqa.restype = i
+    lib.attn_num_splits_fa3.argtypes = [i, i, i, i, ll, i, i]
+    lib.attn_num_splits_fa3.restype = i
+    lib.attn_num_splits_occupancy.argtypes = [i, i, i, i, i, i]
+    lib.attn_num_splits_occupancy.restype = i
+    lib.attn_profile_begin.argtypes = [i]
+    lib.attn_profile_begin.restype = i
     dp = ctypes.POINTER(ctypes.c_double)
-    lib.tpattn_profile_end.argtypes = [dp, ip, dp, ip, dp, ip]
-    lib.tpattn_profile_end.restype = i
-    lib.tpattn_profile_end_kinds.argtypes = [dp, ip, i]
-    lib.tpattn_profile_end_kinds.restype = i
-    lib.tpattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
-    lib.tpattn_bwd.restype = i
-    lib.tpattn_plan_bwd.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(BwdPlan)]
-    lib.tpattn_plan_bwd.restype = i
-    lib.tpattn_m_block_range.argtypes = [i, i, i, i, i, i, i, ip, ip]
-    lib.tpattn_m_block_range.restype = i
-    lib.tpattn_last_error.argtypes = []
-    lib.tpattn_last_error.restype = ctypes.c_char_p
+    lib.attn_profile_end.argtypes = [dp, ip, dp, ip, dp, ip]
+    lib.attn_profile_end.restype = i
+    lib.attn_profile_end_kinds.argtypes = [dp, ip, i]
+    lib.attn_profile_end_kinds.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_plan_bwd.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(BwdPlan)]
+    lib.attn_plan_bwd.restype = i
+    lib.attn_m_block_range.argtypes = [i, i, i, i, i, i, i, ip, ip]
+    lib.attn_m_block_range.restype = i
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
 
 def _check(rc: int):
     if rc != 0:
-        raise TpAttnError(rc, load().tpattn_last_error().decode())
+        raise AttnError(rc, load().attn_last_error().decode())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -166,7 +166,7 @@ def fwd(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[fl
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    rc = load().tpattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+    rc = load().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr() if lse is not None else None,
                            B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                            float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
@@ -177,7 +177,7 @@ def fwd(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[fl
 def fwd_dv(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
            num_splits: int = 0, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
-    """Forward with values of their own width (tpattn_fwd_dv): q, k [.., d], v [.., d_v].
+    """Forward with values of their own width (attn_fwd_dv): q, k [.., d], v [.., d_v].
     Returns (o [B, Sq, Hq, d_v], lse)."""
     _check_tensors(q, k, v, same_width=False)
     B, Sq, Hq, d = q.shape
@@ -188,7 +188,7 @@ def fwd_dv(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional
         out = torch.empty((B, Sq, Hq, dv), dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    rc = load().tpattn_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+    rc = load().attn_fwd_dv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr() if lse is not None else None,
                               B, Hq, Hkv, Sq, Sk, d, dv, int(bool(causal)), int(window_left),
                               float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
@@ -213,7 +213,7 @@ def fwd_varlen(q, k, v, seqlens_k: torch.Tensor, causal: bool = False, window_le
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    rc = load().tpattn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+    rc = load().attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   lse.data_ptr() if lse is not None else None,
                                   B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                                   float(scale), int(num_splits), _dtype_code(q),
@@ -225,7 +225,7 @@ def fwd_varlen(q, k, v, seqlens_k: torch.Tensor, causal: bool = False, window_le
 def bwd(q, k, v, o, dout, lse, causal: bool = False, window_left: int = -1,
         scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
         dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None, stream=None):
-    """Attention backward on the GPU (tpattn_bwd). o and lse are the forward's outputs
+    """Attention backward on the GPU (attn_bwd). o and lse are the forward's outputs
     for (q, k, v); dout the gradient of o. Returns (dq, dk, dv) in the dtype of q."""
     _check_tensors(q, k, v)
     B, Sq, Hq, d = q.shape
@@ -246,7 +246,7 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, window_left: int = -1,
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.shape != ref.shape or t.dtype != ref.dtype or not (t.is_cuda and t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous GPU tensor like {name[1:]}")
-    rc = load().tpattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+    rc = load().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                            B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                            float(scale), _dtype_code(q), _stream_ptr(stream))
@@ -258,7 +258,7 @@ def plan_bwd(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, dtype="bf16") 
     """The backward plan (host only)."""
     p = BwdPlan()
     code = FP32 if dtype in ("fp32", FP32, torch.float32) else BF16
-    _check(load().tpattn_plan_bwd(B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+    _check(load().attn_plan_bwd(B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                                   code, ctypes.byref(p)))
     return p.as_dict()
 
@@ -266,7 +266,7 @@ def plan_bwd(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, dtype="bf16") 
 def m_block_range(Sq, Sk, causal, window_left, block_m, block_n, n_block):
     """get_m_block_min_max: query-block range of key block n_block (host mirror)."""
     lo, hi = ctypes.c_int(), ctypes.c_int()
-    _check(load().tpattn_m_block_range(Sq, Sk, int(bool(causal)), window_left, block_m, block_n,
+    _check(load().attn_m_block_range(Sq, Sk, int(bool(causal)), window_left, block_m, block_n,
                                        n_block, ctypes.byref(lo), ctypes.byref(hi)))
     return lo.value, hi.value
 
@@ -282,7 +282,7 @@ def lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
             raise ValueError("tensors must be contiguous GPU tensors")
     if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
         raise ValueError("partials must be fp32")
-    rc = load().tpattn_lse_combine(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(),
+    rc = load().attn_lse_combine(o_part.data_ptr(), lse_part.data_ptr(), out.data_ptr(),
                                    lse.data_ptr() if lse is not None else None,
                                    B, Sq, Hq, d, S, _dtype_code(out), _stream_ptr(stream))
     _check(rc)
@@ -294,7 +294,7 @@ def plan(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, num_splits=0, dtyp
     """The planner's choices for a problem (host only)."""
     p = Plan()
     code = FP32 if dtype in ("fp32", FP32, torch.float32) else BF16
-    rc = load().tpattn_plan_fwd(B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+    rc = load().attn_plan_fwd(B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                                 int(num_splits), code, int(bool(varlen)), int(sum_seqlens_k),
                                 int(num_cus), ctypes.byref(p))
     _check(rc)
@@ -303,22 +303,22 @@ def plan(B, Hq, Hkv, Sq, Sk, d, causal=False, window_left=-1, num_splits=0, dtyp
 
 def plan_dv(B, Hq, Hkv, Sq, Sk, d, d_v, causal=False, window_left=-1, num_splits=0, dtype="bf16",
             num_cus=0) -> dict:
-    """The plan of tpattn_fwd_dv (host only)."""
+    """The plan of attn_fwd_dv (host only)."""
     p = Plan()
     code = FP32 if dtype in ("fp32", FP32, torch.float32) else BF16
-    _check(load().tpattn_plan_fwd_dv(B, Hq, Hkv, Sq, Sk, d, d_v, int(bool(causal)), int(window_left),
+    _check(load().attn_plan_fwd_dv(B, Hq, Hkv, Sq, Sk, d, d_v, int(bool(causal)), int(window_left),
                                      int(num_splits), code, int(num_cus), ctypes.byref(p)))
     return p.as_dict()
 
 
 def workspace_bytes(B, Hq, Sq, d, num_splits) -> int:
-    return int(load().tpattn_workspace_bytes(B, Hq, Sq, d, num_splits))
+    return int(load().attn_workspace_bytes(B, Hq, Sq, d, num_splits))
 
 
 def n_block_range(Sq, Skb, G, pack, causal, window_left, block_m, block_n, m_block,
                   split=0, num_splits=1):
     lo, hi = ctypes.c_int(), ctypes.c_int()
-    rc = load().tpattn_n_block_range(Sq, Skb, G, int(bool(pack)), int(bool(causal)),
+    rc = load().attn_n_block_range(Sq, Skb, G, int(bool(pack)), int(bool(causal)),
                                      window_left, block_m, block_n, m_block, split, num_splits,
                                      ctypes.byref(lo), ctypes.byref(hi))
     _check(rc)
@@ -326,23 +326,23 @@ def n_block_range(Sq, Skb, G, pack, causal, window_left, block_m, block_n, m_blo
 
 
 def should_pack_gqa(varlen, seqlen_q, qhead_per_khead, block_m) -> bool:
-    return bool(load().tpattn_should_pack_gqa(int(bool(varlen)), seqlen_q, qhead_per_khead, block_m))
+    return bool(load().attn_should_pack_gqa(int(bool(varlen)), seqlen_q, qhead_per_khead, block_m))
 
 
 def num_splits_fa3(total_mblocks, num_sms, num_n_blocks, num_m_blocks, size_one_kv_head,
                    is_causal_or_local, max_splits) -> int:
-    return int(load().tpattn_num_splits_fa3(total_mblocks, num_sms, num_n_blocks, num_m_blocks,
+    return int(load().attn_num_splits_fa3(total_mblocks, num_sms, num_n_blocks, num_m_blocks,
                                             size_one_kv_head, int(bool(is_causal_or_local)),
                                             max_splits))
 
 
 def num_splits_occupancy(tiles, num_cus, n_blocks, block_n, min_chunk_rows=256, wg_per_cu=2):
-    return int(load().tpattn_num_splits_occupancy(tiles, num_cus, n_blocks, block_n,
+    return int(load().attn_num_splits_occupancy(tiles, num_cus, n_blocks, block_n,
                                                   min_chunk_rows, wg_per_cu))
 
 
 def profile_begin(max_launches: int = 4096):
-    _check(load().tpattn_profile_begin(int(max_launches)))
+    _check(load().attn_profile_begin(int(max_launches)))
 
 
 KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost", "bwd_dq")
@@ -352,7 +352,7 @@ def profile_end_kinds() -> dict:
     """Summed event time (ms) and launch count of every kernel kind since profile_begin."""
     ms = (ctypes.c_double * len(KINDS))()
     n = (ctypes.c_int * len(KINDS))()
-    _check(load().tpattn_profile_end_kinds(ms, n, len(KINDS)))
+    _check(load().attn_profile_end_kinds(ms, n, len(KINDS)))
     out = {}
     for i, name in enumerate(KINDS):
         out[name + "_ms"] = ms[i]
@@ -363,7 +363,7 @@ def profile_end_kinds() -> dict:
 def profile_end() -> dict:
     f_ms, c_ms, p_ms = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     f_n, c_n, p_n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(load().tpattn_profile_end(ctypes.byref(f_ms), ctypes.byref(f_n), ctypes.byref(c_ms),
+    _check(load().attn_profile_end(ctypes.byref(f_ms), ctypes.byref(f_n), ctypes.byref(c_ms),
                                      ctypes.byref(c_n), ctypes.byref(p_ms), ctypes.byref(p_n)))
     return {"fwd_ms": f_ms.value, "fwd_launches": f_n.value,
             "combine_ms": c_ms.value, "combine_launches": c_n.value,

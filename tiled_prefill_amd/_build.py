@@ -1,4 +1,4 @@
-"""Build libtpattn.so (HIP kernels + C-ABI) for gfx950 with hipcc, in-tree."""
+"""Build libattn.so (HIP kernels + C-ABI) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
 import os
@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-LIB = os.path.join(PKG, "libtpattn.so")
+LIB = os.path.join(PKG, "libattn.so")
 
 SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_prefill.hip", "attn_mla.hip", "attn_bwd.hip",
            "attn_api.cpp"]
@@ -33,7 +33,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into tiled_prefill_amd/libtpattn.so (always rebuilds)."""
+    """Compile every HIP source into tiled_prefill_amd/libattn.so (always rebuilds)."""
     tmp = LIB + ".tmp"
     cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + [
         "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp,

@@ -1,4 +1,4 @@
-// attn_api.cpp -- the C-ABI of libtpattn.so: argument checks, the host planner
+// attn_api.cpp -- the C-ABI of libattn.so: argument checks, the host planner
 // (tile choice, GQA packing, split count, grid), the split workspace, and the
 // launches of the forward and combine kernels.
 //
@@ -19,7 +19,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/tpattn.h"
+#include "../../include/attn.h"
 #include "attn_kernels.h"
 #include "attn_plan.h"
 
@@ -63,7 +63,7 @@ int occupancy_rule(int tiles, int num_cus, int n_blocks, int block_n, int min_ch
     const int min_chunk_blocks = imax(1, ceil_div(min_chunk_rows, block_n));
     const int s_occ = imin(ceil_div(target, tiles), n_blocks);
     const int s_chunk = n_blocks / min_chunk_blocks;
-    return imax(1, imin(TPATTN_MAX_SPLITS, imin(s_occ, s_chunk)));
+    return imax(1, imin(ATTN_MAX_SPLITS, imin(s_occ, s_chunk)));
 }
 
 // The other reading of the same text, as an ablation: reach the workgroup target
@@ -75,7 +75,7 @@ int occupancy_first_rule(int tiles, int num_cus, int n_blocks, int block_n, int 
     const int min_chunk_blocks = imax(1, ceil_div(min_chunk_rows, block_n));
     const int s_occ = imin(ceil_div(target, tiles), n_blocks);
     const int s_chunk = n_blocks / min_chunk_blocks;
-    return imax(1, imin(TPATTN_MAX_SPLITS, imax(s_occ, s_chunk)));
+    return imax(1, imin(ATTN_MAX_SPLITS, imax(s_occ, s_chunk)));
 }
 
 // [FA-tiling] §5.2, as an ablation.
@@ -137,34 +137,34 @@ struct Problem {
 
 int check_problem(const Problem& p) {
     if (p.B < 0 || p.Sq < 0 || p.Sk < 0)
-        return fail(TPATTN_EINVAL, "negative size (B=%d Sq=%d Sk=%d)", p.B, p.Sq, p.Sk);
+        return fail(ATTN_EINVAL, "negative size (B=%d Sq=%d Sk=%d)", p.B, p.Sq, p.Sk);
     if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv != 0)
-        return fail(TPATTN_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", p.Hq, p.Hkv);
-    if (p.dtype != TPATTN_FP32 && p.dtype != TPATTN_BF16)
-        return fail(TPATTN_EUNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p.dtype);
+        return fail(ATTN_EINVAL, "Hq=%d must be a positive multiple of Hkv=%d", p.Hq, p.Hkv);
+    if (p.dtype != ATTN_FP32 && p.dtype != ATTN_BF16)
+        return fail(ATTN_EUNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p.dtype);
     const int dv = p.dv > 0 ? p.dv : p.d;
     if (dv != p.d) {
-        if (!(p.d == 576 && dv == 512 && p.dtype == TPATTN_BF16))
-            return fail(TPATTN_EUNSUPPORTED, "d=%d with d_v=%d is not built (bf16 576/512 only)", p.d, dv);
+        if (!(p.d == 576 && dv == 512 && p.dtype == ATTN_BF16))
+            return fail(ATTN_EUNSUPPORTED, "d=%d with d_v=%d is not built (bf16 576/512 only)", p.d, dv);
     } else if (p.d != 64 && p.d != 128) {
-        return fail(TPATTN_EUNSUPPORTED, "head dim %d is not built (64 or 128)", p.d);
+        return fail(ATTN_EUNSUPPORTED, "head dim %d is not built (64 or 128)", p.d);
     }
-    if (p.window_left < -1) return fail(TPATTN_EINVAL, "window_left=%d < -1", p.window_left);
+    if (p.window_left < -1) return fail(ATTN_EINVAL, "window_left=%d < -1", p.window_left);
     if (!(p.scale > 0.f) || !isfinite(p.scale))
-        return fail(TPATTN_EINVAL, "scale must be finite and > 0");
-    if (p.num_splits > TPATTN_MAX_SPLITS)
-        return fail(TPATTN_EINVAL, "num_splits=%d > %d", p.num_splits, TPATTN_MAX_SPLITS);
-    if (p.B > 65535) return fail(TPATTN_EINVAL, "B=%d exceeds the grid limit 65535", p.B);
+        return fail(ATTN_EINVAL, "scale must be finite and > 0");
+    if (p.num_splits > ATTN_MAX_SPLITS)
+        return fail(ATTN_EINVAL, "num_splits=%d > %d", p.num_splits, ATTN_MAX_SPLITS);
+    if (p.B > 65535) return fail(ATTN_EINVAL, "B=%d exceeds the grid limit 65535", p.B);
     const long long elems = (long long)p.B * p.Sq * p.Hq * p.d;
     const long long kv = (long long)p.B * p.Sk * p.Hkv * p.d;
-    if (elems > (1LL << 40) || kv > (1LL << 40)) return fail(TPATTN_EINVAL, "tensor too large");
+    if (elems > (1LL << 40) || kv > (1LL << 40)) return fail(ATTN_EINVAL, "tensor too large");
     if ((long long)p.Sq * (p.Hq / p.Hkv) > 0x7fffffffLL / 2)
-        return fail(TPATTN_EINVAL, "Sq*G too large");
-    return TPATTN_OK;
+        return fail(ATTN_EINVAL, "Sq*G too large");
+    return ATTN_OK;
 }
 
 struct Plan {
-    tpattn_plan pub;
+    attn_plan_t pub;
     const FwdVariant* var;
     size_t vt_offset = 0;  // byte offset of the V pre-pass output in the workspace
     size_t ctr_offset = 0; // byte offset of the persistent kernels' tile counters
@@ -189,13 +189,13 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                 var = v;
                 break;
             }
-        if (!var) return fail(TPATTN_EUNSUPPORTED, "no kernel for d=%d d_v=%d", p.d, dv);
+        if (!var) return fail(ATTN_EUNSUPPORTED, "no kernel for d=%d d_v=%d", p.d, dv);
     }
-    if (!var && decode && env_int("TPATTN_GENERIC_DECODE", 0) == 0) {
-        const int want_waves = env_int("TPATTN_DECODE_WAVES", 4);  // waves per workgroup (4 or 8)
+    if (!var && decode && env_int("ATTN_GENERIC_DECODE", 0) == 0) {
+        const int want_waves = env_int("ATTN_DECODE_WAVES", 4);  // waves per workgroup (4 or 8)
         // 1: K through LDS in 32-key halves (else the register-K form where no
         // such variant exists); 0: K straight into registers (ablation)
-        const int want_kdma = env_int("TPATTN_DECODE_KDMA", 1) ? 1 : 0;
+        const int want_kdma = env_int("ATTN_DECODE_KDMA", 1) ? 1 : 0;
         for (int pass = 0; pass < 2 && !var; ++pass)
             for (const FwdVariant* v = decode_variants(); v->launch; ++v)
                 if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves &&
@@ -204,18 +204,18 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                     break;
                 }
     }
-    if (!var && !decode && env_int("TPATTN_GENERIC_PREFILL", 0) == 0) {
+    if (!var && !decode && env_int("ATTN_GENERIC_PREFILL", 0) == 0) {
         // Tile rows ([FA-tiling] §2.5: smaller blocks where masking cuts tiles):
         // 256-row workgroups (8 waves) for full and causal masks, 128 rows (4
         // waves) with a sliding window, where a 256-row tile spends ~20% of its
         // work on masked corners for window 1024 (measured 599 vs 698 TFLOP/s).
-        // TPATTN_PREFILL_WAVES overrides (ablation).
-        const int want = env_int("TPATTN_PREFILL_WAVES", p.window_left >= 0 ? 4 : 8);
+        // ATTN_PREFILL_WAVES overrides (ablation).
+        const int want = env_int("ATTN_PREFILL_WAVES", p.window_left >= 0 ? 4 : 8);
         // kernel family: 1 = 32x32x16 MFMA kernel on fp16 V^T (V pre-pass), 0 = 16x16x32
-        const int want_vt = env_int("TPATTN_PREFILL_VT", 0);
+        const int want_vt = env_int("ATTN_PREFILL_VT", 0);
         // 1 = persistent workgroups over per-XCD tile queues
-        const int want_persist = env_int("TPATTN_PREFILL_PERSIST", 0) ? 1 : 0;
-        int skip = env_int("TPATTN_PREFILL_SKIP", 0);  // ablation: take a later match
+        const int want_persist = env_int("ATTN_PREFILL_PERSIST", 0) ? 1 : 0;
+        int skip = env_int("ATTN_PREFILL_SKIP", 0);  // ablation: take a later match
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
             if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && (want_vt ? v->needs_vt == want_vt : v->needs_vt == 0) && (v->persistent > 0) == (want_persist > 0) &&
                 skip-- <= 0) {
@@ -225,10 +225,10 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     }
     // general tile kernel: decode tiles (16 rows) for decode, 32-row tiles when a
     // KV head's query rows (packed) are at most 32, else the widest row tile
-    // (TPATTN_VERIFY_TILE: 0 = widest row tile, 1 = 32-row tile over 2 x 2 waves,
+    // (ATTN_VERIFY_TILE: 0 = widest row tile, 1 = 32-row tile over 2 x 2 waves,
     // 2 = 32-row tile over 2 x 4 waves with 128-key tiles)
     const int head_rows = G > 1 ? p.Sq * G : p.Sq;
-    const int verify_tile = env_int("TPATTN_VERIFY_TILE", 1);
+    const int verify_tile = env_int("ATTN_VERIFY_TILE", 1);
     const int want_bm = decode ? 16 : (head_rows <= 32 && verify_tile ? 32 : 0);
     const int want_wn = want_bm == 32 ? (verify_tile == 2 ? 4 : 2) : 0;
     for (int pass = 0; pass < 2 && !var; ++pass)
@@ -242,13 +242,13 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                 break;
             }
         }
-    if (!var) return fail(TPATTN_EUNSUPPORTED, "no kernel variant for dtype %d d %d", p.dtype, p.d);
+    if (!var) return fail(ATTN_EUNSUPPORTED, "no kernel variant for dtype %d d %d", p.dtype, p.d);
     const int BM = var->block_m, BN = var->block_n;
     bool pack = false;
     if (G > 1) pack = (decode || var->dv) ? true : should_pack(p.varlen != 0, p.Sq, G, BM);
 
-    tpattn_plan& q = out->pub;
-    q = tpattn_plan{};
+    attn_plan_t& q = out->pub;
+    q = attn_plan_t{};
     q.pack_gqa = pack;
     q.block_m = BM;
     q.block_n = BN;
@@ -276,9 +276,9 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
 
     // ---- split count ([llama.cpp] occupancy rule; [FA-tiling] §5 ablation)
     const long long tiles = (long long)p.B * q.grid_heads * q.num_m_blocks;
-    const int min_chunk = env_int("TPATTN_MIN_CHUNK", 256);
-    const int wg_per_cu = imax(1, env_int("TPATTN_WG_PER_CU", 2));
-    const int rule = env_int("TPATTN_SPLIT_RULE", 0);  // 0 occupancy, 1 fa3, 2 blog, 3 occupancy first
+    const int min_chunk = env_int("ATTN_MIN_CHUNK", 256);
+    const int wg_per_cu = imax(1, env_int("ATTN_WG_PER_CU", 2));
+    const int rule = env_int("ATTN_SPLIT_RULE", 0);  // 0 occupancy, 1 fa3, 2 blog, 3 occupancy first
     int S = 1;
     int chunk = 0;
     if (p.num_splits >= 1) {
@@ -286,7 +286,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     } else if (tiles > 0) {
         const int t = (int)(tiles > 0x7fffffff ? 0x7fffffff : tiles);
         if (rule == 1) {
-            const long long kvh = (long long)p.Sk * p.d * 2 * (p.dtype == TPATTN_BF16 ? 2 : 4);
+            const long long kvh = (long long)p.Sk * p.d * 2 * (p.dtype == ATTN_BF16 ? 2 : 4);
             S = fa3_rule(t, num_cus, max_blocks, q.num_m_blocks, kvh,
                          p.causal || p.window_left >= 0, 128);
         } else if (rule == 2) {
@@ -301,10 +301,10 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             const long long sum = p.sum_seqlens_k > 0 ? p.sum_seqlens_k : (long long)p.B * p.Sk;
             const long long blocks = (sum + BN - 1) / BN * q.grid_heads * (long long)q.num_m_blocks;
             const long long target = (long long)wg_per_cu * num_cus;
-            int cb = imax(1, ceil_div(env_int("TPATTN_VARLEN_CHUNK", 512), BN));
+            int cb = imax(1, ceil_div(env_int("ATTN_VARLEN_CHUNK", 512), BN));
             if (blocks / cb < target) cb = (int)imax(1, (int)(blocks / target));
             chunk = cb;
-            S = imax(1, imin(TPATTN_MAX_SPLITS, ceil_div(imax(max_blocks, 1), cb)));
+            S = imax(1, imin(ATTN_MAX_SPLITS, ceil_div(imax(max_blocks, 1), cb)));
             if (S == 1) chunk = 0;
         } else if (var->dv) {
             // The latent kernel holds one workgroup per CU (136 KB of LDS): split as
@@ -312,20 +312,20 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             // partial wave costs more than the splits save: 65,536 keys, 5 query
             // blocks, 51 splits 161 us vs 64 splits 236 us) and every split keeps
             // a minimum chunk of 128 keys.
-            const int mc = imax(1, ceil_div(env_int("TPATTN_MLA_MIN_CHUNK", 128), BN));
+            const int mc = imax(1, ceil_div(env_int("ATTN_MLA_MIN_CHUNK", 128), BN));
             S = imin(imax(1, num_cus / t), imax(1, max_blocks / mc));
         } else {
             S = occupancy_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
         }
     }
-    S = imax(1, imin(S, TPATTN_MAX_SPLITS));
+    S = imax(1, imin(S, ATTN_MAX_SPLITS));
     q.num_splits = S;
     q.chunk_blocks = chunk;
     if (var->grid_1d) {
         // one dimension over every tile (persistent kernels: over the resident
         // workgroups), padded to a multiple of the 8 XCDs
         const long long total = (long long)p.B * q.grid_heads * S * q.num_m_blocks;
-        if (total > 0x7fffffffLL - 8) return fail(TPATTN_EINVAL, "too many tiles");
+        if (total > 0x7fffffffLL - 8) return fail(ATTN_EINVAL, "too many tiles");
         long long launch = total;
         if (var->persistent > 0) launch = std::min<long long>(total, (long long)num_cus * var->persistent);
         q.grid_x = (int)((launch + 7) / 8 * 8);
@@ -335,11 +335,11 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         q.grid_x = q.num_m_blocks;
         q.grid_y = q.grid_heads * S;
         q.grid_z = p.B;
-        if (q.grid_y > 65535) return fail(TPATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
+        if (q.grid_y > 65535) return fail(ATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
     }
     // workspace: split partials, then (kernels that read it) the fp16 V^T of the
     // V pre-pass, 256-byte aligned
-    size_t ws = S > 1 ? tpattn_workspace_bytes(p.B, p.Hq, p.Sq, dv, S) : 0;
+    size_t ws = S > 1 ? attn_workspace_bytes(p.B, p.Hq, p.Sq, dv, S) : 0;
     out->vt_offset = (ws + 255) & ~(size_t)255;
     out->skp = ceil_div(imax(p.Sk, 0), 64) * 64;
     if (var->needs_vt && p.Sk > 0)
@@ -348,7 +348,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     if (var->persistent > 0) ws = out->ctr_offset + 256;  // one tile counter per XCD
     q.workspace_bytes = ws;
     out->var = var;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -363,7 +363,7 @@ Workspace g_ws[64];
 
 // The per-device workspace, at least `bytes` long (caller holds ws.mu).
 int ensure_workspace(Workspace& ws, size_t bytes) {
-    if (ws.bytes >= bytes) return TPATTN_OK;
+    if (ws.bytes >= bytes) return ATTN_OK;
     if (ws.ptr) {
         (void)hipDeviceSynchronize();  // earlier calls may still use the old buffer
         (void)hipFree(ws.ptr);
@@ -373,10 +373,10 @@ int ensure_workspace(Workspace& ws, size_t bytes) {
     hipError_t e = hipMalloc(&ws.ptr, bytes);
     if (e != hipSuccess) {
         ws.ptr = nullptr;
-        return fail(TPATTN_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+        return fail(ATTN_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
     }
     ws.bytes = bytes;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
 
@@ -409,15 +409,15 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
             const int* seqlens_k, void* stream_v) {
     // pointers are checked only where they will be read (empty tensors may be null)
     const bool has_rows = pr.B > 0 && pr.Sq > 0;
-    if (has_rows && (!q || !o)) return fail(TPATTN_EINVAL, "null q or o pointer");
-    if (has_rows && pr.Sk > 0 && (!k || !v)) return fail(TPATTN_EINVAL, "null k or v pointer");
-    if (pr.varlen && pr.B > 0 && !seqlens_k) return fail(TPATTN_EINVAL, "seqlens_k is null");
+    if (has_rows && (!q || !o)) return fail(ATTN_EINVAL, "null q or o pointer");
+    if (has_rows && pr.Sk > 0 && (!k || !v)) return fail(ATTN_EINVAL, "null k or v pointer");
+    if (pr.varlen && pr.B > 0 && !seqlens_k) return fail(ATTN_EINVAL, "seqlens_k is null");
     Plan plan;
     int rc = make_plan(pr, 0, &plan);
     if (rc) return rc;
-    if (!has_rows) return TPATTN_OK;
+    if (!has_rows) return ATTN_OK;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-    const tpattn_plan& pl = plan.pub;
+    const attn_plan_t& pl = plan.pub;
 
     FwdParams fp{};
     fp.q = q;
@@ -444,7 +444,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.lpt = pl.lpt;
     // decode grids: the workgroups of one key range (all grid heads) are
     // dispatched together, so concurrent reads cover whole interleaved KV rows
-    fp.split_major = env_int("TPATTN_SPLIT_MAJOR", plan.var->block_m <= 16 ? 1 : 0);
+    fp.split_major = env_int("ATTN_SPLIT_MAJOR", plan.var->block_m <= 16 ? 1 : 0);
     // decode tiles: block range and split share of fixed-length problems, and the
     // grid-y divisor as a multiply-high
     {
@@ -464,13 +464,13 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         const int slot = prof_start(0, stream);
         hipError_t e = plan.var->launch(fp, grid, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
-        return TPATTN_OK;
+        if (e != hipSuccess) return fail(ATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
+        return ATTN_OK;
     }
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return fail(TPATTN_EHIP, "hipGetDevice failed");
+        return fail(ATTN_EHIP, "hipGetDevice failed");
     Workspace& ws = g_ws[dev];
     std::lock_guard<std::mutex> lk(ws.mu);
     rc = ensure_workspace(ws, pl.workspace_bytes);
@@ -487,7 +487,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         slot = prof_start(2, stream);
         e = launch_v_to_f16t(fp, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "V pre-pass launch: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(ATTN_EHIP, "V pre-pass launch: %s", hipGetErrorString(e));
     }
 
     if (plan.var->persistent > 0) {
@@ -495,14 +495,14 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         slot = prof_start(2, stream);
         e = launch_tile_counters_reset(fp.tile_counters, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "tile counter reset: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(ATTN_EHIP, "tile counter reset: %s", hipGetErrorString(e));
     }
 
     slot = prof_start(0, stream);
     e = plan.var->launch(fp, grid, stream);
     prof_stop(slot, stream);
-    if (e != hipSuccess) return fail(TPATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
-    if (pl.num_splits == 1) return TPATTN_OK;
+    if (e != hipSuccess) return fail(ATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
+    if (pl.num_splits == 1) return ATTN_OK;
 
     CombineParams cp{};
     cp.o_part = fp.o_part;
@@ -514,10 +514,10 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     cp.Sq = pr.Sq;
     cp.Hq = pr.Hq;
     slot = prof_start(1, stream);
-    e = launch_combine(cp, dvv, pr.dtype == TPATTN_BF16, stream);
+    e = launch_combine(cp, dvv, pr.dtype == ATTN_BF16, stream);
     prof_stop(slot, stream);
-    if (e != hipSuccess) return fail(TPATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
-    return TPATTN_OK;
+    if (e != hipSuccess) return fail(ATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
 }
 
 
@@ -525,7 +525,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
 // backward pass ([FA-tiling] §3.4, §4.6)
 // ---------------------------------------------------------------------------
 struct BwdPlan {
-    tpattn_bwd_plan pub;
+    attn_bwd_plan_t pub;
     const BwdVariant* var;
     size_t lse2_offset = 0, dsum_offset = 0;  // byte offsets in the workspace
 };
@@ -533,13 +533,13 @@ struct BwdPlan {
 int make_bwd_plan(const Problem& p, BwdPlan* out) {
     int rc = check_problem(p);
     if (rc) return rc;
-    // key block: 64 keys (16 per wave) unless TPATTN_BWD_BN asks for 128 (bf16);
-    // dQ by a second kernel unless TPATTN_BWD_ATOMIC=1 (fp32 atomics, ablation)
-    const int want_bn = env_int("TPATTN_BWD_BN", 64);
-    const int want_atomic = env_int("TPATTN_BWD_ATOMIC", 0) ? 1 : 0;
-    const int want_dq_rows = env_int("TPATTN_BWD_DQ_ROWS", 0);  // 0: first listed
+    // key block: 64 keys (16 per wave) unless ATTN_BWD_BN asks for 128 (bf16);
+    // dQ by a second kernel unless ATTN_BWD_ATOMIC=1 (fp32 atomics, ablation)
+    const int want_bn = env_int("ATTN_BWD_BN", 64);
+    const int want_atomic = env_int("ATTN_BWD_ATOMIC", 0) ? 1 : 0;
+    const int want_dq_rows = env_int("ATTN_BWD_DQ_ROWS", 0);  // 0: first listed
     // 2: both kernels DMA their tiles; 1: only the dQ kernel; 0: neither
-    const int want_dq_dma = env_int("TPATTN_BWD_DMA", 2);
+    const int want_dq_dma = env_int("ATTN_BWD_DMA", 2);
     const BwdVariant* var = nullptr;
     for (int pass = 0; pass < 2 && !var; ++pass)
         for (const BwdVariant* v = bwd_variants(); v->launch; ++v)
@@ -549,10 +549,10 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
                 var = v;
                 break;
             }
-    if (!var) return fail(TPATTN_EUNSUPPORTED, "no backward kernel for dtype %d d %d", p.dtype, p.d);
+    if (!var) return fail(ATTN_EUNSUPPORTED, "no backward kernel for dtype %d d %d", p.dtype, p.d);
     const int G = p.Hq / p.Hkv;
-    tpattn_bwd_plan& q = out->pub;
-    q = tpattn_bwd_plan{};
+    attn_bwd_plan_t& q = out->pub;
+    q = attn_bwd_plan_t{};
     q.block_m = var->block_m;
     q.block_n = var->block_n;
     q.threads = 256;
@@ -561,7 +561,7 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
     const long long grid = (long long)q.num_n_blocks * p.Hkv * p.B;
     const long long dq_tiles = (long long)ceil_div(imax(p.Sq, 0), imax(1, var->dq_block_m)) * p.Hq * p.B;
     if (grid > 0x7fffffffLL - 8 || dq_tiles > 0x7fffffffLL - 8)
-        return fail(TPATTN_EINVAL, "too many key or query blocks");
+        return fail(ATTN_EINVAL, "too many key or query blocks");
     q.grid_x = (int)grid;
     long long visited = 0;
     for (int n = 0; n < q.num_n_blocks; ++n) {
@@ -577,7 +577,7 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
     out->dsum_offset = (out->lse2_offset + rows * sizeof(float) + 255) & ~(size_t)255;
     q.workspace_bytes = rows ? out->dsum_offset + rows * sizeof(float) : 0;
     out->var = var;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
 int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* o,
@@ -585,12 +585,12 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     const bool has_rows = pr.B > 0 && pr.Sq > 0;
     const bool has_keys = pr.B > 0 && pr.Sk > 0;
     if (has_rows && (!q || !o || !dout || !lse || !dq))
-        return fail(TPATTN_EINVAL, "null q, o, dout, lse or dq pointer");
-    if (has_keys && (!k || !v || !dk || !dv)) return fail(TPATTN_EINVAL, "null k, v, dk or dv pointer");
+        return fail(ATTN_EINVAL, "null q, o, dout, lse or dq pointer");
+    if (has_keys && (!k || !v || !dk || !dv)) return fail(ATTN_EINVAL, "null k, v, dk or dv pointer");
     BwdPlan plan;
     int rc = make_bwd_plan(pr, &plan);
     if (rc) return rc;
-    if (!has_rows && !has_keys) return TPATTN_OK;
+    if (!has_rows && !has_keys) return ATTN_OK;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
 
     BwdParams bp{};
@@ -617,7 +617,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return fail(TPATTN_EHIP, "hipGetDevice failed");
+        return fail(ATTN_EHIP, "hipGetDevice failed");
     Workspace& ws = g_ws[dev];
     std::lock_guard<std::mutex> lk(ws.mu);
     if (plan.pub.workspace_bytes > 0) {
@@ -633,40 +633,40 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
         slot = prof_start(4, stream);
         e = plan.var->launch_pre(bp, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward pre-pass launch: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(ATTN_EHIP, "backward pre-pass launch: %s", hipGetErrorString(e));
     }
     if (has_keys) {
         slot = prof_start(3, stream);
         e = plan.var->launch(bp, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward launch: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(ATTN_EHIP, "backward launch: %s", hipGetErrorString(e));
     }
     if (has_rows && plan.var->atomic_dq) {
         slot = prof_start(4, stream);
         e = plan.var->launch_post(bp, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward post-pass launch: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(ATTN_EHIP, "backward post-pass launch: %s", hipGetErrorString(e));
     } else if (has_rows) {
         slot = prof_start(5, stream);
         e = plan.var->launch_dq(bp, stream);
         prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(TPATTN_EHIP, "backward dQ launch: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(ATTN_EHIP, "backward dQ launch: %s", hipGetErrorString(e));
     }
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
-int tpattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                int Hkv, int Sq, int Sk, int d, int causal, int window_left, float scale,
                int num_splits, int dtype, void* stream) {
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, scale};
     return run_fwd(p, q, k, v, o, lse, nullptr, stream);
 }
 
-int tpattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
                       float scale, int num_splits, int dtype, const int* seqlens_k,
                       long long sum_seqlens_k, void* stream) {
@@ -674,87 +674,87 @@ int tpattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, floa
     return run_fwd(p, q, k, v, o, lse, seqlens_k, stream);
 }
 
-int tpattn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                   int Hkv, int Sq, int Sk, int d, int d_v, int causal, int window_left,
                   float scale, int num_splits, int dtype, void* stream) {
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, scale};
     p.dv = d_v;
-    if (d_v <= 0) return fail(TPATTN_EINVAL, "d_v=%d must be positive", d_v);
+    if (d_v <= 0) return fail(ATTN_EINVAL, "d_v=%d must be positive", d_v);
     return run_fwd(p, q, k, v, o, lse, nullptr, stream);
 }
 
-int tpattn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
-                       int window_left, int num_splits, int dtype, int num_cus, tpattn_plan* out) {
-    if (!out) return fail(TPATTN_EINVAL, "null plan pointer");
-    if (d_v <= 0) return fail(TPATTN_EINVAL, "d_v=%d must be positive", d_v);
+int attn_plan_fwd_dv(int B, int Hq, int Hkv, int Sq, int Sk, int d, int d_v, int causal,
+                       int window_left, int num_splits, int dtype, int num_cus, attn_plan_t* out) {
+    if (!out) return fail(ATTN_EINVAL, "null plan pointer");
+    if (d_v <= 0) return fail(ATTN_EINVAL, "d_v=%d must be positive", d_v);
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, 1.0f};
     p.dv = d_v;
     Plan plan;
     int rc = make_plan(p, num_cus, &plan);
     if (rc) return rc;
     *out = plan.pub;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-int tpattn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+int attn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
                     int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
-                    tpattn_plan* out) {
-    if (!out) return fail(TPATTN_EINVAL, "null plan pointer");
+                    attn_plan_t* out) {
+    if (!out) return fail(ATTN_EINVAL, "null plan pointer");
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, varlen ? 1 : 0,
               sum_seqlens_k, 1.0f};
     Plan plan;
     int rc = make_plan(p, num_cus, &plan);
     if (rc) return rc;
     *out = plan.pub;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-int tpattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
                int Sk, int d, int causal, int window_left, float scale, int dtype, void* stream) {
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, 0, dtype, 0, 0, scale};
     return run_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, stream);
 }
 
-int tpattn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
-                    int dtype, tpattn_bwd_plan* out) {
-    if (!out) return fail(TPATTN_EINVAL, "null plan pointer");
+int attn_plan_bwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    int dtype, attn_bwd_plan_t* out) {
+    if (!out) return fail(ATTN_EINVAL, "null plan pointer");
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, 0, dtype, 0, 0, 1.0f};
     BwdPlan plan;
     int rc = make_bwd_plan(p, &plan);
     if (rc) return rc;
     *out = plan.pub;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-int tpattn_m_block_range(int Sq, int Sk, int causal, int window_left, int block_m, int block_n,
+int attn_m_block_range(int Sq, int Sk, int causal, int window_left, int block_m, int block_n,
                          int n_block, int* m_min, int* m_max) {
-    if (!m_min || !m_max) return fail(TPATTN_EINVAL, "null output pointer");
+    if (!m_min || !m_max) return fail(ATTN_EINVAL, "null output pointer");
     if (Sq < 0 || Sk < 0 || block_m < 1 || block_n < 1 || n_block < 0 || window_left < -1)
-        return fail(TPATTN_EINVAL, "bad block-range arguments");
+        return fail(ATTN_EINVAL, "bad block-range arguments");
     m_block_range(Sq, Sk, causal, window_left, block_m, block_n, n_block, m_min, m_max);
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-size_t tpattn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits) {
+size_t attn_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits) {
     if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0 || num_splits <= 1) return 0;
     const size_t rows = (size_t)B * Hq * Sq;
     return (size_t)num_splits * rows * ((size_t)d + 1) * sizeof(float);
 }
 
-int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B,
+int attn_lse_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B,
                        int Sq, int Hq, int d, int num_splits, int dtype, void* stream_v) {
-    if (!o_part || !lse_part || !o) return fail(TPATTN_EINVAL, "null tensor pointer");
-    if (B < 0 || Sq < 0 || Hq < 1) return fail(TPATTN_EINVAL, "bad shape");
+    if (!o_part || !lse_part || !o) return fail(ATTN_EINVAL, "null tensor pointer");
+    if (B < 0 || Sq < 0 || Hq < 1) return fail(ATTN_EINVAL, "bad shape");
     if (d != 64 && d != 128 && d != 512)
-        return fail(TPATTN_EUNSUPPORTED, "value width %d is not built (64, 128, 512)", d);
-    if (dtype != TPATTN_FP32 && dtype != TPATTN_BF16)
-        return fail(TPATTN_EUNSUPPORTED, "dtype %d", dtype);
-    if (num_splits < 1 || num_splits > TPATTN_MAX_SPLITS)
-        return fail(TPATTN_EINVAL, "num_splits=%d outside [1, 256]", num_splits);
+        return fail(ATTN_EUNSUPPORTED, "value width %d is not built (64, 128, 512)", d);
+    if (dtype != ATTN_FP32 && dtype != ATTN_BF16)
+        return fail(ATTN_EUNSUPPORTED, "dtype %d", dtype);
+    if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS)
+        return fail(ATTN_EINVAL, "num_splits=%d outside [1, 256]", num_splits);
     const long long rows = (long long)B * Sq * Hq;
-    if (rows > 0x7fffffffLL) return fail(TPATTN_EINVAL, "too many rows");
-    if (rows == 0) return TPATTN_OK;
+    if (rows > 0x7fffffffLL) return fail(ATTN_EINVAL, "too many rows");
+    if (rows == 0) return ATTN_OK;
     CombineParams cp{};
     cp.o_part = o_part;
     cp.lse_part = lse_part;
@@ -766,58 +766,58 @@ int tpattn_lse_combine(const float* o_part, const float* lse_part, void* o, floa
     cp.Hq = Hq;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     const int slot = prof_start(1, stream);
-    hipError_t e = launch_combine(cp, d, dtype == TPATTN_BF16, stream);
+    hipError_t e = launch_combine(cp, d, dtype == ATTN_BF16, stream);
     prof_stop(slot, stream);
-    if (e != hipSuccess) return fail(TPATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
-    return TPATTN_OK;
+    if (e != hipSuccess) return fail(ATTN_EHIP, "combine launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
 }
 
-int tpattn_n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
+int attn_n_block_range(int Sq, int Skb, int G, int pack, int causal, int window_left,
                          int block_m, int block_n, int m_block, int split, int num_splits,
                          int* n_min, int* n_max) {
-    if (!n_min || !n_max) return fail(TPATTN_EINVAL, "null output pointer");
+    if (!n_min || !n_max) return fail(ATTN_EINVAL, "null output pointer");
     if (Sq < 1 || Skb < 0 || G < 1 || block_m < 1 || block_n < 1 || m_block < 0 ||
         num_splits < 1 || split < 0 || split >= num_splits || window_left < -1)
-        return fail(TPATTN_EINVAL, "bad block-range arguments");
+        return fail(ATTN_EINVAL, "bad block-range arguments");
     int lo, hi;
     n_block_range(Sq, Skb, G, pack, causal, window_left, block_m, block_n, m_block, &lo, &hi);
     split_range(lo, hi, split, num_splits, n_min, n_max);
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-int tpattn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int block_m) {
+int attn_should_pack_gqa(int varlen, int seqlen_q, int qhead_per_khead, int block_m) {
     if (seqlen_q < 1 || qhead_per_khead < 1 || block_m < 1) return 0;
     return should_pack(varlen != 0, seqlen_q, qhead_per_khead, block_m) ? 1 : 0;
 }
 
-int tpattn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
+int attn_num_splits_fa3(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
                           long long size_one_kv_head, int is_causal_or_local, int max_splits) {
     if (total_mblocks < 1 || num_sms < 1 || max_splits < 1) return 1;
     return fa3_rule(total_mblocks, num_sms, num_n_blocks, num_m_blocks, size_one_kv_head,
                     is_causal_or_local != 0, max_splits);
 }
 
-int tpattn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
+int attn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
                                 int min_chunk_rows, int wg_per_cu) {
     if (tiles < 1 || num_cus < 1 || block_n < 1 || wg_per_cu < 1) return 1;
     return occupancy_rule(tiles, num_cus, n_blocks, block_n, min_chunk_rows, wg_per_cu);
 }
 
-int tpattn_profile_begin(int max_launches) {
-    if (max_launches < 1 || max_launches > (1 << 20)) return fail(TPATTN_EINVAL, "max_launches");
+int attn_profile_begin(int max_launches) {
+    if (max_launches < 1 || max_launches > (1 << 20)) return fail(ATTN_EINVAL, "max_launches");
     std::lock_guard<std::mutex> lk(g_prof.mu);
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
     g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
     g_prof.kind.assign(max_launches, 0);
     for (auto& e : g_prof.ev)
-        if (hipEventCreate(&e) != hipSuccess) return fail(TPATTN_EHIP, "hipEventCreate");
+        if (hipEventCreate(&e) != hipSuccess) return fail(ATTN_EHIP, "hipEventCreate");
     g_prof.max_launches = max_launches;
     g_prof.used = 0;
     g_prof.on = true;
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
+int attn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     double t[6] = {0, 0, 0, 0, 0, 0};
     int n[6] = {0, 0, 0, 0, 0, 0};
@@ -838,14 +838,14 @@ int tpattn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
         if (ms) ms[k] = t[k];
         if (launches) launches[k] = n[k];
     }
-    return TPATTN_OK;
+    return ATTN_OK;
 }
 
-int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
+int attn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
                        int* combine_launches, double* prep_ms, int* prep_launches) {
     double t[3];
     int n[3];
-    int rc = tpattn_profile_end_kinds(t, n, 3);
+    int rc = attn_profile_end_kinds(t, n, 3);
     if (fwd_ms) *fwd_ms = t[0];
     if (fwd_launches) *fwd_launches = n[0];
     if (combine_ms) *combine_ms = t[1];
@@ -855,6 +855,6 @@ int tpattn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
     return rc;
 }
 
-const char* tpattn_last_error(void) { return g_last_error.c_str(); }
+const char* attn_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

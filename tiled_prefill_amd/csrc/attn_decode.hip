@@ -970,7 +970,7 @@ const FwdVariant* decode_variants() {
 // Kernel choice: the split-group kernel parallelises over splits (decode: many
 // splits, few rows); the column kernel over output elements.
 bool combine_by_columns(int rows, int d, int num_splits) {
-    const int env = env_flag("TPATTN_COMBINE_COLS", -1);
+    const int env = env_flag("ATTN_COMBINE_COLS", -1);
     if (env >= 0) return env != 0;
     (void)rows;
     (void)d;
@@ -983,7 +983,7 @@ hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream
     // 512-wide rows (latent values): one workgroup per row (measured on the latent
     // verify shape, 16 splits x 544 rows: the column kernel took 11.1 us; on the
     // 65,536-key prefix, 51 splits x 272 rows: 24 us with either other kernel)
-    if (d == 512 && env_flag("TPATTN_COMBINE_ROWS", 1) != 0) {
+    if (d == 512 && env_flag("ATTN_COMBINE_ROWS", 1) != 0) {
         if (out_bf16) hipLaunchKernelGGL((lse_combine_rows_kernel<true, 512>), dim3(p.rows), dim3(512), 0, stream, p);
         else hipLaunchKernelGGL((lse_combine_rows_kernel<false, 512>), dim3(p.rows), dim3(512), 0, stream, p);
         return hipGetLastError();
@@ -992,8 +992,8 @@ hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream
         const long long n = (long long)p.rows * (d / 4);
         dim3 grid((unsigned)((n + 255) / 256)), block(256);
         // every partial of a thread in flight at once for up to 8 / 16 splits
-        // (TPATTN_COMBINE_SMALL=0: the looped form for any count)
-        const int small = env_flag("TPATTN_COMBINE_SMALL", 1);
+        // (ATTN_COMBINE_SMALL=0: the looped form for any count)
+        const int small = env_flag("ATTN_COMBINE_SMALL", 1);
         if (small && p.num_splits <= 8) {
             if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_small_kernel<true, 8>), grid, block, 0, stream, p, d);
             else hipLaunchKernelGGL((lse_combine_cols_small_kernel<false, 8>), grid, block, 0, stream, p, d);

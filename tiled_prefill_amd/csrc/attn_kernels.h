@@ -1,5 +1,5 @@
 // attn_kernels.h -- launchers of the gfx950 attention kernels (internal to the
-// library; the public C-ABI is include/tpattn.h).
+// library; the public C-ABI is include/attn.h).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -114,7 +114,7 @@ def small_case(seed: int, dtype: str, B: int, Hq: int, Hkv: int, Sq: int, Sk: in
     return q, k, v
 
 
-# Latent-attention verify workloads (tpattn_fwd_dv; keys 576 wide, values 512, one
+# Latent-attention verify workloads (attn_fwd_dv; keys 576 wide, values 512, one
 # KV head shared by Hq query heads, causal over the last Sq positions):
 # name -> (B, Hq, Sq, Sk). The first is the verify parity shape printed on the
 # occupancy blog page; the second its long-prefix case (the 65k prefix for which
