@@ -37,13 +37,21 @@
  *     key splits (splits beyond the key blocks are empty and legal).
  *   stream: a hipStream_t, or NULL for the default stream. Calls are
  *     asynchronous on the stream and never synchronise the device, except
- *     that growing the internal split workspace synchronises once.
+ *     that growing the library's own workspace synchronises once.
  *   Ownership: all tensors belong to the caller; the library never frees
  *     them. Split partials (and the backward's dQ accumulator and row sums) go
- *     to a library-owned device workspace (one per device, grown on demand,
- *     released at unload). Host threads are serialised on it by a lock, so the
- *     library is thread-safe; on the GPU, calls on one device that use it must
- *     not overlap (issue them on one stream, or order the streams).
+ *     to a caller-owned workspace bound with attn_set_workspace, or else to a
+ *     library-owned device buffer (one per device, grown on demand, released
+ *     at unload). Host threads are serialised on the library's buffer by a
+ *     lock, so the library is thread-safe; on the GPU, calls on one device
+ *     that use it must not overlap (issue them on one stream, or order the
+ *     streams, or bind one workspace per stream).
+ *   Numerics: scores scale * q.k must be finite in fp32 (fp32 accumulation).
+ *     Every finite bf16 value of v is handled: the bf16 prefill and latent
+ *     kernels compute P.V on fp16 operands (P and V rounded to fp16) and, when
+ *     a V element lies beyond fp16's range (|v| > 65504), run that tile again
+ *     with bf16 V and P as two bf16 parts. Non-finite inputs give unspecified
+ *     (non-finite) outputs.
  *   Errors: a negative status code; nothing is launched and the message is
  *     available from attn_last_error() (thread-local). Argument checks never
  *     touch the GPU.
@@ -219,18 +227,45 @@ int attn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
                                 int min_chunk_rows, int wg_per_cu);
 
 /* Kernel timing for measurement tools: while enabled, every launch of the
- * forward kernel, the combine kernel and the V pre-pass (bf16 prefill kernels
- * that read V as fp16 V^T) is bracketed by HIP events on its stream.
+ * forward kernel, the combine kernel and the persistent kernels' counter reset
+ * is bracketed by HIP events on its stream.
  * attn_profile_end synchronises those events and returns the summed
  * durations (ms) and launch counts per kind (any output pointer may be null),
  * then disables recording. */
 int attn_profile_begin(int max_launches);
 int attn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
                        int* combine_launches, double* prep_ms, int* prep_launches);
-/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 6) with
- * kinds 0 forward, 1 combine, 2 V pre-pass / counter reset, 3 backward
- * key-block kernel, 4 backward pre- and post-passes, 5 backward dQ kernel. */
+/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 7) with
+ * kinds 0 forward, 1 combine, 2 tile counter reset, 3 backward
+ * key-block kernel, 4 backward pre- and post-passes, 5 backward dQ kernel,
+ * 6 the bf16 fix-up pass of the prefill kernel (tiles whose V overflowed fp16). */
 int attn_profile_end_kinds(double* ms, int* launches, int n_kinds);
+
+/* Caller-owned scratch ([Occupancy], "The Fix": the split partials live in a
+ * global scratch buffer). Binds dev_ptr[0, bytes) -- device memory of the
+ * device the calls run on, 256-byte aligned -- to the calling host thread:
+ * later calls from this thread put their split partials, per-tile flags, the
+ * backward's row sums and tile counters there, and never allocate or
+ * synchronise. A call that needs more than `bytes` (the workspace_bytes of its
+ * plan: attn_plan_fwd, attn_plan_fwd_dv, attn_plan_bwd) returns ATTN_EINVAL
+ * and launches nothing. dev_ptr NULL or bytes 0 unbinds (back to the
+ * library's own buffer). The memory stays the caller's: keep it alive while
+ * calls that use it may run, and do not give one workspace to calls that can
+ * overlap on the GPU (two streams need two workspaces; then they may run
+ * concurrently). Its contents need no initialisation. Errors: ATTN_EINVAL for
+ * a misaligned pointer. */
+int attn_set_workspace(void* dev_ptr, size_t bytes);
+
+/* Process-wide planner switches, for tools and tests (defaults are the measured
+ * best; other values select ablations). name is the switch's environment
+ * variable, with or without its ATTN_ prefix, e.g. "ATTN_PREFILL_WAVES" or
+ * "SPLIT_RULE"; each is read from the environment once, at the first call, and
+ * afterwards changes only through attn_set_option. Not synchronised with calls
+ * running on other host threads: set switches before issuing such calls.
+ * ATTN_TRACE=1 prints every forward call's plan to stderr. Unknown names give
+ * ATTN_EINVAL. */
+int attn_set_option(const char* name, int value);
+int attn_get_option(const char* name, int* value);
 
 /* Message of the last failure on this thread ("" if none). */
 const char* attn_last_error(void);

@@ -18,8 +18,12 @@ Parity status of each oracle function (what pins it, in tests/test_oracle.py):
   lse_combine_ref   pinned: closed forms (equal lse, single split, all empty)
                     and the partition identity above.
   needed_block_range
-                    pinned: the printed causal block count (528 of 1024) and
-                    the closed-form count of a window.
+                    pinned: the printed causal block count (528 of 1024); with a
+                    left window, a count derived by hand for square blocks
+                    (min(m, ceil(wl / B)) + 1 key blocks per query block m) and
+                    the per-block ranges it implies; with GQA packing, the hull
+                    of the one-row-per-block ranges of the packed rows'
+                    positions.
   attn_bwd_ref      pinned: central finite differences of attn_ref (tiny
                     shapes with causal, window, GQA and fully masked rows), a
                     library routine (torch fp64 autograd through an explicitly

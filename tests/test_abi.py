@@ -18,8 +18,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("attn_fwd", "attn_fwd_varlen", "attn_plan_fwd",
-                     "attn_workspace_bytes", "attn_lse_combine", "attn_last_error"):
+    for required in ("attn_fwd", "attn_fwd_varlen", "attn_plan_fwd", "attn_workspace_bytes",
+                     "attn_set_workspace", "attn_lse_combine", "attn_last_error",
+                     "attn_set_option", "attn_get_option"):
         assert required in names
 
 
@@ -135,3 +136,42 @@ def test_host_block_range_mirrors_reject_bad_arguments():
     with pytest.raises(tpa.AttnError):
         tpa.plan_bwd(1, 6, 4, 8, 8, 64)
     assert tpa.m_block_range(0, 8, True, -1, 64, 64, 0)[1] == 0   # no query rows: empty
+
+
+def test_caller_workspace_errors_launch_nothing():
+    """A bound workspace that is too small (or misaligned) is refused before any GPU
+    call: the decode problem below needs split partials."""
+    lib = tpa.load()
+    assert lib.attn_set_workspace(ctypes.c_void_p(FAKE + 8), 1 << 20) == -1  # not 256-byte aligned
+    need = tpa.plan(1, 32, 4, 1, 32768, 128, num_cus=256)["workspace_bytes"]
+    assert need > 0
+    assert lib.attn_set_workspace(ctypes.c_void_p(FAKE), need - 1) == 0
+    try:
+        rc = lib.attn_fwd(FAKE, FAKE, FAKE, FAKE, None, 1, 32, 4, 1, 32768, 128, 0, -1, 0.088,
+                          0, tpa.BF16, None)
+        assert rc == -1
+        assert "workspace" in lib.attn_last_error().decode()
+        bneed = tpa.plan_bwd(1, 4, 2, 64, 64, 64, causal=True)["workspace_bytes"]
+        assert lib.attn_set_workspace(ctypes.c_void_p(FAKE), bneed - 1) == 0
+        rc = lib.attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 64, 64,
+                          64, 1, -1, 0.125, tpa.BF16, None)
+        assert rc == -1 and "workspace" in lib.attn_last_error().decode()
+    finally:
+        assert lib.attn_set_workspace(None, 0) == 0
+
+
+def test_options_round_trip_and_reject_unknown_names(attn_options):
+    assert tpa.get_option("ATTN_SPLIT_RULE") == tpa.get_option("SPLIT_RULE")
+    attn_options("SPLIT_RULE", 3)
+    assert tpa.get_option("ATTN_SPLIT_RULE") == 3
+    with pytest.raises(tpa.AttnError):
+        tpa.set_option("NO_SUCH_SWITCH", 1)
+    with pytest.raises(tpa.AttnError):
+        tpa.get_option("NO_SUCH_SWITCH")
+
+
+def test_options_change_the_plan(attn_options):
+    base = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
+    attn_options("PREFILL_WAVES", 4)
+    assert tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)["block_m"] == 128
+    assert base["block_m"] == 256

@@ -97,10 +97,10 @@ def test_bwd_small_shapes(case):
     {"ATTN_BWD_ATOMIC": "1"},                            # dQ by fp32 atomics
     {"ATTN_BWD_ATOMIC": "1", "ATTN_BWD_BN": "128"},
 ])
-def test_bwd_variants(env, monkeypatch):
+def test_bwd_variants(env, attn_options):
     # the selectable variants (ablations) on ragged, masked, GQA shapes
     for k, v in env.items():
-        monkeypatch.setenv(k, v)
+        attn_options(k, v)
     print(f"bwd variant {env}", flush=True)
     bwd_case("bf16", 1, 4, 2, 190, 333, 128, True, -1, seed=6)
     bwd_case("bf16", 1, 4, 2, 190, 333, 64, True, 70, seed=6)

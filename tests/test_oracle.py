@@ -191,6 +191,53 @@ def test_printed_causal_block_count():
     assert round(100.0 * computed / g["blocks_total"], 1) == g["fraction_percent"]
 
 
+def _window_block_pairs(N, B, wl):
+    """(query block, key block) pairs a causal sliding window needs, counted by hand for
+    Sq = Sk = N and square B x B blocks: query block m holds rows mB .. mB + B - 1, whose
+    keys run from max(0, mB - wl) to the diagonal, so it needs key blocks
+    max(0, m - ceil(wl / B)) .. m, i.e. min(m, c) + 1 of them with c = ceil(wl / B).
+    Summed over the M = N / B query blocks: (c + 1)(c + 2) / 2 + (M - 1 - c)(c + 1) when
+    c < M, else the causal M (M + 1) / 2."""
+    M = N // B
+    c = -(-wl // B)
+    if c >= M:
+        return M * (M + 1) // 2
+    return (c + 1) * (c + 2) // 2 + (M - 1 - c) * (c + 1)
+
+
+@pytest.mark.parametrize("wl,expected", [(1024, 252), (1000, 252), (1025, 275), (0, 32),
+                                         (127, 63), (128, 63), (4095, 528), (100000, 528)])
+def test_window_block_count_closed_form(wl, expected):
+    # the causal example of "分块策略与调度" §3.3 (N = 4096, 128 x 128 blocks) with a
+    # left window: the brute-force ranges of needed_block_range against the count above
+    assert _window_block_pairs(4096, 128, wl) == expected
+    rng = oracle.needed_block_range(4096, 4096, True, wl, 128, 128)
+    assert sum(hi - lo for lo, hi in rng) == expected
+    # every block's range by the same reasoning: [max(0, m - c), m + 1)
+    c = -(-wl // 128)
+    assert rng == [(max(0, m - c), m + 1) for m in range(32)]
+
+
+@pytest.mark.parametrize("Sq,Skb,causal,wl,BM,BN,G", [
+    (5, 9, True, -1, 4, 3, 3), (7, 7, True, 2, 8, 4, 4), (3, 20, False, 5, 5, 4, 2),
+    (9, 5, True, -1, 16, 2, 8), (6, 13, True, 0, 3, 5, 3), (4, 4, False, -1, 2, 2, 5),
+    (11, 17, True, 6, 7, 3, 2), (1, 30, True, 4, 16, 8, 8)])
+def test_packed_block_range_is_the_hull_of_its_positions(Sq, Skb, causal, wl, BM, BN, G):
+    # "分块策略与调度" §6.3: packed row r is query position r // G, so a packed block of
+    # rows [r0, r1) needs the union (hull) of the key-block ranges of positions
+    # r0 // G .. (r1 - 1) // G, each taken from the unpacked ranges with one row per block
+    packed = oracle.needed_block_range(Sq, Skb, causal, wl, BM, BN, G=G, pack=True)
+    per_pos = oracle.needed_block_range(Sq, Skb, causal, wl, 1, BN)
+    assert len(packed) == -(-(Sq * G) // BM)
+    for m, got in enumerate(packed):
+        p0, p1 = (m * BM) // G, (min((m + 1) * BM, Sq * G) - 1) // G
+        rs = [per_pos[p] for p in range(p0, p1 + 1) if per_pos[p] is not None]
+        want = (min(r[0] for r in rs), max(r[1] for r in rs)) if rs else None
+        assert got == want, (m, got, want)
+    assert oracle.needed_block_range(Sq, Skb, causal, wl, BM, BN, G=1, pack=True) == \
+        oracle.needed_block_range(Sq, Skb, causal, wl, BM, BN)
+
+
 def test_varlen_equals_truncated_fixed_length():
     q, k, v = small_case(8, "fp32", 3, 4, 2, 3, 20, 16)
     seqlens = [20, 5, 11]

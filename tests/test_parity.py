@@ -94,9 +94,9 @@ def test_verify_page_shapes_fp32(B, H, q_len, kv_len):
 @pytest.mark.parametrize("case", [(2, 16, 16, 17, 2065, 128, True, -1, 0), (1, 8, 2, 9, 521, 128, True, -1, 3),
                                   (2, 4, 4, 20, 300, 64, False, -1, 0), (1, 4, 1, 5, 77, 128, True, 2, 2),
                                   (1, 2, 2, 32, 129, 64, True, 40, 1)])
-def test_verify_tile_choices_fp32(tile, case, monkeypatch):
+def test_verify_tile_choices_fp32(tile, case, attn_options):
     # the other tiles the planner can pick for <= 32 query rows per KV head
-    monkeypatch.setenv("ATTN_VERIFY_TILE", tile)
+    attn_options("ATTN_VERIFY_TILE", tile)
     run_case("fp32", *case, seed=4)
 
 
@@ -197,17 +197,17 @@ def test_non_default_stream():
                                        (64, 128, "fp32"), (256, 64, "fp32"), (128, 128, "bf16"),
                                        (7, 512, "bf16"), (51, 512, "bf16"), (256, 512, "fp32"),
                                        (1, 512, "fp32")])
-def test_combine_kernel_parity(S, d, dtype, cols, monkeypatch):
+def test_combine_kernel_parity(S, d, dtype, cols, attn_options):
     # four kernels: split groups; columns, with every partial of a thread in flight
     # at once (up to 16 splits) or looped; (512-wide rows only) one workgroup per row
     if cols == "rows":
         if d != 512:
             pytest.skip("the row-parallel combine serves 512-wide rows")
-        monkeypatch.setenv("ATTN_COMBINE_ROWS", "1")
+        attn_options("ATTN_COMBINE_ROWS", "1")
     else:
-        monkeypatch.setenv("ATTN_COMBINE_ROWS", "0")
-        monkeypatch.setenv("ATTN_COMBINE_COLS", cols[0])
-        monkeypatch.setenv("ATTN_COMBINE_SMALL", "0" if cols == "1l" else "1")
+        attn_options("ATTN_COMBINE_ROWS", "0")
+        attn_options("ATTN_COMBINE_COLS", cols[0])
+        attn_options("ATTN_COMBINE_SMALL", "0" if cols == "1l" else "1")
     B, Sq, Hq = 2, 3, 5
     rows = B * Sq * Hq
     o_part, lse_part = random_partials(10 + S, S, rows, d, p_empty=0.3)
@@ -323,14 +323,10 @@ def test_prefill_full_sampled(name):
 # ---------------------------------------------------------------------------
 ABLATIONS = [
     {"ATTN_PREFILL_SKIP": "1"},             # prefill with raised wave priority
-    {"ATTN_PREFILL_SKIP": "2"},             # software-pipelined prefill
     {"ATTN_PREFILL_WAVES": "4"},            # 128-row tiles (default with a window)
     {"ATTN_PREFILL_WAVES": "8"},            # 256-row tiles (default without one)
     {"ATTN_PREFILL_PERSIST": "1"},          # persistent workgroups, per-XCD tile queues
     {"ATTN_PREFILL_PERSIST": "1", "ATTN_PREFILL_WAVES": "8"},
-    {"ATTN_PREFILL_VT": "16"},              # 32x32 MFMA kernel on fp16 V^T
-    {"ATTN_PREFILL_VT": "16", "ATTN_PREFILL_WAVES": "8"},
-    {"ATTN_PREFILL_VT": "16", "ATTN_PREFILL_WAVES": "4"},
     {"ATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
     {"ATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
     {"ATTN_DECODE_WAVES": "8"},             # 8-wave decode workgroups
@@ -354,9 +350,9 @@ def test_decode_forced_split_counts(S):
 
 
 @pytest.mark.parametrize("env", ABLATIONS, ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
-def test_ablation_paths(env, monkeypatch):
+def test_ablation_paths(env, attn_options):
     for k_, v_ in env.items():
-        monkeypatch.setenv(k_, v_)
+        attn_options(k_, v_)
     for case in [("bf16", 1, 8, 2, 300, 300, 128, True, 40, 0), ("bf16", 2, 16, 2, 200, 333, 64, True, -1, 0),
                  ("bf16", 1, 32, 4, 1, 3000, 128, False, -1, 0), ("bf16", 1, 4, 4, 130, 520, 128, False, -1, 0)]:
         run_case(*case, seed=12)
@@ -413,3 +409,178 @@ def test_latent_long_prefix_sampled():
         kl = i + Sk - Sq + 1  # causal, bottom-right: row i sees keys [0, kl)
         ro, rl = oracle.attn_ref(q[:, i:i + 1], k[:, :kl], v[:, :kl], False, -1, scale)
         assert_parity(o[:, i:i + 1], lse[:, :, i:i + 1], ro, rl, "bf16", f"latent long row {i}")
+
+
+# ---------------------------------------------------------------------------
+# V beyond fp16's range: legal bf16 values the fp16 P.V operands cannot hold
+# ---------------------------------------------------------------------------
+BIG = 2.0 ** 17  # a power of two: scaled bf16 values stay exact
+
+
+def _assert_scaled_parity(o, lse, q, k, v, causal, wl, scale, what, dv_path=False):
+    """Tolerance in units of the row's value magnitude: the stated bars (max-abs 2e-2;
+    max-rel 1e-2 where |ref| > 0.1) applied to o / m, m = max(1, sum_j P_ij |v_j|) per
+    element, where the oracle gives sum_j P_ij |v_j| as attention over |v|. For inputs of
+    unit scale m = 1 and this is the ordinary check; attention is linear in V, so
+    scaling rows of V by 2^17 scales their share of each output by the same factor."""
+    ro, rl = oracle.attn_ref(q, k, v, causal, wl, scale)
+    mag, _ = oracle.attn_ref(q, k, v.abs(), causal, wl, scale)
+    m = np.maximum(1.0, mag)
+    of = o.detach().float().cpu().double().numpy()
+    assert np.isfinite(of).all(), f"{what}: non-finite output"
+    err = np.abs(of - ro) / m
+    assert err.max() <= 2e-2, f"{what}: max scaled abs {err.max()}"
+    big = np.abs(ro) / m > 0.1
+    if big.any():
+        rel = (np.abs(of - ro)[big] / np.abs(ro[big])).max()
+        assert rel <= 1e-2, f"{what}: max rel {rel}"
+    lse = lse.detach().cpu().double().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse), fin)
+    if fin.any():
+        d = np.abs(lse[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))
+        assert d.max() <= 1e-3, f"{what}: lse err {d.max()}"
+
+
+@pytest.mark.parametrize("rows,causal,wl,d,Hkv", [
+    ("all", True, -1, 128, 4),       # every tile overflows: the bf16 form runs them all
+    ("tail", True, -1, 128, 4),      # only tiles that see the last keys overflow
+    ("tail", True, 300, 128, 2),     # sliding window: the scaled keys leave most windows
+    ("some", False, -1, 128, 4),     # scattered rows, dense mask
+    ("some", True, -1, 64, 4),
+    ("tail", True, 200, 64, 1),
+])
+def test_prefill_values_beyond_fp16_range(rows, causal, wl, d, Hkv):
+    B, Hq, S = 1, 4, 1100
+    q, k, v = small_case(21, "bf16", B, Hq, Hkv, S, S, d)
+    vf = v.float()
+    if rows == "all":
+        vf = vf * BIG
+    elif rows == "tail":
+        vf[:, 1000:1040] *= BIG
+    else:
+        vf[:, 3::97] *= BIG
+    v = vf.to(torch.bfloat16)
+    assert v.float().abs().max().item() > 65504.0
+    scale = 1.0 / math.sqrt(d)
+    print(f"V beyond fp16 rows={rows} causal={causal} wl={wl} d={d} Hkv={Hkv}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window_left=wl, scale=scale)
+    torch.cuda.synchronize()
+    _assert_scaled_parity(o, lse, q, k, v, causal, wl, scale, f"prefill rows={rows}")
+    if rows == "all":
+        # linearity: O(V * 2^17) / 2^17 is O(V), at the ordinary tolerance
+        ro, rl = oracle.attn_ref(q, k, (v.float() / BIG).to(torch.bfloat16), causal, wl, scale)
+        assert_parity((o.float() / BIG), lse, ro, rl, "bf16", "prefill all rows / 2^17")
+
+
+@pytest.mark.parametrize("env", [{"PREFILL_WAVES": 4}, {"PREFILL_WAVES": 8},
+                                 {"PREFILL_PERSIST": 1}, {"PREFILL_SKIP": 1}],
+                         ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
+def test_prefill_values_beyond_fp16_range_every_variant(env, attn_options):
+    for k_, v_ in env.items():
+        attn_options(k_, v_)
+    q, k, v = small_case(22, "bf16", 2, 8, 2, 700, 900, 128)
+    vf = v.float()
+    vf[:, 850:870] *= BIG
+    v = vf.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    print(f"V beyond fp16, variant {env}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _assert_scaled_parity(o, lse, q, k, v, True, -1, scale, f"variant {env}")
+
+
+def test_decode_and_verify_values_beyond_fp16_range():
+    # decode tiles keep V in bf16; the split combine sees large partials
+    q, k, v = small_case(23, "bf16", 1, 32, 4, 1, 5000, 128)
+    vf = v.float()
+    vf[:, 4000:4100] *= BIG
+    v = vf.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    print("decode V beyond fp16", flush=True)
+    for S in (0, 1, 7):
+        o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, num_splits=S)
+        torch.cuda.synchronize()
+        _assert_scaled_parity(o, lse, q, k, v, False, -1, scale, f"decode S={S}")
+
+
+@pytest.mark.parametrize("rows", ["all", "tail"])
+def test_latent_values_beyond_fp16_range(rows):
+    B, Hq, Sq, Sk = 2, 16, 17, 2065
+    q, k, v = latent_case(5, B, Hq, Sq, Sk)
+    vf = v.float()
+    if rows == "all":
+        vf = vf * BIG
+    else:
+        vf[:, 2000:2030] *= BIG
+    v = vf.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(576)
+    print(f"latent V beyond fp16 rows={rows}", flush=True)
+    o, lse = tpa.fwd_dv(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _assert_scaled_parity(o, lse, q, k, v, True, -1, scale, f"latent rows={rows}")
+
+
+# ---------------------------------------------------------------------------
+# caller-owned workspaces (attn_set_workspace)
+# ---------------------------------------------------------------------------
+def test_caller_workspaces_on_two_streams():
+    """Two decode problems on two streams, each with its own workspace bound at its
+    launch, run concurrently; both match the oracle, twice in a row."""
+    cases = [(small_case(31, "bf16", 1, 32, 4, 1, 20000, 128), 0),
+             (small_case(32, "bf16", 2, 16, 2, 1, 9000, 64), 5)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs, outs, refs = [], [], []
+    for (q, k, v), S in cases:
+        B, Sq, Hq, d = q.shape
+        need = tpa.plan(B, Hq, k.shape[2], Sq, k.shape[1], d, num_splits=S)["workspace_bytes"]
+        assert need > 0
+        bufs.append(torch.empty(need, dtype=torch.uint8, device=DEV))
+        refs.append(oracle.attn_ref(q, k, v, False, -1, 1.0 / math.sqrt(d)))
+    dev_in = [tuple(t.to(DEV) for t in qkv) for qkv, _ in cases]
+    torch.cuda.synchronize()
+    print("two streams, two workspaces", flush=True)
+    try:
+        for _ in range(2):
+            outs = []
+            for (q, k, v), (_, S), buf, st in zip(dev_in, cases, bufs, streams):
+                tpa.set_workspace(buf)
+                outs.append(tpa.fwd(q, k, v, num_splits=S, stream=st))
+            torch.cuda.synchronize()
+            for (o, lse), (ro, rl) in zip(outs, refs):
+                assert_parity(o, lse, ro, rl, "bf16", "caller workspace")
+        # a workspace one byte too small is refused
+        q, k, v = dev_in[0]
+        tpa.set_workspace(bufs[0][: bufs[0].numel() - 256])
+        with pytest.raises(tpa.AttnError):
+            tpa.fwd(q, k, v)
+    finally:
+        tpa.set_workspace(None)
+
+
+# ---------------------------------------------------------------------------
+# the persistent scheduler with several tiles per resident workgroup
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,Hq,Hkv,S,wl", [(4, 32, 32, 2048, -1), (4, 32, 8, 2048, 512)])
+def test_persistent_several_tiles_per_workgroup(B, Hq, Hkv, S, wl, attn_options):
+    q, k, v = small_case(41, "bf16", B, Hq, Hkv, S, S, 128)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_ref, lse_ref = tpa.fwd(qd, kd, vd, causal=True, window_left=wl)
+    attn_options("PREFILL_PERSIST", 1)
+    p = tpa.plan(B, Hq, Hkv, S, S, 128, causal=True, window_left=wl)
+    tiles = B * p["grid_heads"] * p["num_m_blocks"] * p["num_splits"]
+    assert tiles >= 2 * p["grid_x"], (tiles, p["grid_x"])  # several tiles per workgroup
+    print(f"persistent B={B} Hq={Hq} Hkv={Hkv} S={S} wl={wl}: {tiles} tiles on {p['grid_x']} "
+          "workgroups", flush=True)
+    for _ in range(2):  # the queue counters are reset before every launch
+        o, lse = tpa.fwd(qd, kd, vd, causal=True, window_left=wl)
+        torch.cuda.synchronize()
+        # the same per-tile arithmetic as the one-tile-per-workgroup grid: same bits
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    o, lse = o.cpu(), lse.cpu()
+    scale = 1.0 / math.sqrt(128)
+    for b, i in [(0, 0), (1, 255), (2, 256), (3, 1023), (3, S - 1), (0, S // 2 + 3)]:
+        ro, rl = oracle.attn_ref(q[b:b + 1, i:i + 1], k[b:b + 1, :i + 1], v[b:b + 1, :i + 1],
+                                 True, wl, scale)
+        assert_parity(o[b:b + 1, i:i + 1], lse[b:b + 1, :, i:i + 1], ro, rl, "bf16",
+                      f"persistent row {b},{i}")

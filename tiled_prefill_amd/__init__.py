@@ -111,6 +111,12 @@ def load():
     lib.attn_plan_bwd.restype = i
     lib.attn_m_block_range.argtypes = [i, i, i, i, i, i, i, ip, ip]
     lib.attn_m_block_range.restype = i
+    lib.attn_set_workspace.argtypes = [vp, ctypes.c_size_t]
+    lib.attn_set_workspace.restype = i
+    lib.attn_set_option.argtypes = [ctypes.c_char_p, i]
+    lib.attn_set_option.restype = i
+    lib.attn_get_option.argtypes = [ctypes.c_char_p, ip]
+    lib.attn_get_option.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -341,11 +347,53 @@ def num_splits_occupancy(tiles, num_cus, n_blocks, block_n, min_chunk_rows=256, 
                                                   min_chunk_rows, wg_per_cu))
 
 
+def set_workspace(buf: Optional[torch.Tensor]):
+    """Bind a caller-owned GPU workspace (any dtype, 256-byte aligned) to this host
+    thread (attn_set_workspace); None unbinds. The caller keeps `buf` alive while
+    calls that use it may run."""
+    if buf is None:
+        _check(load().attn_set_workspace(None, 0))
+        return
+    if not (isinstance(buf, torch.Tensor) and buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("the workspace must be a contiguous GPU tensor")
+    _check(load().attn_set_workspace(buf.data_ptr(), buf.numel() * buf.element_size()))
+
+
+def set_option(name: str, value: int):
+    """Set a process-wide planner switch (attn_set_option), e.g. "PREFILL_WAVES"."""
+    _check(load().attn_set_option(name.encode(), int(value)))
+
+
+def get_option(name: str) -> int:
+    out = ctypes.c_int()
+    _check(load().attn_get_option(name.encode(), ctypes.byref(out)))
+    return out.value
+
+
+class options:
+    """Context manager: set switches for a block, restore them afterwards."""
+
+    def __init__(self, **kw):
+        self.kw = kw
+        self.old = {}
+
+    def __enter__(self):
+        for k, v in self.kw.items():
+            self.old[k] = get_option(k)
+            set_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            set_option(k, v)
+        return False
+
+
 def profile_begin(max_launches: int = 4096):
     _check(load().attn_profile_begin(int(max_launches)))
 
 
-KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost", "bwd_dq")
+KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost", "bwd_dq", "fix")
 
 
 def profile_end_kinds() -> dict:

@@ -14,6 +14,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <string.h>
+
 #include <algorithm>
 #include <mutex>
 #include <string>
@@ -43,6 +45,57 @@ int env_int(const char* name, int dflt) {
     const char* s = getenv(name);
     if (!s || !*s) return dflt;
     return atoi(s);
+}
+
+// ---------------------------------------------------------------------------
+// process-wide switches (attn_kernels.h: Options), read from the environment
+// once, then changed only by attn_set_option
+// ---------------------------------------------------------------------------
+struct OptionDef {
+    const char* name;
+    int Options::*field;
+    int dflt;
+};
+const OptionDef kOptionDefs[] = {
+    {"ATTN_GENERIC_DECODE", &Options::generic_decode, 0},
+    {"ATTN_DECODE_WAVES", &Options::decode_waves, 4},
+    {"ATTN_DECODE_KDMA", &Options::decode_kdma, 1},
+    {"ATTN_GENERIC_PREFILL", &Options::generic_prefill, 0},
+    {"ATTN_PREFILL_WAVES", &Options::prefill_waves, 0},
+    {"ATTN_PREFILL_PERSIST", &Options::prefill_persist, 0},
+    {"ATTN_PREFILL_SKIP", &Options::prefill_skip, 0},
+    {"ATTN_VERIFY_TILE", &Options::verify_tile, 1},
+    {"ATTN_MIN_CHUNK", &Options::min_chunk, 256},
+    {"ATTN_WG_PER_CU", &Options::wg_per_cu, 2},
+    {"ATTN_SPLIT_RULE", &Options::split_rule, 0},
+    {"ATTN_VARLEN_CHUNK", &Options::varlen_chunk, 512},
+    {"ATTN_MLA_MIN_CHUNK", &Options::mla_min_chunk, 128},
+    {"ATTN_SPLIT_MAJOR", &Options::split_major, -1},
+    {"ATTN_COMBINE_COLS", &Options::combine_cols, -1},
+    {"ATTN_COMBINE_ROWS", &Options::combine_rows, 1},
+    {"ATTN_COMBINE_SMALL", &Options::combine_small, 1},
+    {"ATTN_BWD_BN", &Options::bwd_bn, 64},
+    {"ATTN_BWD_ATOMIC", &Options::bwd_atomic, 0},
+    {"ATTN_BWD_DQ_ROWS", &Options::bwd_dq_rows, 0},
+    {"ATTN_BWD_DMA", &Options::bwd_dma, 2},
+    {"ATTN_TRACE", &Options::trace, 0},
+};
+Options g_options;
+std::once_flag g_options_once;
+
+Options& mutable_options() {
+    std::call_once(g_options_once, [] {
+        for (const OptionDef& o : kOptionDefs) g_options.*o.field = env_int(o.name, o.dflt);
+    });
+    return g_options;
+}
+
+// "ATTN_X" or "X", case as declared
+const OptionDef* find_option(const char* name) {
+    if (!name) return nullptr;
+    for (const OptionDef& o : kOptionDefs)
+        if (strcmp(o.name, name) == 0 || strcmp(o.name + 5, name) == 0) return &o;
+    return nullptr;
 }
 
 // ---------------------------------------------------------------------------
@@ -104,13 +157,18 @@ int fa3_rule(int total_mblocks, int num_sms, int num_n_blocks, int num_m_blocks,
 // [Occupancy] "The Fix": NSPLIT = clamp(ceil(kv_len / 2048), 1, 32), as an ablation.
 int blog_rule(int sk) { return imax(1, imin(32, ceil_div(sk, 2048))); }
 
-// [FA-tiling] §6.2
+// GQA packing decision ([FA-tiling] §6.2). The row efficiency of a tiling is
+// the share of a query block's rows that exist: seqlen_q / (block_m *
+// ceil(seqlen_q / block_m)) without packing, and the same with g * seqlen_q
+// packed rows. Packing pays when the first is below nine tenths of the second.
+// seqlen_q cancels from that inequality, leaving the integer comparison
+//   10 * ceil(g * seqlen_q / block_m) < 9 * g * ceil(seqlen_q / block_m).
+// Variable-length batches always pack.
 bool should_pack(bool varlen, int seqlen_q, int g, int block_m) {
     if (varlen) return true;
-    auto round_up = [](int a, int b) { return (a + b - 1) / b * b; };
-    const float nopack = float(seqlen_q) / float(round_up(seqlen_q, block_m));
-    const float pack = float(seqlen_q * g) / float(round_up(seqlen_q * g, block_m));
-    return nopack < 0.9f * pack;
+    const long long blocks_packed = ((long long)seqlen_q * g + block_m - 1) / block_m;
+    const long long blocks_plain = ceil_div(seqlen_q, block_m);
+    return 10 * blocks_packed < 9LL * g * blocks_plain;
 }
 
 int device_cus() {
@@ -166,9 +224,9 @@ int check_problem(const Problem& p) {
 struct Plan {
     attn_plan_t pub;
     const FwdVariant* var;
-    size_t vt_offset = 0;  // byte offset of the V pre-pass output in the workspace
-    size_t ctr_offset = 0; // byte offset of the persistent kernels' tile counters
-    int skp = 0;           // its key pitch
+    size_t ctr_offset = 0;  // byte offset of the persistent kernels' tile counters
+    size_t flag_offset = 0; // byte offset of the per-tile fp16-overflow flags
+    int fix_grid = 0;       // workgroups of the bf16 form over flagged tiles (0: none)
 };
 
 int make_plan(const Problem& p, int num_cus, Plan* out) {
@@ -176,6 +234,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     if (rc) return rc;
     const int G = p.Hq / p.Hkv;
     if (num_cus <= 0) num_cus = device_cus();
+    const Options& opt = options();
 
     // ---- tile choice ([FA-tiling] §2, retargeted to gfx950): a "decode" tile of
     // 16 rows when all query rows of a KV head (packed) fit in 16, else a
@@ -191,11 +250,11 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             }
         if (!var) return fail(ATTN_EUNSUPPORTED, "no kernel for d=%d d_v=%d", p.d, dv);
     }
-    if (!var && decode && env_int("ATTN_GENERIC_DECODE", 0) == 0) {
-        const int want_waves = env_int("ATTN_DECODE_WAVES", 4);  // waves per workgroup (4 or 8)
+    if (!var && decode && opt.generic_decode == 0) {
+        const int want_waves = opt.decode_waves;  // waves per workgroup (4 or 8)
         // 1: K through LDS in 32-key halves (else the register-K form where no
         // such variant exists); 0: K straight into registers (ablation)
-        const int want_kdma = env_int("ATTN_DECODE_KDMA", 1) ? 1 : 0;
+        const int want_kdma = opt.decode_kdma ? 1 : 0;
         for (int pass = 0; pass < 2 && !var; ++pass)
             for (const FwdVariant* v = decode_variants(); v->launch; ++v)
                 if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves &&
@@ -204,21 +263,19 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                     break;
                 }
     }
-    if (!var && !decode && env_int("ATTN_GENERIC_PREFILL", 0) == 0) {
+    if (!var && !decode && opt.generic_prefill == 0) {
         // Tile rows ([FA-tiling] §2.5: smaller blocks where masking cuts tiles):
         // 256-row workgroups (8 waves) for full and causal masks, 128 rows (4
         // waves) with a sliding window, where a 256-row tile spends ~20% of its
         // work on masked corners for window 1024 (measured 599 vs 698 TFLOP/s).
         // ATTN_PREFILL_WAVES overrides (ablation).
-        const int want = env_int("ATTN_PREFILL_WAVES", p.window_left >= 0 ? 4 : 8);
-        // kernel family: 1 = 32x32x16 MFMA kernel on fp16 V^T (V pre-pass), 0 = 16x16x32
-        const int want_vt = env_int("ATTN_PREFILL_VT", 0);
+        const int want = opt.prefill_waves > 0 ? opt.prefill_waves : (p.window_left >= 0 ? 4 : 8);
         // 1 = persistent workgroups over per-XCD tile queues
-        const int want_persist = env_int("ATTN_PREFILL_PERSIST", 0) ? 1 : 0;
-        int skip = env_int("ATTN_PREFILL_SKIP", 0);  // ablation: take a later match
+        const int want_persist = opt.prefill_persist ? 1 : 0;
+        int skip = opt.prefill_skip;  // ablation: take a later match
         for (const FwdVariant* v = prefill_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want && (want_vt ? v->needs_vt == want_vt : v->needs_vt == 0) && (v->persistent > 0) == (want_persist > 0) &&
-                skip-- <= 0) {
+            if (v->dtype == p.dtype && v->d == p.d && v->waves_m == want &&
+                (v->persistent > 0) == (want_persist > 0) && skip-- <= 0) {
                 var = v;
                 break;
             }
@@ -228,7 +285,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     // (ATTN_VERIFY_TILE: 0 = widest row tile, 1 = 32-row tile over 2 x 2 waves,
     // 2 = 32-row tile over 2 x 4 waves with 128-key tiles)
     const int head_rows = G > 1 ? p.Sq * G : p.Sq;
-    const int verify_tile = env_int("ATTN_VERIFY_TILE", 1);
+    const int verify_tile = opt.verify_tile;
     const int want_bm = decode ? 16 : (head_rows <= 32 && verify_tile ? 32 : 0);
     const int want_wn = want_bm == 32 ? (verify_tile == 2 ? 4 : 2) : 0;
     for (int pass = 0; pass < 2 && !var; ++pass)
@@ -276,9 +333,9 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
 
     // ---- split count ([llama.cpp] occupancy rule; [FA-tiling] §5 ablation)
     const long long tiles = (long long)p.B * q.grid_heads * q.num_m_blocks;
-    const int min_chunk = env_int("ATTN_MIN_CHUNK", 256);
-    const int wg_per_cu = imax(1, env_int("ATTN_WG_PER_CU", 2));
-    const int rule = env_int("ATTN_SPLIT_RULE", 0);  // 0 occupancy, 1 fa3, 2 blog, 3 occupancy first
+    const int min_chunk = opt.min_chunk;
+    const int wg_per_cu = imax(1, opt.wg_per_cu);
+    const int rule = opt.split_rule;  // 0 occupancy, 1 fa3, 2 blog, 3 occupancy first
     int S = 1;
     int chunk = 0;
     if (p.num_splits >= 1) {
@@ -301,7 +358,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             const long long sum = p.sum_seqlens_k > 0 ? p.sum_seqlens_k : (long long)p.B * p.Sk;
             const long long blocks = (sum + BN - 1) / BN * q.grid_heads * (long long)q.num_m_blocks;
             const long long target = (long long)wg_per_cu * num_cus;
-            int cb = imax(1, ceil_div(env_int("ATTN_VARLEN_CHUNK", 512), BN));
+            int cb = imax(1, ceil_div(opt.varlen_chunk, BN));
             if (blocks / cb < target) cb = (int)imax(1, (int)(blocks / target));
             chunk = cb;
             S = imax(1, imin(ATTN_MAX_SPLITS, ceil_div(imax(max_blocks, 1), cb)));
@@ -312,7 +369,7 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             // partial wave costs more than the splits save: 65,536 keys, 5 query
             // blocks, 51 splits 161 us vs 64 splits 236 us) and every split keeps
             // a minimum chunk of 128 keys.
-            const int mc = imax(1, ceil_div(env_int("ATTN_MLA_MIN_CHUNK", 128), BN));
+            const int mc = imax(1, ceil_div(opt.mla_min_chunk, BN));
             S = imin(imax(1, num_cus / t), imax(1, max_blocks / mc));
         } else {
             S = occupancy_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
@@ -337,22 +394,32 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         q.grid_z = p.B;
         if (q.grid_y > 65535) return fail(ATTN_EINVAL, "grid heads x splits = %d exceeds 65535", q.grid_y);
     }
-    // workspace: split partials, then (kernels that read it) the fp16 V^T of the
-    // V pre-pass, 256-byte aligned
+    // workspace: split partials, then (persistent kernels) the tile counters,
+    // 256-byte aligned
     size_t ws = S > 1 ? attn_workspace_bytes(p.B, p.Hq, p.Sq, dv, S) : 0;
-    out->vt_offset = (ws + 255) & ~(size_t)255;
-    out->skp = ceil_div(imax(p.Sk, 0), 64) * 64;
-    if (var->needs_vt && p.Sk > 0)
-        ws = out->vt_offset + (size_t)p.B * p.Hkv * p.d * (size_t)out->skp * 2;
     out->ctr_offset = (ws + 255) & ~(size_t)255;
     if (var->persistent > 0) ws = out->ctr_offset + 256;  // one tile counter per XCD
+    // kernels with fp16 P.V operands: one overflow flag per tile, and the bf16
+    // form's grid (one workgroup per CU at most)
+    out->flag_offset = (ws + 255) & ~(size_t)255;
+    out->fix_grid = 0;
+    if (var->launch_fix) {
+        const long long total = (long long)p.B * q.grid_heads * S * q.num_m_blocks;
+        if (total > 0) {
+            ws = out->flag_offset + (size_t)total * sizeof(int);
+            out->fix_grid = (int)std::min<long long>(total, num_cus);
+        }
+    }
     q.workspace_bytes = ws;
     out->var = var;
     return ATTN_OK;
 }
 
 // ---------------------------------------------------------------------------
-// split workspace (one per device) and kernel timing
+// scratch memory of a call (split partials, the backward's row sums, tile
+// counters): the caller's workspace bound with attn_set_workspace if there is
+// one, else the library's own buffer on the current device (grown on demand;
+// host threads serialised on it by a lock)
 // ---------------------------------------------------------------------------
 struct Workspace {
     std::mutex mu;
@@ -379,15 +446,50 @@ int ensure_workspace(Workspace& ws, size_t bytes) {
     return ATTN_OK;
 }
 
+struct UserWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+thread_local UserWorkspace t_user_ws;  // per host thread
+
+struct Scratch {
+    void* ptr = nullptr;
+    std::unique_lock<std::mutex> lock;  // held while the library's own buffer is in use
+};
+
+// Scratch of `bytes` for one call on the current device. Fails, with nothing
+// launched yet, when a caller workspace is bound and too small.
+int get_scratch(size_t bytes, Scratch* out) {
+    if (bytes == 0) return ATTN_OK;
+    const UserWorkspace& u = t_user_ws;
+    if (u.ptr) {
+        if (bytes > u.bytes)
+            return fail(ATTN_EINVAL, "the workspace bound to this thread holds %zu bytes; this call needs %zu",
+                        u.bytes, bytes);
+        out->ptr = u.ptr;
+        return ATTN_OK;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(ATTN_EHIP, "hipGetDevice failed");
+    Workspace& ws = g_ws[dev];
+    out->lock = std::unique_lock<std::mutex>(ws.mu);
+    const int rc = ensure_workspace(ws, bytes);
+    if (rc) return rc;
+    out->ptr = ws.ptr;
+    return ATTN_OK;
+}
+
 
 struct Profiler {
     std::mutex mu;
     bool on = false;
     int max_launches = 0;
     std::vector<hipEvent_t> ev;  // pairs
-    std::vector<int> kind;       // 0 forward, 1 combine, 2 V pre-pass / counters,
+    std::vector<int> kind;       // 0 forward, 1 combine, 2 tile counter reset,
                                  // 3 backward key-block kernel, 4 backward pre/post
-                                 // passes, 5 backward dQ kernel
+                                 // passes, 5 backward dQ kernel, 6 the bf16 fix-up
+                                 // of the fp16 P.V kernels
     int used = 0;
 } g_prof;
 
@@ -403,6 +505,19 @@ int prof_start(int kind, hipStream_t s) {
 void prof_stop(int slot, hipStream_t s) {
     if (slot < 0) return;
     (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+}
+
+// ATTN_TRACE=1: one line per forward call with the planner's choices
+void trace_plan(const Problem& pr, const Plan& plan) {
+    const attn_plan_t& q = plan.pub;
+    fprintf(stderr,
+            "attn: B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d dv=%d dtype=%d causal=%d window_left=%d varlen=%d -> "
+            "tile %dx%d waves %dx%d pack=%d splits=%d chunk=%d grid=(%d,%d,%d) threads=%d lds=%d "
+            "persistent=%d workspace=%zu\n",
+            pr.B, pr.Hq, pr.Hkv, pr.Sq, pr.Sk, pr.d, pr.dv > 0 ? pr.dv : pr.d, pr.dtype, pr.causal,
+            pr.window_left, pr.varlen, q.block_m, q.block_n, q.waves_m, q.waves_n, q.pack_gqa,
+            q.num_splits, q.chunk_blocks, q.grid_x, q.grid_y, q.grid_z, q.threads, q.lds_bytes,
+            plan.var->persistent, q.workspace_bytes);
 }
 
 int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -444,7 +559,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.lpt = pl.lpt;
     // decode grids: the workgroups of one key range (all grid heads) are
     // dispatched together, so concurrent reads cover whole interleaved KV rows
-    fp.split_major = env_int("ATTN_SPLIT_MAJOR", plan.var->block_m <= 16 ? 1 : 0);
+    fp.split_major = options().split_major >= 0 ? options().split_major : (plan.var->block_m <= 16 ? 1 : 0);
     // decode tiles: block range and split share of fixed-length problems, and the
     // grid-y divisor as a multiply-high
     {
@@ -457,8 +572,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         div_magic((unsigned int)fp.y_div, &fp.y_mul, &fp.y_s1, &fp.y_s2);
     }
 
-    fp.d_head = pr.d;
-    fp.skp = plan.skp;
+    if (options().trace) trace_plan(pr, plan);
     const dim3 grid(pl.grid_x, pl.grid_y, pl.grid_z);
     if (pl.workspace_bytes == 0) {
         const int slot = prof_start(0, stream);
@@ -468,12 +582,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         return ATTN_OK;
     }
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return fail(ATTN_EHIP, "hipGetDevice failed");
-    Workspace& ws = g_ws[dev];
-    std::lock_guard<std::mutex> lk(ws.mu);
-    rc = ensure_workspace(ws, pl.workspace_bytes);
+    Scratch ws;
+    rc = get_scratch(pl.workspace_bytes, &ws);
     if (rc) return rc;
     const size_t rows = (size_t)pr.B * pr.Sq * pr.Hq;
     fp.o_part = reinterpret_cast<float*>(ws.ptr);
@@ -481,15 +591,6 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.lse_part = fp.o_part + (size_t)pl.num_splits * rows * dvv;
     hipError_t e;
     int slot;
-    if (plan.var->needs_vt) {
-        fp.vt = static_cast<char*>(ws.ptr) + plan.vt_offset;
-        fp.vt_blk = plan.var->needs_vt;
-        slot = prof_start(2, stream);
-        e = launch_v_to_f16t(fp, stream);
-        prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(ATTN_EHIP, "V pre-pass launch: %s", hipGetErrorString(e));
-    }
-
     if (plan.var->persistent > 0) {
         fp.tile_counters = reinterpret_cast<int*>(static_cast<char*>(ws.ptr) + plan.ctr_offset);
         slot = prof_start(2, stream);
@@ -498,10 +599,20 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         if (e != hipSuccess) return fail(ATTN_EHIP, "tile counter reset: %s", hipGetErrorString(e));
     }
 
+    if (plan.fix_grid > 0)
+        fp.tile_flags = reinterpret_cast<int*>(static_cast<char*>(ws.ptr) + plan.flag_offset);
+
     slot = prof_start(0, stream);
     e = plan.var->launch(fp, grid, stream);
     prof_stop(slot, stream);
     if (e != hipSuccess) return fail(ATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
+    if (plan.fix_grid > 0) {
+        // tiles whose V overflowed fp16, again in the bf16 form (before the combine)
+        slot = prof_start(6, stream);
+        e = plan.var->launch_fix(fp, dim3(plan.fix_grid), stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(ATTN_EHIP, "bf16 fix-up launch: %s", hipGetErrorString(e));
+    }
     if (pl.num_splits == 1) return ATTN_OK;
 
     CombineParams cp{};
@@ -535,11 +646,12 @@ int make_bwd_plan(const Problem& p, BwdPlan* out) {
     if (rc) return rc;
     // key block: 64 keys (16 per wave) unless ATTN_BWD_BN asks for 128 (bf16);
     // dQ by a second kernel unless ATTN_BWD_ATOMIC=1 (fp32 atomics, ablation)
-    const int want_bn = env_int("ATTN_BWD_BN", 64);
-    const int want_atomic = env_int("ATTN_BWD_ATOMIC", 0) ? 1 : 0;
-    const int want_dq_rows = env_int("ATTN_BWD_DQ_ROWS", 0);  // 0: first listed
+    const Options& opt = options();
+    const int want_bn = opt.bwd_bn;
+    const int want_atomic = opt.bwd_atomic ? 1 : 0;
+    const int want_dq_rows = opt.bwd_dq_rows;  // 0: first listed
     // 2: both kernels DMA their tiles; 1: only the dQ kernel; 0: neither
-    const int want_dq_dma = env_int("ATTN_BWD_DMA", 2);
+    const int want_dq_dma = opt.bwd_dma;
     const BwdVariant* var = nullptr;
     for (int pass = 0; pass < 2 && !var; ++pass)
         for (const BwdVariant* v = bwd_variants(); v->launch; ++v)
@@ -615,13 +727,9 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     bp.scale_log2 = pr.scale * 1.4426950408889634f;
     bp.num_n_blocks = plan.pub.num_n_blocks;
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return fail(ATTN_EHIP, "hipGetDevice failed");
-    Workspace& ws = g_ws[dev];
-    std::lock_guard<std::mutex> lk(ws.mu);
+    Scratch ws;
     if (plan.pub.workspace_bytes > 0) {
-        rc = ensure_workspace(ws, plan.pub.workspace_bytes);
+        rc = get_scratch(plan.pub.workspace_bytes, &ws);
         if (rc) return rc;
         if (plan.var->atomic_dq) bp.dq_acc = reinterpret_cast<float*>(ws.ptr);
         bp.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + plan.lse2_offset);
@@ -656,6 +764,10 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
 }
 
 }  // namespace
+
+namespace tpa {
+const Options& options() { return mutable_options(); }
+}  // namespace tpa
 
 extern "C" {
 
@@ -819,8 +931,8 @@ int attn_profile_begin(int max_launches) {
 
 int attn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    double t[6] = {0, 0, 0, 0, 0, 0};
-    int n[6] = {0, 0, 0, 0, 0, 0};
+    double t[7] = {0, 0, 0, 0, 0, 0, 0};
+    int n[7] = {0, 0, 0, 0, 0, 0, 0};
     for (int i = 0; i < g_prof.used; ++i) {
         if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) continue;
         float e_ms = 0.f;
@@ -834,7 +946,7 @@ int attn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     g_prof.kind.clear();
     g_prof.on = false;
     g_prof.used = 0;
-    for (int k = 0; k < n_kinds && k < 6; ++k) {
+    for (int k = 0; k < n_kinds && k < 7; ++k) {
         if (ms) ms[k] = t[k];
         if (launches) launches[k] = n[k];
     }
@@ -853,6 +965,33 @@ int attn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
     if (prep_ms) *prep_ms = t[2];
     if (prep_launches) *prep_launches = n[2];
     return rc;
+}
+
+int attn_set_workspace(void* dev_ptr, size_t bytes) {
+    if (dev_ptr && (reinterpret_cast<uintptr_t>(dev_ptr) & 255) != 0)
+        return fail(ATTN_EINVAL, "the workspace must be 256-byte aligned");
+    UserWorkspace& u = t_user_ws;
+    if (!dev_ptr || bytes == 0) {
+        u = UserWorkspace{};
+        return ATTN_OK;
+    }
+    u.ptr = dev_ptr;
+    u.bytes = bytes;
+    return ATTN_OK;
+}
+
+int attn_set_option(const char* name, int value) {
+    const OptionDef* o = find_option(name);
+    if (!o) return fail(ATTN_EINVAL, "unknown option %s", name ? name : "(null)");
+    mutable_options().*o->field = value;
+    return ATTN_OK;
+}
+
+int attn_get_option(const char* name, int* value) {
+    const OptionDef* o = find_option(name);
+    if (!o || !value) return fail(ATTN_EINVAL, "unknown option %s or null output", name ? name : "(null)");
+    *value = mutable_options().*o->field;
+    return ATTN_OK;
 }
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }

@@ -28,11 +28,6 @@
 namespace tpa {
 
 // a switch read from the environment on the host (dflt when unset)
-static int env_flag(const char* name, int dflt) {
-    const char* v = getenv(name);
-    return v && *v ? atoi(v) : dflt;
-}
-
 template <int D, int NW>
 struct DecodeTile {
     static constexpr int KB = 64;              // keys per wave block
@@ -952,14 +947,14 @@ hipError_t launch_decode_kdma(const FwdParams& p, dim3 grid, hipStream_t stream)
 const FwdVariant* decode_variants() {
     static const FwdVariant v[] = {
         // K through LDS in 32-key halves (see attn_decode_kdma_kernel)
-        {DT_BF16, 128, 16, 64, 1, 4, DecodeKdmaTile<128, 4>::LDS_BYTES, &launch_decode_kdma<128, 4>, 0, 0, 0, 0, 1},
-        {DT_BF16, 64, 16, 64, 1, 4, DecodeKdmaTile<64, 4>::LDS_BYTES, &launch_decode_kdma<64, 4>, 0, 0, 0, 0, 1},
+        {DT_BF16, 128, 16, 64, 1, 4, DecodeKdmaTile<128, 4>::LDS_BYTES, &launch_decode_kdma<128, 4>, 0, 0, 0, 1},
+        {DT_BF16, 64, 16, 64, 1, 4, DecodeKdmaTile<64, 4>::LDS_BYTES, &launch_decode_kdma<64, 4>, 0, 0, 0, 1},
         {DT_BF16, 128, 16, 64, 1, 4, DecodeTile<128, 4>::LDS_BYTES, &launch_decode<128, 4>, 0},
         {DT_BF16, 64, 16, 64, 1, 4, DecodeTile<64, 4>::LDS_BYTES, &launch_decode<64, 4>, 0},
         // 8 waves (512 keys per workgroup at one block per wave), one workgroup per CU
         // (K through LDS: 8 x 20 KB, the whole 160 KB; d = 128 only, where the
         // merge splits the 8 d tiles one per wave)
-        {DT_BF16, 128, 16, 64, 1, 8, DecodeKdmaTile<128, 8>::LDS_BYTES, &launch_decode_kdma<128, 8>, 0, 0, 0, 0, 1},
+        {DT_BF16, 128, 16, 64, 1, 8, DecodeKdmaTile<128, 8>::LDS_BYTES, &launch_decode_kdma<128, 8>, 0, 0, 0, 1},
         {DT_BF16, 128, 16, 64, 1, 8, DecodeTile<128, 8>::LDS_BYTES, &launch_decode<128, 8>, 0},
         {DT_BF16, 64, 16, 64, 1, 8, DecodeTile<64, 8>::LDS_BYTES, &launch_decode<64, 8>, 0},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
@@ -970,8 +965,8 @@ const FwdVariant* decode_variants() {
 // Kernel choice: the split-group kernel parallelises over splits (decode: many
 // splits, few rows); the column kernel over output elements.
 bool combine_by_columns(int rows, int d, int num_splits) {
-    const int env = env_flag("ATTN_COMBINE_COLS", -1);
-    if (env >= 0) return env != 0;
+    const int force = options().combine_cols;
+    if (force >= 0) return force != 0;
     (void)rows;
     (void)d;
     // measured: columns win at <= 16 splits (latent verify, 4 splits x 544 rows:
@@ -983,7 +978,7 @@ hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream
     // 512-wide rows (latent values): one workgroup per row (measured on the latent
     // verify shape, 16 splits x 544 rows: the column kernel took 11.1 us; on the
     // 65,536-key prefix, 51 splits x 272 rows: 24 us with either other kernel)
-    if (d == 512 && env_flag("ATTN_COMBINE_ROWS", 1) != 0) {
+    if (d == 512 && options().combine_rows != 0) {
         if (out_bf16) hipLaunchKernelGGL((lse_combine_rows_kernel<true, 512>), dim3(p.rows), dim3(512), 0, stream, p);
         else hipLaunchKernelGGL((lse_combine_rows_kernel<false, 512>), dim3(p.rows), dim3(512), 0, stream, p);
         return hipGetLastError();
@@ -993,7 +988,7 @@ hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream
         dim3 grid((unsigned)((n + 255) / 256)), block(256);
         // every partial of a thread in flight at once for up to 8 / 16 splits
         // (ATTN_COMBINE_SMALL=0: the looped form for any count)
-        const int small = env_flag("ATTN_COMBINE_SMALL", 1);
+        const int small = options().combine_small;
         if (small && p.num_splits <= 8) {
             if (out_bf16) hipLaunchKernelGGL((lse_combine_cols_small_kernel<true, 8>), grid, block, 0, stream, p, d);
             else hipLaunchKernelGGL((lse_combine_cols_small_kernel<false, 8>), grid, block, 0, stream, p, d);

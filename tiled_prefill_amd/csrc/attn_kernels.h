@@ -18,11 +18,12 @@ struct FwdVariant {
     int lds_bytes;
     hipError_t (*launch)(const FwdParams&, dim3 grid, hipStream_t stream);
     int grid_1d;            // 1: one-dimensional XCD-aware grid over all tiles
-    int needs_vt;           // > 0: reads V as fp16 V^T from the V pre-pass (FwdParams::vt),
-                            // keys permuted in blocks of this many (16 or 32)
     int persistent;         // > 0: persistent workgroups (this many per CU) over tile queues
     int dv;                 // value / output width when it differs from d (0: equal to d)
     int kdma;               // decode kernels: 1 = K through LDS in 32-key halves, 0 = K into registers
+    // kernels that compute P.V on fp16 operands: the bf16 form over the tiles
+    // they flag in FwdParams::tile_flags (null for kernels without flags)
+    hipError_t (*launch_fix)(const FwdParams&, dim3 grid, hipStream_t stream);
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
@@ -31,9 +32,6 @@ const FwdVariant* fwd_variants();
 const FwdVariant* decode_variants();
 const FwdVariant* prefill_variants();
 const FwdVariant* mla_variants();   // values of their own width (d_v != d)
-
-// The V pre-pass: V (bf16) -> fp16 V^T in FwdParams::vt (pitch FwdParams::skp).
-hipError_t launch_v_to_f16t(const FwdParams& p, hipStream_t stream);
 
 // Zeroes the per-XCD tile queue counters of a persistent kernel.
 hipError_t launch_tile_counters_reset(int* counters, hipStream_t stream);
@@ -56,5 +54,35 @@ const BwdVariant* bwd_variants();  // null-terminated by launch == nullptr
 
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);
+
+// Planner and launch switches. Each starts at its default, is read once per
+// process from its ATTN_* environment variable (at the first use), and can be
+// changed at run time with attn_set_option. Apart from `trace`, every
+// non-default value selects an ablation measured against the default path.
+struct Options {
+    int generic_decode;   // ATTN_GENERIC_DECODE=1: general tile kernel for bf16 decode tiles
+    int decode_waves;     // ATTN_DECODE_WAVES: waves per decode workgroup (4; 8)
+    int decode_kdma;      // ATTN_DECODE_KDMA: 1 K through LDS in 32-key halves; 0 K into registers
+    int generic_prefill;  // ATTN_GENERIC_PREFILL=1: general tile kernel for bf16 prefill
+    int prefill_waves;    // ATTN_PREFILL_WAVES: 8 (256 rows) or 4 (128 rows); 0 = by mask
+    int prefill_persist;  // ATTN_PREFILL_PERSIST=1: persistent workgroups over per-XCD queues
+    int prefill_skip;     // ATTN_PREFILL_SKIP=n: the n-th later matching prefill variant
+    int verify_tile;      // ATTN_VERIFY_TILE: 0 widest row tile, 1 32-row 2x2, 2 32-row 2x4
+    int min_chunk;        // ATTN_MIN_CHUNK: minimum keys per split (256)
+    int wg_per_cu;        // ATTN_WG_PER_CU: workgroup target per CU of the split rule (2)
+    int split_rule;       // ATTN_SPLIT_RULE: 0 occupancy, 1 [FA-tiling] 5.2, 2 NSPLIT, 3 occupancy first
+    int varlen_chunk;     // ATTN_VARLEN_CHUNK: keys per split of variable-length problems (512)
+    int mla_min_chunk;    // ATTN_MLA_MIN_CHUNK: minimum keys per split of the latent kernel (128)
+    int split_major;      // ATTN_SPLIT_MAJOR: grid order of split workgroups; -1 = by tile
+    int combine_cols;     // ATTN_COMBINE_COLS: -1 by split count, 0/1 force split groups / columns
+    int combine_rows;     // ATTN_COMBINE_ROWS: 1 row-parallel combine for 512-wide rows
+    int combine_small;    // ATTN_COMBINE_SMALL: 1 all-loads-first column combine up to 16 splits
+    int bwd_bn;           // ATTN_BWD_BN: keys per backward workgroup (64; 128)
+    int bwd_atomic;       // ATTN_BWD_ATOMIC=1: single-pass backward with fp32 dQ atomics
+    int bwd_dq_rows;      // ATTN_BWD_DQ_ROWS: query rows per dQ workgroup (0 = first listed)
+    int bwd_dma;          // ATTN_BWD_DMA: 2 both kernels DMA their tiles, 1 only dQ, 0 neither
+    int trace;            // ATTN_TRACE=1: print every call's plan to stderr
+};
+const Options& options();
 
 }  // namespace tpa

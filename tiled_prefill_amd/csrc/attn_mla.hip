@@ -13,13 +13,16 @@
 // ([FA-tiling] §6.3: packed row r is query position r / G, head hkv G + r % G),
 // so every K/V tile is read once for all of them. One workgroup: 4 waves x 16
 // packed rows, 32-key tiles, double-buffered in LDS (K 36 KB by DMA, V 32 KB
-// converted to fp16 through registers; 136 KB, one workgroup per CU, one wave
-// per SIMD, up to 512 VGPRs: the 576-wide Q^T fragments take 72, the 512-wide
-// O^T accumulators 128). The arithmetic is that of attn_prefill_kernel:
-// S^T = K Q^T on 16x16x32 bf16 MFMA, online softmax with a lazy reference max,
-// O^T += V^T P^T on 16x16x32 fp16 MFMA with P rounded once to fp16, row sums on
-// the matrix core. Split-KV partials ([FA-tiling] §5) go to the combine kernel
-// with rows of DV values.
+// through registers; 136 KB, one workgroup per CU, one wave per SIMD, up to
+// 512 VGPRs: the 576-wide Q^T fragments take 72, the 512-wide O^T accumulators
+// 128). S^T = K Q^T on 16x16x32 bf16 MFMA, online softmax with a lazy
+// reference max, O^T += V^T P^T on 16x16x32 bf16 MFMA with V as stored and P
+// as two bf16 parts (P ~= hi + lo to about 16 bits: one bf16 rounding of P
+// would cost up to 2^-9 per term, and fp16 operands would not hold V beyond
+// 65504), row sums of hi + lo on the matrix core. The kernel is bound by its
+// per-tile latency, not the matrix core, so the second P.V product is cheap
+// here. Split-KV partials ([FA-tiling] §5) go to the combine kernel with rows
+// of DV values.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -126,9 +129,9 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
 #pragma unroll
     for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
-    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};  // fp16 1.0
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     const float sl2 = p.scale_log2;
-    constexpr float LAZY = 8.f;  // lazy reference max (P <= 2^8 stays inside fp16)
+    constexpr float LAZY = 8.f;  // lazy reference max: O is rescaled only when the max moves by > 2^8
 
     // ---- K/V tiles
     const size_t k_stride = (size_t)p.Hkv * DK, v_stride = (size_t)p.Hkv * DV;
@@ -166,10 +169,7 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
         for (int j = 0; j < C::VCH; ++j) {
             const int id = tid + C::NTHR * j;
             const int rr = id / C::VCPR, ch = id % C::VCPR;
-            u32x4 h;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(vst[j][e]);
-            *reinterpret_cast<u32x4*>(dst + rr * VROWB + 16 * C::vslot(ch, rr)) = h;
+            *reinterpret_cast<u32x4*>(dst + rr * VROWB + 16 * C::vslot(ch, rr)) = vst[j];
         }
     };
 
@@ -239,14 +239,17 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sacc[tt][e] = fast_exp2(fmaf(sacc[tt][e], sl2, neg));
 
-        // O^T += V^T . P^T (fp16): one 32-key step; lane group g supplies keys
-        // 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3
-        u32x4 pf;
-        pf[0] = pack_f16x2(sacc[0][0], sacc[0][1]);
-        pf[1] = pack_f16x2(sacc[0][2], sacc[0][3]);
-        pf[2] = pack_f16x2(sacc[1][0], sacc[1][1]);
-        pf[3] = pack_f16x2(sacc[1][2], sacc[1][3]);
-        lacc = mfma_f16(ones, pf, lacc);
+        // O^T += V^T . P^T (bf16, P as hi + lo): one 32-key step; lane group g
+        // supplies keys 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3
+        u32x4 ph, plo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const u32x2 hl = split_bf16x2(sacc[w >> 1][2 * (w & 1)], sacc[w >> 1][2 * (w & 1) + 1]);
+            ph[w] = hl[0];
+            plo[w] = hl[1];
+        }
+        lacc = mfma_bf16(ones, ph, lacc);
+        lacc = mfma_bf16(ones, plo, lacc);
         const int ra = 4 * lg + (li >> 2), rb = ra + 16;
         const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
 #pragma unroll
@@ -255,7 +258,8 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
             const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + ra * VROWB + 16 * C::vslot(ch, ra) + hb));
             const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * VROWB + 16 * C::vslot(ch, rb) + hb));
             const u32x4 vf = {a[0], a[1], c[0], c[1]};
-            oacc[u] = mfma_f16(vf, pf, oacc[u]);
+            oacc[u] = mfma_bf16(vf, ph, oacc[u]);
+            oacc[u] = mfma_bf16(vf, plo, oacc[u]);
         }
 
         if (more) {
@@ -303,7 +307,7 @@ hipError_t launch_mla(const FwdParams& p, dim3 grid, hipStream_t stream) {
 const FwdVariant* mla_variants() {
     static const FwdVariant v[] = {
         // d = 576, d_v = 512 (latent attention); block_n 32, 4 waves x 16 packed rows
-        {DT_BF16, 576, 64, 32, 4, 1, MlaTile<576, 512>::LDS_BYTES, &launch_mla<576, 512>, 1, 0, 0, 512},
+        {DT_BF16, 576, 64, 32, 4, 1, MlaTile<576, 512>::LDS_BYTES, &launch_mla<576, 512>, 1, 0, 512},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;

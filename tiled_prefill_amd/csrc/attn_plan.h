@@ -139,11 +139,9 @@ struct FwdParams {
     int chunk_blocks;       // > 0: per-sequence split count (variable length)
     int lpt;                // reverse query-block order (heaviest causal blocks first)
     int split_major;        // grid y = split * grid_heads + head (else head * splits + split)
-    const void* vt;         // fp16 V^T written by the V pre-pass (kernels that take it), else null
-    int skp;                // key pitch of vt (Sk rounded up to 64)
-    int d_head;             // head dim (for launchers that dispatch on it)
-    int vt_blk;             // key-permutation block of vt (16 or 32; see the V pre-pass)
     int* tile_counters;     // persistent kernels: one tile queue counter per XCD, zero at launch
+    int* tile_flags;        // fp16 P.V kernels: per tile, 1 if its V overflowed fp16 (then the
+                            // bf16 form reruns it), written for every tile on every launch
     // Decode tiles of fixed-length problems (seqlens_k null): the key-block
     // range of the single query block and its blocks per split, computed once
     // on the host. blockIdx.y / y_div (y_div = grid_heads when split_major, else
