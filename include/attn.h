@@ -106,6 +106,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                int causal, int window_left, float scale, int num_splits,
                int dtype, void* stream);
 
+/* attn_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * kernels and results as attn_fwd; its scratch (split partials, per-tile
+ * flags, tile counters) is a static device array of ATTN_NOALLOC_SCRATCH_BYTES
+ * in the library, one per device, held from the library's load until the
+ * process ends. The call allocates nothing and ignores attn_set_workspace. A
+ * problem whose plan needs more scratch (workspace_bytes of attn_plan_fwd)
+ * returns ATTN_EINVAL and launches nothing. Every call on a device shares that
+ * device's array, which keeps the last call's contents: calls that can overlap
+ * on one GPU (other streams, other host threads) race on it -- issue them on
+ * one stream. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                     int causal, int window_left, float scale, int num_splits,
+                     int dtype, void* stream);
+
 /* Values of their own width: the latent-attention verify shape of [Occupancy]
  * (one KV head shared by every query head; keys 576 wide = 512 latent + 64
  * rotary, values 512 wide). q [B][Sq][Hq][d], k [B][Sk][Hkv][d],

@@ -175,3 +175,13 @@ def test_options_change_the_plan(attn_options):
     attn_options("PREFILL_WAVES", 4)
     assert tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)["block_m"] == 128
     assert base["block_m"] == 256
+
+
+def test_noalloc_refuses_a_problem_beyond_its_static_scratch():
+    # 256 forced splits of 2048 decode rows need ~270 MB of partials: refused
+    # before any GPU call
+    lib = tpa.load()
+    rc = lib.attn_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, None, 64, 32, 32, 1, 4096, 128, 0, -1,
+                              0.088, 256, tpa.BF16, None)
+    assert rc == -1
+    assert "noalloc" in lib.attn_last_error().decode()

@@ -78,6 +78,8 @@ def load():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_fwd.restype = i
+    lib.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd_noalloc.restype = i
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp, ll, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_plan_fwd.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ll, i, ctypes.POINTER(Plan)]
@@ -176,6 +178,24 @@ def fwd(q, k, v, causal: bool = False, window_left: int = -1, scale: Optional[fl
                            lse.data_ptr() if lse is not None else None,
                            B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
                            float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
+    _check(rc)
+    return out, lse
+
+
+def fwd_noalloc(q, k, v, out: torch.Tensor, lse: Optional[torch.Tensor], causal: bool = False,
+                window_left: int = -1, scale: Optional[float] = None, num_splits: int = 0,
+                stream=None):
+    """attn_fwd_noalloc: attn_fwd with its scratch in the library's static device array
+    (nothing allocated; the caller passes the outputs)."""
+    _check_tensors(q, k, v)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rc = load().attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), int(window_left),
+                                 float(scale), int(num_splits), _dtype_code(q), _stream_ptr(stream))
     _check(rc)
     return out, lse
 

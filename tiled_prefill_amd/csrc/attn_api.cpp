@@ -457,10 +457,25 @@ struct Scratch {
     std::unique_lock<std::mutex> lock;  // held while the library's own buffer is in use
 };
 
+static_assert(ATTN_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library agree on the static scratch");
+
+// Where a forward call's scratch comes from: the default (a bound caller
+// workspace, else the library's own buffer), or attn_fwd_noalloc's static array.
+enum ScratchSource { SCRATCH_DEFAULT = 0, SCRATCH_STATIC = 1 };
+
 // Scratch of `bytes` for one call on the current device. Fails, with nothing
-// launched yet, when a caller workspace is bound and too small.
-int get_scratch(size_t bytes, Scratch* out) {
+// launched yet, when a caller workspace is bound and too small, or when the
+// static array is too small.
+int get_scratch(size_t bytes, Scratch* out, int source = SCRATCH_DEFAULT) {
     if (bytes == 0) return ATTN_OK;
+    if (source == SCRATCH_STATIC) {
+        if (bytes > kNoAllocScratchBytes)
+            return fail(ATTN_EINVAL, "this call needs %zu bytes of scratch; attn_fwd_noalloc holds %zu",
+                        bytes, kNoAllocScratchBytes);
+        const hipError_t e = noalloc_scratch(&out->ptr);
+        if (e != hipSuccess) return fail(ATTN_EHIP, "static scratch address: %s", hipGetErrorString(e));
+        return ATTN_OK;
+    }
     const UserWorkspace& u = t_user_ws;
     if (u.ptr) {
         if (bytes > u.bytes)
@@ -521,7 +536,7 @@ void trace_plan(const Problem& pr, const Plan& plan) {
 }
 
 int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* o, float* lse,
-            const int* seqlens_k, void* stream_v) {
+            const int* seqlens_k, void* stream_v, int scratch_source = SCRATCH_DEFAULT) {
     // pointers are checked only where they will be read (empty tensors may be null)
     const bool has_rows = pr.B > 0 && pr.Sq > 0;
     if (has_rows && (!q || !o)) return fail(ATTN_EINVAL, "null q or o pointer");
@@ -583,7 +598,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     }
 
     Scratch ws;
-    rc = get_scratch(pl.workspace_bytes, &ws);
+    rc = get_scratch(pl.workspace_bytes, &ws, scratch_source);
     if (rc) return rc;
     const size_t rows = (size_t)pr.B * pr.Sq * pr.Hq;
     fp.o_part = reinterpret_cast<float*>(ws.ptr);
@@ -776,6 +791,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                int num_splits, int dtype, void* stream) {
     Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, scale};
     return run_fwd(p, q, k, v, o, lse, nullptr, stream);
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                     float scale, int num_splits, int dtype, void* stream) {
+    Problem p{B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, 0, 0, scale};
+    return run_fwd(p, q, k, v, o, lse, nullptr, stream, SCRATCH_STATIC);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, int B,

@@ -55,6 +55,12 @@ const BwdVariant* bwd_variants();  // null-terminated by launch == nullptr
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);
 
+// The static device scratch of attn_fwd_noalloc (attn_scratch.hip): its size,
+// and the address of the current device's copy (read once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** ptr);
+
 // Planner and launch switches. Each starts at its default, is read once per
 // process from its ATTN_* environment variable (at the first use), and can be
 // changed at run time with attn_set_option. Apart from `trace`, every
