@@ -758,6 +758,14 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
         prof_stop(slot, stream);
         if (e != hipSuccess) return fail(ATTN_EHIP, "backward pre-pass launch: %s", hipGetErrorString(e));
     }
+    // two-pass form: the dQ kernel first (the bf16 form also stores the rows'
+    // D = sum_j P dP there), then the key-block kernel, which reads D
+    if (has_rows && !plan.var->atomic_dq) {
+        slot = prof_start(5, stream);
+        e = plan.var->launch_dq(bp, stream);
+        prof_stop(slot, stream);
+        if (e != hipSuccess) return fail(ATTN_EHIP, "backward dQ launch: %s", hipGetErrorString(e));
+    }
     if (has_keys) {
         slot = prof_start(3, stream);
         e = plan.var->launch(bp, stream);
@@ -769,11 +777,6 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
         e = plan.var->launch_post(bp, stream);
         prof_stop(slot, stream);
         if (e != hipSuccess) return fail(ATTN_EHIP, "backward post-pass launch: %s", hipGetErrorString(e));
-    } else if (has_rows) {
-        slot = prof_start(5, stream);
-        e = plan.var->launch_dq(bp, stream);
-        prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(ATTN_EHIP, "backward dQ launch: %s", hipGetErrorString(e));
     }
     return ATTN_OK;
 }

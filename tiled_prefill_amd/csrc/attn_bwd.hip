@@ -84,7 +84,8 @@ struct BwdTile {
     static constexpr int Q_BYTES = BM * QST * ESZ;
     // the K tile and the dS^T tile are needed only when dQ is accumulated here
     static constexpr int K_BYTES = ATOMIC ? BN * QST * ESZ : 0;
-    static constexpr int S_BYTES = ATOMIC ? BN * SST * ESZ : 0;
+    // (bf16: dS^T as hi and lo tiles, one after the other)
+    static constexpr int S_BYTES = ATOMIC ? (BF ? 2 : 1) * BN * SST * ESZ : 0;
     static constexpr int LDS_BYTES = 2 * Q_BYTES + K_BYTES + S_BYTES + 2 * BM * 4;
     static_assert(NKW % 16 == 0 && (!BF || BN % 32 == 0), "key slice must fill the MFMA");
     static_assert(QITEMS >= 1 && BM * CPR % NTHR == 0, "Q tile load must divide evenly");
@@ -96,9 +97,9 @@ struct BwdTile {
 };
 
 // ---------------------------------------------------------------------------
-// pre-pass: D = <dO, O> per row, lse in log2 units, zero dQ accumulator
+// pre-pass: D = <dO, O> per row (WITH_D), lse in log2 units, zero dQ accumulator
 // ---------------------------------------------------------------------------
-template <class T, int D>
+template <class T, int D, bool WITH_D = true>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
     constexpr int CE = 16 / (int)sizeof(T);
     constexpr int TPR = D / CE;  // threads per row (8, 16 or 32; divides 64)
@@ -107,7 +108,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
     const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
     const int c = threadIdx.x % TPR;
     float dot = 0.f;
-    if (row < rows) {
+    if (WITH_D && row < rows) {
         const u32x4 ov = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.o) + row * D + c * CE);
         const u32x4 gv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.dout) + row * D + c * CE);
         if constexpr (std::is_same<T, bf16_t>::value) {
@@ -135,7 +136,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams p) {
         const int b = (int)(row / ((long long)p.Hq * p.Sq));
         const size_t idx = ((size_t)b * p.Hq + h) * p.Sq + i;
         const float l = p.lse[idx];
-        p.dsum[idx] = dot;
+        if (WITH_D) p.dsum[idx] = dot;
         p.lse2[idx] = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
     }
 }
@@ -360,17 +361,11 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
         if constexpr (BF) {
 #pragma unroll
             for (int pp = 0; pp < BM / 32; ++pp) {
-                u32x4 pb[NT], sb[NT];
+                u32x4 pb[NT], sb[NT], pbl[NT], sbl[NT];  // P and dS as bf16 hi + lo
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    pb[t] = u32x4{pack_bf16x2(sacc[2 * pp][t][0], sacc[2 * pp][t][1]),
-                                  pack_bf16x2(sacc[2 * pp][t][2], sacc[2 * pp][t][3]),
-                                  pack_bf16x2(sacc[2 * pp + 1][t][0], sacc[2 * pp + 1][t][1]),
-                                  pack_bf16x2(sacc[2 * pp + 1][t][2], sacc[2 * pp + 1][t][3])};
-                    sb[t] = u32x4{pack_bf16x2(pacc[2 * pp][t][0], pacc[2 * pp][t][1]),
-                                  pack_bf16x2(pacc[2 * pp][t][2], pacc[2 * pp][t][3]),
-                                  pack_bf16x2(pacc[2 * pp + 1][t][0], pacc[2 * pp + 1][t][1]),
-                                  pack_bf16x2(pacc[2 * pp + 1][t][2], pacc[2 * pp + 1][t][3])};
+                    split_bf16x8(sacc[2 * pp][t], sacc[2 * pp + 1][t], pb[t], pbl[t]);
+                    split_bf16x8(pacc[2 * pp][t], pacc[2 * pp + 1][t], sb[t], sbl[t]);
                 }
                 const int ra = (32 * pp + 4 * lg + (li >> 2)) * QST + 4 * (li & 3);
                 const int rb = ra + 16 * QST;
@@ -385,7 +380,9 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         dvT[u][t] = mfma_bf16(da, pb[t], dvT[u][t]);
+                        dvT[u][t] = mfma_bf16(da, pbl[t], dvT[u][t]);
                         dkT[u][t] = mfma_bf16(qa, sb[t], dkT[u][t]);
+                        dkT[u][t] = mfma_bf16(qa, sbl[t], dkT[u][t]);
                     }
                 }
             }
@@ -416,8 +413,10 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
             for (int t = 0; t < NT; ++t) {
                 T* dst = dSt + (kw0 + 16 * t + li) * SST + 16 * qb + 4 * lg;
                 if constexpr (BF) {
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(pacc[qb][t][0], pacc[qb][t][1]),
-                                                           pack_bf16x2(pacc[qb][t][2], pacc[qb][t][3])};
+                    const u32x2 w0 = split_bf16x2(pacc[qb][t][0], pacc[qb][t][1]);
+                    const u32x2 w1 = split_bf16x2(pacc[qb][t][2], pacc[qb][t][3]);
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{w0[0], w1[0]};
+                    *reinterpret_cast<u32x2*>(dst + BN * SST) = u32x2{w0[1], w1[1]};  // lo parts
                 } else {
                     *reinterpret_cast<f32x4*>(dst) = pacc[qb][t];
                 }
@@ -435,12 +434,16 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_kernel(BwdParams p) {
                 const u32x2 a0 = lds_read_tr16(dSt + ka * SST + 16 * wave + 4 * (li & 3));
                 const u32x2 a1 = lds_read_tr16(dSt + (ka + 4) * SST + 16 * wave + 4 * (li & 3));
                 const u32x4 sa = {a0[0], a0[1], a1[0], a1[1]};
+                const u32x2 c0 = lds_read_tr16(dSt + BN * SST + ka * SST + 16 * wave + 4 * (li & 3));
+                const u32x2 c1 = lds_read_tr16(dSt + BN * SST + (ka + 4) * SST + 16 * wave + 4 * (li & 3));
+                const u32x4 sl = {c0[0], c0[1], c1[0], c1[1]};
 #pragma unroll
                 for (int u = 0; u < D / 16; ++u) {
                     const u32x2 b0 = lds_read_tr16(Ks + ka * QST + 16 * u + 4 * (li & 3));
                     const u32x2 b1 = lds_read_tr16(Ks + (ka + 4) * QST + 16 * u + 4 * (li & 3));
                     const u32x4 kb = {b0[0], b0[1], b1[0], b1[1]};
                     dqa[u] = mfma_bf16(sa, kb, dqa[u]);
+                    dqa[u] = mfma_bf16(sl, kb, dqa[u]);
                 }
             }
         } else {
@@ -718,13 +721,10 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_kernel(BwdParams p) {
         if constexpr (BF) {
 #pragma unroll
             for (int pp = 0; pp < NT / 2; ++pp) {
-                u32x4 sb[NQW];
+                u32x4 sb[NQW], sbl[NQW];  // dS as bf16 hi + lo
 #pragma unroll
                 for (int qq = 0; qq < NQW; ++qq)
-                    sb[qq] = u32x4{pack_bf16x2(pacc[2 * pp][qq][0], pacc[2 * pp][qq][1]),
-                                   pack_bf16x2(pacc[2 * pp][qq][2], pacc[2 * pp][qq][3]),
-                                   pack_bf16x2(pacc[2 * pp + 1][qq][0], pacc[2 * pp + 1][qq][1]),
-                                   pack_bf16x2(pacc[2 * pp + 1][qq][2], pacc[2 * pp + 1][qq][3])};
+                    split_bf16x8(pacc[2 * pp][qq], pacc[2 * pp + 1][qq], sb[qq], sbl[qq]);
 #pragma unroll
                 for (int u = 0; u < D / 16; ++u) {
                     const T* krow = KT + (16 * u + li) * TST + 32 * pp + 4 * lg;
@@ -732,7 +732,10 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_kernel(BwdParams p) {
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(krow + 16);
                     const u32x4 ka = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-                    for (int qq = 0; qq < NQW; ++qq) dqT[u][qq] = mfma_bf16(ka, sb[qq], dqT[u][qq]);
+                    for (int qq = 0; qq < NQW; ++qq) {
+                        dqT[u][qq] = mfma_bf16(ka, sb[qq], dqT[u][qq]);
+                        dqT[u][qq] = mfma_bf16(ka, sbl[qq], dqT[u][qq]);
+                    }
                 }
             }
         } else {
@@ -843,7 +846,6 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
             whi = imin(whi, hi);
             const size_t idx = ((size_t)b * p.Hq + hq) * Sq + pos;
             l2[qq] = p.lse2[idx];
-            dsum[qq] = p.dsum[idx];
         }
         row_lo[qq] = lo;
         row_hi[qq] = hi;
@@ -899,9 +901,19 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
         }
     };
 
-    // key blocks in ascending order: the query blocks of a head, which run
-    // together on one XCD, then walk the head's K and V tiles roughly in step
-    // and share them in L2
+    // Two sweeps over the key blocks, in ascending order (the query blocks of a
+    // head, which run together on one XCD, then walk the head's K and V tiles
+    // roughly in step and share them in L2). The first forms the row sums
+    // D_i = sum_j P_ij dP_ij of the exact softmax -- <dO_i, O_i> of the forward
+    // output would carry O's bf16 rounding, which dS = P (dP - D) turns into a
+    // relative error of several percent in dQ and dK of rows with few keys --
+    // and stores them for the key-block kernel, which runs after this one; the
+    // second forms dS and dQ.
+    float dacc[NQW];
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) dacc[qq] = 0.f;
+    auto sweep = [&](auto pass) {
+    constexpr bool ROWSUM = decltype(pass)::value;
     if (has_work) {
         load_kv(n_lo, 0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed
@@ -954,17 +966,15 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
                             const int key = key0 + 16 * (2 * pp + h) + 4 * lg + r;
                             pv = (key < row_lo[qq] || key > row_hi[qq]) ? 0.f : pv;
                         }
-                        pacc[h][qq][r] = pv * (pacc[h][qq][r] - dsum[qq]);
+                        if constexpr (ROWSUM) dacc[qq] += pv * pacc[h][qq][r];
+                        else pacc[h][qq][r] = pv * (pacc[h][qq][r] - dsum[qq]);
                     }
+            if constexpr (ROWSUM) continue;
             // K^T by transpose reads of the K tile; source lane s of a 16-lane
             // group addresses key row k0 + s / 4, columns 16u + 4 (s % 4)
-            u32x4 sb[NQW];
+            u32x4 sb[NQW], sbl[NQW];  // dS as bf16 hi + lo
 #pragma unroll
-            for (int qq = 0; qq < NQW; ++qq)
-                sb[qq] = u32x4{pack_bf16x2(pacc[0][qq][0], pacc[0][qq][1]),
-                               pack_bf16x2(pacc[0][qq][2], pacc[0][qq][3]),
-                               pack_bf16x2(pacc[1][qq][0], pacc[1][qq][1]),
-                               pack_bf16x2(pacc[1][qq][2], pacc[1][qq][3])};
+            for (int qq = 0; qq < NQW; ++qq) split_bf16x8(pacc[0][qq], pacc[1][qq], sb[qq], sbl[qq]);
             const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
 #pragma unroll
             for (int u = 0; u < D / 16; ++u) {
@@ -975,13 +985,24 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
                 const u32x2 hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(kt + o1));
                 const u32x4 ka = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-                for (int qq = 0; qq < NQW; ++qq) dqT[u][qq] = mfma_bf16(ka, sb[qq], dqT[u][qq]);
+                for (int qq = 0; qq < NQW; ++qq) {
+                    dqT[u][qq] = mfma_bf16(ka, sb[qq], dqT[u][qq]);
+                    dqT[u][qq] = mfma_bf16(ka, sbl[qq], dqT[u][qq]);
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
         __syncthreads();
         stage ^= 1;
     }
+    };
+    sweep(std::true_type{});
+#pragma unroll
+    for (int qq = 0; qq < NQW; ++qq) {
+        dsum[qq] = xor_sum(dacc[qq]);  // the four lane groups hold disjoint keys of the row
+        if (lg == 0 && row_pos[qq] < Sq) p.dsum[((size_t)b * p.Hq + hq) * Sq + row_pos[qq]] = dsum[qq];
+    }
+    sweep(std::false_type{});
 
 #pragma unroll
     for (int qq = 0; qq < NQW; ++qq) {
@@ -1186,13 +1207,11 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
                     }
                 }
             }
-            u32x4 pb[NT], sb[NT];
+            u32x4 pb[NT], sb[NT], pbl[NT], sbl[NT];  // P and dS as bf16 hi + lo
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                pb[t] = u32x4{pack_bf16x2(sacc[0][t][0], sacc[0][t][1]), pack_bf16x2(sacc[0][t][2], sacc[0][t][3]),
-                              pack_bf16x2(sacc[1][t][0], sacc[1][t][1]), pack_bf16x2(sacc[1][t][2], sacc[1][t][3])};
-                sb[t] = u32x4{pack_bf16x2(pacc[0][t][0], pacc[0][t][1]), pack_bf16x2(pacc[0][t][2], pacc[0][t][3]),
-                              pack_bf16x2(pacc[1][t][0], pacc[1][t][1]), pack_bf16x2(pacc[1][t][2], pacc[1][t][3])};
+                split_bf16x8(sacc[0][t], sacc[1][t], pb[t], pbl[t]);
+                split_bf16x8(pacc[0][t], pacc[1][t], sb[t], sbl[t]);
             }
             const int r0 = 32 * pp + 4 * lg + (li >> 2), r1 = r0 + 16;
 #pragma unroll
@@ -1209,7 +1228,9 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     dvT[u][t] = mfma_bf16(da, pb[t], dvT[u][t]);
+                    dvT[u][t] = mfma_bf16(da, pbl[t], dvT[u][t]);
                     dkT[u][t] = mfma_bf16(qa, sb[t], dkT[u][t]);
+                    dkT[u][t] = mfma_bf16(qa, sbl[t], dkT[u][t]);
                 }
             }
         }
@@ -1239,13 +1260,13 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
 // ---------------------------------------------------------------------------
 // launchers and the variant table
 // ---------------------------------------------------------------------------
-template <class T, int D>
+template <class T, int D, bool WITH_D = true>
 hipError_t launch_bwd_pre(const BwdParams& p, hipStream_t stream) {
     constexpr int TPR = D / (16 / (int)sizeof(T));
     const long long rows = (long long)p.B * p.Sq * p.Hq;
     const long long blocks = (rows + 256 / TPR - 1) / (256 / TPR);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D, WITH_D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1306,12 +1327,12 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
 #define TPA_BWD_TWO_PASS_DMA(D, NKW, OCC, NQW, QOCC)                                                  \
     {DT_BF16, D, BwdTile<bf16_t, D, NKW>::BN, BwdTile<bf16_t, D, NKW>::BM,                          \
      BwdTile<bf16_t, D, NKW>::LDS_BYTES, 0, &launch_bwd<bf16_t, D, NKW, OCC, false>,               \
-     &launch_bwd_pre<bf16_t, D>, nullptr, &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 1}
+     &launch_bwd_pre<bf16_t, D, false>, nullptr, &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 1}
 // both kernels on DMA'd tiles
 #define TPA_BWD_DMA(D, NKW, OCC, NQW, QOCC)                                                          \
     {DT_BF16, D, BwdKvDmaTile<D, NKW>::BN, BwdKvDmaTile<D, NKW>::BM,                               \
      BwdKvDmaTile<D, NKW>::LDS_BYTES, 0, &launch_bwd_dkdv_dma<D, NKW, OCC>,                       \
-     &launch_bwd_pre<bf16_t, D>, nullptr,                                                         \
+     &launch_bwd_pre<bf16_t, D, false>, nullptr,                                                  \
      &launch_bwd_dq_dma<D, NQW, QOCC>, BwdDqDmaTile<D, NQW>::BM, 2}
 
 static const BwdVariant kBwdVariants[] = {
@@ -1328,11 +1349,7 @@ static const BwdVariant kBwdVariants[] = {
     TPA_BWD_TWO_PASS_DMA(64, 16, 2, 1, 2),
     TPA_BWD_TWO_PASS_DMA(128, 16, 2, 2, 2),  // 128-row dQ blocks
     TPA_BWD_TWO_PASS_DMA(64, 16, 2, 2, 2),
-    // register-staged dQ kernel (the fp32 path's kernel), as an ablation for bf16
-    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 16, 2, 1, 2),
-    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 16, 2, 1, 2),
-    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 128, 32, 1, 2, 1),  // 128-key blocks
-    TPA_BWD_TWO_PASS(bf16_t, DT_BF16, 64, 32, 1, 2, 2),
+    // fp32: register-staged tiles (D from the fp32 forward output)
     TPA_BWD_TWO_PASS(float, DT_FP32, 128, 16, 1, 1, 1),
     TPA_BWD_TWO_PASS(float, DT_FP32, 64, 16, 1, 1, 2),
     // dQ by atomics (ablation)

@@ -44,6 +44,16 @@ __device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
     return u32x2{hi, lo};
 }
 
+// Eight fp32 values (a[0..3], then b[0..3]) as bf16 hi and lo parts, x ~= hi + lo
+// to about 16 significant bits, each packed in pairs in that order: the B operand
+// of a 16x16x32 bf16 MFMA twice over (one product with hi, one with lo).
+__device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, u32x4& hi, u32x4& lo) {
+    const u32x2 w0 = split_bf16x2(a[0], a[1]), w1 = split_bf16x2(a[2], a[3]);
+    const u32x2 w2 = split_bf16x2(b[0], b[1]), w3 = split_bf16x2(b[2], b[3]);
+    hi = u32x4{w0[0], w1[0], w2[0], w3[0]};
+    lo = u32x4{w0[1], w1[1], w2[1], w3[1]};
+}
+
 // Cross-lane moves without the LDS crossbar. v_permlane16_swap(v, v) returns a
 // pair whose elements are {v[l], v[l ^ 16]} in some order for every lane l (and
 // v_permlane32_swap likewise for l ^ 32), so combining the pair reduces over
