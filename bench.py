@@ -29,9 +29,14 @@ LLC_BYTES = 256 << 20       # MI355X Infinity Cache
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "tiled_prefill_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TIMES_FILE = os.path.join(ROOT, "profiles", "kernel_times.json")
 # kernel -> source file it is compiled from
 KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_decode_kdma_kernel": "attn_decode.hip",
-                  "attn_prefill_kernel": "attn_prefill.hip",
+                  "lse_combine_kernel": "attn_decode.hip", "lse_combine_cols_kernel": "attn_decode.hip",
+                  "lse_combine_cols_small_kernel": "attn_decode.hip",
+                  "lse_combine_rows_kernel": "attn_decode.hip",
+                  "attn_prefill_kernel": "attn_prefill.hip", "attn_fwd_kernel": "attn_fwd.hip",
+                  "attn_mla_kernel": "attn_mla.hip", "stream_read_kernel": "attn_tools.hip",
                   "attn_bwd_dkdv_dma_kernel": "attn_bwd.hip", "attn_bwd_dq_dma_kernel": "attn_bwd.hip"}
 
 
@@ -53,6 +58,14 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first copy a buffer of this many MiB three times (a plain copy "
                          "of known size, to calibrate HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", default=None, metavar="DIR",
+                    help="summarise the rocprofv3 kernel trace under DIR into "
+                         "profiles/kernel_trace_<workload>.md and profiles/kernel_times.json")
+    ap.add_argument("--rocprof-cmd", default="", help="with --summarize-rocprof: the command that made DIR")
+    ap.add_argument("--title", default="", help="with --summarize-rocprof: what the trace covers")
+    ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs (one DIR per pass) into "
+                         "profiles/counters_<workload>.md; --rocprof-cmd names each pass's command, '|'-separated")
     return ap.parse_args()
 
 
@@ -84,6 +97,127 @@ def traffic_for(kernel: str, workload: str):
     if not e or e.get("source_sha") != source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
+
+
+def kernel_time_for(kernel: str, workload: str):
+    """rocprofv3 kernel-trace durations (us: mean, median, ...) of a kernel on a
+    workload, if they were recorded for the current source of that kernel; else None."""
+    try:
+        rec = json.load(open(TIMES_FILE))
+    except (OSError, ValueError):
+        return None
+    e = rec.get(f"{kernel}:{workload}")
+    if not e or e.get("source_sha") != source_hash(kernel):
+        return None
+    return e
+
+
+def summarize_rocprof(args):
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace run (every
+    dispatch in the trace): a markdown summary under profiles/ and, for the
+    kernels bench.py reports, an entry in profiles/kernel_times.json keyed on the
+    kernel's source hash."""
+    import csv
+    import glob
+    import re
+    import statistics
+    files = glob.glob(os.path.join(args.summarize_rocprof, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no kernel_trace.csv under {args.summarize_rocprof}")
+    durs = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = re.sub(r"\(.*\)$", "", r["Kernel_Name"]).replace("void ", "").replace("tpa::", "")
+            durs.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in durs.values())
+    lines = [f"# Kernel trace: {args.title or args.workload}", "",
+             "command (from the repository root on one MI355X, TMPDIR=/tmp), then this summary:", "",
+             f"    {args.rocprof_cmd}",
+             f"    python3 bench.py --summarize-rocprof {args.summarize_rocprof} --workload {args.workload}",
+             "", "Durations in us over every dispatch of the run (warm-up and timed steps alike).", "",
+             "| kernel | calls | mean | median | p10 | p90 | min | max | share % |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    try:
+        times = json.load(open(TIMES_FILE))
+    except (OSError, ValueError):
+        times = {}
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        q = lambda f: v[min(len(v) - 1, int(f * len(v)))]
+        st = {"calls": len(v), "mean_us": round(statistics.fmean(v), 3),
+              "median_us": round(statistics.median(v), 3), "p10_us": round(q(0.1), 3),
+              "p90_us": round(q(0.9), 3), "min_us": round(v[0], 3), "max_us": round(v[-1], 3)}
+        lines.append(f"| {name} | {st['calls']} | {st['mean_us']:.2f} | {st['median_us']:.2f} | "
+                     f"{st['p10_us']:.2f} | {st['p90_us']:.2f} | {st['min_us']:.2f} | {st['max_us']:.2f} | "
+                     f"{100 * sum(v) / total:.1f} |")
+        base = name.split("<")[0]
+        if base in KERNEL_SOURCES:
+            times[f"{base}:{args.workload}"] = dict(st, kernel=name, source=KERNEL_SOURCES[base],
+                                                    source_sha=source_hash(base))
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{args.workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    json.dump(times, open(TIMES_FILE, "w"), indent=1, sort_keys=True)
+    print(out)
+
+
+def summarize_counters(args, num_cus=256, num_xcd=8):
+    """Per-kernel means of rocprofv3 --pmc counters (values summed over the GPU's
+    instances, averaged over a kernel's dispatches), plus derived shares:
+      cycles per XCD     = GRBM_GUI_ACTIVE / 8
+      MFMA busy          = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x 256 CUs x cycles per XCD)
+      VALU / MFMA per wave = SQ_INSTS_VALU / SQ_WAVES, SQ_INSTS_MFMA / SQ_WAVES
+      waiting            = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of wave lifetime)
+      VALU active        = SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES
+      LDS bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS"""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for d in args.summarize_counters:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name = re.sub(r"\(.*\)$", "", r["Kernel_Name"]).replace("void ", "").replace("tpa::", "")
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cmds = [c.strip() for c in args.rocprof_cmd.split("|") if c.strip()]
+    lines = [f"# Counters: {args.title or args.workload}", "",
+             "commands (from the repository root on one MI355X, TMPDIR=/tmp; one pass each), then this summary:", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += [f"    python3 bench.py --summarize-counters {' '.join(args.summarize_counters)} "
+              f"--workload {args.workload}", "",
+              "Mean per dispatch of each counter (summed over the GPU). Derived: cycles per XCD = "
+              "GRBM_GUI_ACTIVE / 8; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 x 256 x cycles per XCD); "
+              "per wave = SQ_INSTS_* / SQ_WAVES; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES; VALU active = "
+              "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES; LDS conflicts = SQ_LDS_BANK_CONFLICT / "
+              "SQ_ACTIVE_INST_LDS.", ""]
+    mean = lambda v: sum(v) / len(v)
+    for name, cs in sorted(vals.items()):
+        if name.startswith("__amd"):
+            continue
+        m = {c: mean(v) for c, v in cs.items()}
+        lines += [f"## {name}", "", "| counter | dispatches | mean |", "|---|---|---|"]
+        lines += [f"| {c} | {len(cs[c])} | {m[c]:.6g} |" for c in sorted(m)]
+        der = []
+        if "GRBM_GUI_ACTIVE" in m:
+            cyc = m["GRBM_GUI_ACTIVE"] / num_xcd
+            der.append(f"cycles per XCD {cyc:.4g}")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                der.append(f"MFMA busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * num_cus * cyc):.1f}%")
+        if "SQ_WAVES" in m and m["SQ_WAVES"] > 0:
+            for c, lab in (("SQ_INSTS_VALU", "VALU"), ("SQ_INSTS_MFMA", "MFMA"), ("SQ_INSTS_LDS", "LDS"),
+                           ("SQ_INSTS_VMEM_RD", "VMEM reads")):
+                if c in m:
+                    der.append(f"{lab} per wave {m[c] / m['SQ_WAVES']:.1f}")
+        if "SQ_WAVE_CYCLES" in m and m["SQ_WAVE_CYCLES"] > 0:
+            for c, lab in (("SQ_WAIT_ANY", "waiting"), ("SQ_ACTIVE_INST_VALU", "VALU active"),
+                           ("SQ_WAIT_INST_LDS", "waiting on LDS")):
+                if c in m:
+                    der.append(f"{lab} {100 * m[c] / m['SQ_WAVE_CYCLES']:.1f}% of wave cycles")
+        if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_ACTIVE_INST_LDS", 0) > 0:
+            der.append(f"LDS conflicts {m['SQ_LDS_BANK_CONFLICT'] / m['SQ_ACTIVE_INST_LDS']:.3f} per LDS active cycle")
+        lines += ["", "derived: " + "; ".join(der), ""]
+    out = os.path.join(ROOT, "profiles", f"counters_{args.workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
 
 
 def warm(step, n_steps, min_seconds=0.3):
@@ -287,6 +421,12 @@ def run_latent_suite(args):
 
 def main():
     args = parse()
+    if args.summarize_rocprof:
+        summarize_rocprof(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(every workload fits one MI355X); run with --gpus 1", file=sys.stderr)
@@ -363,6 +503,23 @@ def main():
         out["decode"] = dict(value=value, ms_per_step=ms, fwd_ms=fwd_ms, combine_ms=comb_ms,
                              achieved=achieved, traffic=traffic, n_rot=n_rot, step_us=pct)
         del ks, vs, q, k, v
+        # the reference: a plain streaming read of the same bytes (one launch of 512
+        # workgroups with the decode kernel's 16-byte non-temporal loads), rotated
+        # over as many buffers and timed the same way as the decode steps
+        bufs = [torch.empty(kv_bytes, dtype=torch.uint8, device=dev) for _ in range(n_rot)]
+        sink = torch.zeros(512, dtype=torch.int32, device=dev)
+
+        def sstep(i):
+            tpa.stream_read(bufs[i % n_rot], sink, 512)
+
+        warm(sstep, args.warmup)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            sstep(i)
+        torch.cuda.synchronize()
+        sdt = (time.perf_counter() - t0) / args.steps
+        out["stream"] = dict(GBps=kv_bytes / sdt / 1e9, us=sdt * 1e6)
+        del bufs
 
     # ----------------------------------------------------------------- prefill
     wp = WORKLOADS["causal_prefill_bf16"]
@@ -500,7 +657,17 @@ def main():
                             "traffic": dec["traffic"],
                             "avg_launch_ms": round(dec["fwd_ms"], 5),
                             "combine_avg_launch_ms": round(dec["combine_ms"], 5)}
+        kt = kernel_time_for(DECODE_KERNEL, w.name)
+        if kt:  # the same fraction from the committed rocprofv3 kernel trace
+            line["roofline"]["rocprof_median_us"] = kt["median_us"]
+            line["roofline"]["frac_rocprof"] = round(
+                (kv_bytes + q_bytes) / (kt["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         line["step_us"] = dec["step_us"]
+        st = out.get("stream")
+        if st:
+            line["stream_read"] = {"GBps": round(st["GBps"], 1), "us_per_read": round(st["us"], 2),
+                                   "pct_of_hbm_peak": round(100 * st["GBps"] / HBM_PEAK_GBS, 2),
+                                   "decode_step_vs_stream_read": round(dec["value"] / st["GBps"], 4)}
     if pre:
         line["prefill"] = {
             "metric": "causal prefill TFLOP/s", "value": round(pre["value"], 2),
@@ -515,6 +682,11 @@ def main():
                          "traffic": traffic_for("attn_prefill_kernel", wp.name),
                          "avg_launch_ms": round(pre["fwd_ms"], 4)},
         }
+        kt = kernel_time_for("attn_prefill_kernel", wp.name)
+        if kt:
+            line["prefill"]["roofline"]["rocprof_median_us"] = kt["median_us"]
+            line["prefill"]["roofline"]["frac_rocprof"] = round(
+                flops / (kt["median_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
     bwd = out.get("backward")
     if bwd:
         # counter bytes of the two matrix kernels together, when both are recorded

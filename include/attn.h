@@ -47,11 +47,12 @@
  *     that use it must not overlap (issue them on one stream, or order the
  *     streams, or bind one workspace per stream).
  *   Numerics: scores scale * q.k must be finite in fp32 (fp32 accumulation).
- *     Every finite bf16 value of v is handled: the bf16 prefill and latent
- *     kernels compute P.V on fp16 operands (P and V rounded to fp16) and, when
- *     a V element lies beyond fp16's range (|v| > 65504), run that tile again
- *     with bf16 V and P as two bf16 parts. Non-finite inputs give unspecified
- *     (non-finite) outputs.
+ *     Every finite bf16 value of v is handled: the bf16 prefill kernel
+ *     computes P.V on fp16 operands (P and V rounded to fp16) and, when a V
+ *     element of a tile lies beyond fp16's range (|v| > 65504), runs that tile
+ *     again with bf16 V and P as two bf16 parts (the decode and latent kernels
+ *     always take that form). Non-finite inputs give unspecified (non-finite)
+ *     outputs.
  *   Errors: a negative status code; nothing is launched and the message is
  *     available from attn_last_error() (thread-local). Argument checks never
  *     touch the GPU.
@@ -108,8 +109,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* attn_fwd for callers that cannot allocate (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
- * kernels and results as attn_fwd; its scratch (split partials, per-tile
- * flags, tile counters) is a static device array of ATTN_NOALLOC_SCRATCH_BYTES
+ * kernels and results as attn_fwd; its scratch (split partials, tile
+ * counters) is a static device array of ATTN_NOALLOC_SCRATCH_BYTES
  * in the library, one per device, held from the library's load until the
  * process ends. The call allocates nothing and ignores attn_set_workspace. A
  * problem whose plan needs more scratch (workspace_bytes of attn_plan_fwd)
@@ -252,17 +253,16 @@ int attn_num_splits_occupancy(int tiles, int num_cus, int n_blocks, int block_n,
 int attn_profile_begin(int max_launches);
 int attn_profile_end(double* fwd_ms, int* fwd_launches, double* combine_ms,
                        int* combine_launches, double* prep_ms, int* prep_launches);
-/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 7) with
+/* Same, for every kind: ms[k], launches[k] for k < n_kinds (at most 6) with
  * kinds 0 forward, 1 combine, 2 tile counter reset, 3 backward
- * key-block kernel, 4 backward pre- and post-passes, 5 backward dQ kernel,
- * 6 the bf16 fix-up pass of the prefill kernel (tiles whose V overflowed fp16). */
+ * key-block kernel, 4 backward pre- and post-passes, 5 backward dQ kernel. */
 int attn_profile_end_kinds(double* ms, int* launches, int n_kinds);
 
 /* Caller-owned scratch ([Occupancy], "The Fix": the split partials live in a
  * global scratch buffer). Binds dev_ptr[0, bytes) -- device memory of the
  * device the calls run on, 256-byte aligned -- to the calling host thread:
- * later calls from this thread put their split partials, per-tile flags, the
- * backward's row sums and tile counters there, and never allocate or
+ * later calls from this thread put their split partials, the backward's row
+ * sums and tile counters there, and never allocate or
  * synchronise. A call that needs more than `bytes` (the workspace_bytes of its
  * plan: attn_plan_fwd, attn_plan_fwd_dv, attn_plan_bwd) returns ATTN_EINVAL
  * and launches nothing. dev_ptr NULL or bytes 0 unbinds (back to the
@@ -283,6 +283,15 @@ int attn_set_workspace(void* dev_ptr, size_t bytes);
  * ATTN_EINVAL. */
 int attn_set_option(const char* name, int value);
 int attn_get_option(const char* name, int* value);
+
+/* Measurement aid (not part of the attention path): reads [buf, buf + bytes)
+ * of device memory once with the 16-byte non-temporal loads the decode kernel
+ * streams K and V with, over `workgroups` workgroups of 256 threads (<= 0:
+ * 512, the decode grid of the GQA decode workload), and writes almost nothing
+ * (sink: device uint32[workgroups], written only for one improbable value).
+ * The reference rate for the decode kernel's HBM bandwidth. buf 16-byte
+ * aligned, bytes a multiple of 16; errors ATTN_EINVAL, ATTN_EHIP. */
+int attn_stream_read(const void* buf, size_t bytes, int workgroups, void* sink, void* stream);
 
 /* Message of the last failure on this thread ("" if none). */
 const char* attn_last_error(void);

@@ -185,3 +185,12 @@ def test_noalloc_refuses_a_problem_beyond_its_static_scratch():
                               0.088, 256, tpa.BF16, None)
     assert rc == -1
     assert "noalloc" in lib.attn_last_error().decode()
+
+
+def test_stream_read_rejects_bad_buffers():
+    lib = tpa.load()
+    assert lib.attn_stream_read(None, 1024, 0, FAKE, None) == -1
+    assert lib.attn_stream_read(FAKE, 1000, 0, FAKE, None) == -1       # not a multiple of 16
+    assert lib.attn_stream_read(FAKE + 4, 1024, 0, FAKE, None) == -1   # misaligned
+    assert lib.attn_stream_read(FAKE, 1 << 34, 4, FAKE, None) == -1    # > 2 GiB per workgroup
+    assert lib.attn_stream_read(FAKE, 0, 0, FAKE, None) == 0           # nothing to read

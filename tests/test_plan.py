@@ -160,8 +160,7 @@ def test_persistent_grid_is_resident_workgroups(attn_options):
     assert tiles < 256 and p["grid_x"] == -(-tiles // 8) * 8
     attn_options("ATTN_PREFILL_PERSIST", "0")
     p = tpa.plan(1, 32, 32, 8192, 8192, 128, causal=True, num_cus=256)
-    # one fp16-overflow flag per tile (the bf16 form reruns flagged tiles)
-    assert p["grid_x"] == 1024 and p["workspace_bytes"] == 1024 * 4
+    assert p["grid_x"] == 1024 and p["workspace_bytes"] == 0
 
 
 # ---------------------------------------------------------------------------

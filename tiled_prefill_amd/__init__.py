@@ -113,6 +113,8 @@ def load():
     lib.attn_plan_bwd.restype = i
     lib.attn_m_block_range.argtypes = [i, i, i, i, i, i, i, ip, ip]
     lib.attn_m_block_range.restype = i
+    lib.attn_stream_read.argtypes = [vp, ctypes.c_size_t, i, vp, vp]
+    lib.attn_stream_read.restype = i
     lib.attn_set_workspace.argtypes = [vp, ctypes.c_size_t]
     lib.attn_set_workspace.restype = i
     lib.attn_set_option.argtypes = [ctypes.c_char_p, i]
@@ -367,6 +369,14 @@ def num_splits_occupancy(tiles, num_cus, n_blocks, block_n, min_chunk_rows=256, 
                                                   min_chunk_rows, wg_per_cu))
 
 
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, stream=None):
+    """attn_stream_read: read a GPU buffer once (the streaming-read reference)."""
+    if not (buf.is_cuda and buf.is_contiguous() and sink.is_cuda):
+        raise ValueError("buf and sink must be GPU tensors")
+    _check(load().attn_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                   int(workgroups), sink.data_ptr(), _stream_ptr(stream)))
+
+
 def set_workspace(buf: Optional[torch.Tensor]):
     """Bind a caller-owned GPU workspace (any dtype, 256-byte aligned) to this host
     thread (attn_set_workspace); None unbinds. The caller keeps `buf` alive while
@@ -413,7 +423,7 @@ def profile_begin(max_launches: int = 4096):
     _check(load().attn_profile_begin(int(max_launches)))
 
 
-KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost", "bwd_dq", "fix")
+KINDS = ("fwd", "combine", "prep", "bwd", "bwd_prepost", "bwd_dq")
 
 
 def profile_end_kinds() -> dict:

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 
 SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_prefill.hip", "attn_mla.hip", "attn_bwd.hip",
-           "attn_scratch.hip", "attn_api.cpp"]
+           "attn_scratch.hip", "attn_tools.hip", "attn_api.cpp"]
 HEADERS = ["attn_plan.h", "attn_kernels.h", "attn_device.h"]
 
 HIPCC_FLAGS = [

@@ -225,8 +225,6 @@ struct Plan {
     attn_plan_t pub;
     const FwdVariant* var;
     size_t ctr_offset = 0;  // byte offset of the persistent kernels' tile counters
-    size_t flag_offset = 0; // byte offset of the per-tile fp16-overflow flags
-    int fix_grid = 0;       // workgroups of the bf16 form over flagged tiles (0: none)
 };
 
 int make_plan(const Problem& p, int num_cus, Plan* out) {
@@ -399,17 +397,6 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     size_t ws = S > 1 ? attn_workspace_bytes(p.B, p.Hq, p.Sq, dv, S) : 0;
     out->ctr_offset = (ws + 255) & ~(size_t)255;
     if (var->persistent > 0) ws = out->ctr_offset + 256;  // one tile counter per XCD
-    // kernels with fp16 P.V operands: one overflow flag per tile, and the bf16
-    // form's grid (one workgroup per CU at most)
-    out->flag_offset = (ws + 255) & ~(size_t)255;
-    out->fix_grid = 0;
-    if (var->launch_fix) {
-        const long long total = (long long)p.B * q.grid_heads * S * q.num_m_blocks;
-        if (total > 0) {
-            ws = out->flag_offset + (size_t)total * sizeof(int);
-            out->fix_grid = (int)std::min<long long>(total, num_cus);
-        }
-    }
     q.workspace_bytes = ws;
     out->var = var;
     return ATTN_OK;
@@ -503,8 +490,7 @@ struct Profiler {
     std::vector<hipEvent_t> ev;  // pairs
     std::vector<int> kind;       // 0 forward, 1 combine, 2 tile counter reset,
                                  // 3 backward key-block kernel, 4 backward pre/post
-                                 // passes, 5 backward dQ kernel, 6 the bf16 fix-up
-                                 // of the fp16 P.V kernels
+                                 // passes, 5 backward dQ kernel
     int used = 0;
 } g_prof;
 
@@ -614,20 +600,10 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
         if (e != hipSuccess) return fail(ATTN_EHIP, "tile counter reset: %s", hipGetErrorString(e));
     }
 
-    if (plan.fix_grid > 0)
-        fp.tile_flags = reinterpret_cast<int*>(static_cast<char*>(ws.ptr) + plan.flag_offset);
-
     slot = prof_start(0, stream);
     e = plan.var->launch(fp, grid, stream);
     prof_stop(slot, stream);
     if (e != hipSuccess) return fail(ATTN_EHIP, "forward launch: %s", hipGetErrorString(e));
-    if (plan.fix_grid > 0) {
-        // tiles whose V overflowed fp16, again in the bf16 form (before the combine)
-        slot = prof_start(6, stream);
-        e = plan.var->launch_fix(fp, dim3(plan.fix_grid), stream);
-        prof_stop(slot, stream);
-        if (e != hipSuccess) return fail(ATTN_EHIP, "bf16 fix-up launch: %s", hipGetErrorString(e));
-    }
     if (pl.num_splits == 1) return ATTN_OK;
 
     CombineParams cp{};
@@ -956,8 +932,8 @@ int attn_profile_begin(int max_launches) {
 
 int attn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
-    double t[7] = {0, 0, 0, 0, 0, 0, 0};
-    int n[7] = {0, 0, 0, 0, 0, 0, 0};
+    double t[6] = {0, 0, 0, 0, 0, 0};
+    int n[6] = {0, 0, 0, 0, 0, 0};
     for (int i = 0; i < g_prof.used; ++i) {
         if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) continue;
         float e_ms = 0.f;
@@ -971,7 +947,7 @@ int attn_profile_end_kinds(double* ms, int* launches, int n_kinds) {
     g_prof.kind.clear();
     g_prof.on = false;
     g_prof.used = 0;
-    for (int k = 0; k < n_kinds && k < 7; ++k) {
+    for (int k = 0; k < n_kinds && k < 6; ++k) {
         if (ms) ms[k] = t[k];
         if (launches) launches[k] = n[k];
     }
@@ -1002,6 +978,21 @@ int attn_set_workspace(void* dev_ptr, size_t bytes) {
     }
     u.ptr = dev_ptr;
     u.bytes = bytes;
+    return ATTN_OK;
+}
+
+int attn_stream_read(const void* buf, size_t bytes, int workgroups, void* sink, void* stream) {
+    if (bytes == 0) return ATTN_OK;
+    if (!buf || !sink) return fail(ATTN_EINVAL, "null buffer or sink");
+    if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+        return fail(ATTN_EINVAL, "the buffer must be 16-byte aligned and a multiple of 16 bytes long");
+    if (bytes > ((size_t)1 << 40)) return fail(ATTN_EINVAL, "buffer too large");
+    if (workgroups <= 0) workgroups = 512;
+    if (workgroups > (1 << 20)) return fail(ATTN_EINVAL, "workgroups=%d", workgroups);
+    if (bytes / (size_t)workgroups >= ((size_t)1 << 31))
+        return fail(ATTN_EINVAL, "more than 2 GiB per workgroup; use more workgroups");
+    const hipError_t e = launch_stream_read(buf, bytes, workgroups, sink, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_EHIP, "stream read launch: %s", hipGetErrorString(e));
     return ATTN_OK;
 }
 

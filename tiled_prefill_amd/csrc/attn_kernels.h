@@ -21,9 +21,6 @@ struct FwdVariant {
     int persistent;         // > 0: persistent workgroups (this many per CU) over tile queues
     int dv;                 // value / output width when it differs from d (0: equal to d)
     int kdma;               // decode kernels: 1 = K through LDS in 32-key halves, 0 = K into registers
-    // kernels that compute P.V on fp16 operands: the bf16 form over the tiles
-    // they flag in FwdParams::tile_flags (null for kernels without flags)
-    hipError_t (*launch_fix)(const FwdParams&, dim3 grid, hipStream_t stream);
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
@@ -54,6 +51,10 @@ const BwdVariant* bwd_variants();  // null-terminated by launch == nullptr
 
 // The log-sum-exp combine of split partials.
 hipError_t launch_combine(const CombineParams& p, int d, int out_bf16, hipStream_t stream);
+
+// A plain streaming read of [buf, buf + bytes) over `workgroups` workgroups
+// (measurement aid, attn_tools.hip); sink is device uint32[workgroups].
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, void* sink, hipStream_t stream);
 
 // The static device scratch of attn_fwd_noalloc (attn_scratch.hip): its size,
 // and the address of the current device's copy (read once per device).

@@ -140,8 +140,6 @@ struct FwdParams {
     int lpt;                // reverse query-block order (heaviest causal blocks first)
     int split_major;        // grid y = split * grid_heads + head (else head * splits + split)
     int* tile_counters;     // persistent kernels: one tile queue counter per XCD, zero at launch
-    int* tile_flags;        // fp16 P.V kernels: per tile, 1 if its V overflowed fp16 (then the
-                            // bf16 form reruns it), written for every tile on every launch
     // Decode tiles of fixed-length problems (seqlens_k null): the key-block
     // range of the single query block and its blocks per split, computed once
     // on the host. blockIdx.y / y_div (y_div = grid_heads when split_major, else

@@ -72,12 +72,11 @@ struct PrefillTile {
     }
 };
 
-template <int D, int NWV, int MW, int PRI, int PERSIST = 0, int VBF = 0>
+template <int D, int NWV, int MW, int PRI, int PERSIST = 0>
 __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_kernel(FwdParams p) {
     constexpr bool PRIO = PRI != 0;
-    constexpr bool VB = VBF != 0;
     using C = PrefillTile<D, NWV, MW>;
-    constexpr int BN = C::BN, BM = C::BM, NQ = C::NQ, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
+    constexpr int BN = C::BN, BM = C::BM, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
     constexpr int CPR = C::CPR, ROWB = C::ROWB, TILEB = C::TILEB, STAGEB = C::STAGEB;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
@@ -89,14 +88,18 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     const int M = p.num_m_blocks, S = p.num_splits;
     const int total = p.B * p.grid_heads * S * M;
     const int per_xcd = (total + NUM_XCD - 1) / NUM_XCD;
-    // run_tile(t) computes tile t. VB == 0 (the fast form): V converted to fp16;
-    // when the O accumulators come out non-finite -- a V element beyond fp16's
-    // range (|v| > 65504) became +-inf -- it writes nothing but the tile's flag
-    // in p.tile_flags, and the bf16 form runs the tile again. VB == 1 (that
-    // form): V kept in bf16 and P split into bf16 hi + lo parts, exact for any
-    // finite bf16 V; it runs the flagged tiles only.
+    // run_tile(t, vbf16, nq, q0) computes tile t for the 16-row column blocks q0
+    // .. q0 + nq - 1 of every wave's MW rows. The fast form (vbf16 false, all
+    // C::NQ blocks at once) converts V to fp16; when its O accumulators come out
+    // non-finite -- a V element beyond fp16's range (|v| > 65504) became +-inf
+    // -- it writes nothing and returns true, and the tile runs again in the
+    // bf16 form (vbf16 true): V kept in bf16 and P split into bf16 hi + lo parts,
+    // exact for any finite bf16 V, one column block at a time so that it needs
+    // fewer registers than the fast form and the kernel none beyond them.
     __shared__ int s_bad;
-    auto run_tile = [&](const int t) {
+    auto run_tile = [&](const int t, auto vbf16, auto nqc, const int q0) -> bool {
+    constexpr bool VB = decltype(vbf16)::value;
+    constexpr int NQ = decltype(nqc)::value;
     int rest = t / M;
     const int m_rev = t % M;
     const int m_block = p.lpt ? M - 1 - m_rev : m_rev;
@@ -125,7 +128,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     int wlo = -0x7fffffff, whi = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int r = m_block * BM + wave * MW + 16 * q + li;
+        const int r = m_block * BM + wave * MW + 16 * (q0 + q) + li;
         const bool ok = r < nrows;
         const int pos = ok ? (p.pack ? r / G : r) : 0;
         const int head = p.pack ? hkv * G + (ok ? r % G : 0) : hg;
@@ -468,8 +471,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             for (int q = 0; q < NQ; ++q) chk += (oacc[u][q][0] + oacc[u][q][1]) + (oacc[u][q][2] + oacc[u][q][3]);
         if (__builtin_amdgcn_ballot_w64(!(__builtin_fabsf(chk) <= 3.0e38f)) != 0 && lane == 0) s_bad = 1;
         __syncthreads();
-        if (tid == 0) p.tile_flags[t] = s_bad;
-        if (s_bad) return;
+        if (s_bad) return true;
     }
     const bool split_out = S > 1;
 #pragma unroll
@@ -500,17 +502,18 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             }
         }
     }
+    return false;
+    };
+    auto run = [&](const int t) {
+        if (run_tile(t, std::false_type{}, std::integral_constant<int, C::NQ>{}, 0))
+            for (int q0 = 0; q0 < C::NQ; ++q0) run_tile(t, std::true_type{}, std::integral_constant<int, 1>{}, q0);
     };
 
-    if constexpr (VB) {
-        // the tiles the fast form flagged, strided over the workgroups
-        for (int t = blockIdx.x; t < total; t += gridDim.x)
-            if (p.tile_flags[t]) run_tile(t);
-    } else if constexpr (PERSIST == 0) {
+    if constexpr (PERSIST == 0) {
         // one tile per workgroup; workgroups are dealt round-robin to the 8 XCDs,
         // so tile t of section blockIdx % 8 lands on that XCD
         const int t = ((int)blockIdx.x % NUM_XCD) * per_xcd + (int)blockIdx.x / NUM_XCD;
-        if (t < total) run_tile(t);
+        if (t < total) run(t);
     } else {
         // persistent: each workgroup pops tiles from its own XCD's queue (an
         // atomic counter per section, zeroed before the launch), then from the
@@ -541,7 +544,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             const int t = s_next;
             __syncthreads();  // all waves have read s_next before thread 0 overwrites it
             if (t < 0) break;
-            run_tile(t);
+            run(t);
         }
     }
 }
@@ -559,35 +562,26 @@ template <int D, int NWV, int MW, int PRI = 1, int PERSIST = 0>
 hipError_t launch_prefill(const FwdParams& p, dim3 grid, hipStream_t stream) {
     // grid: one dimension over every tile (persistent: over the resident
     // workgroups), padded to a multiple of the XCD count
-    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW, PRI, PERSIST, 0>), grid, dim3(64 * NWV), 0, stream, p);
-    return hipGetLastError();
-}
-
-// The bf16 form over the tiles the fast form flagged: one workgroup per CU at
-// most, each striding over the tile flags (with none set, every workgroup only
-// reads its flags and leaves).
-template <int D, int NWV, int MW>
-hipError_t launch_prefill_fix(const FwdParams& p, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW, 0, 0, 1>), grid, dim3(64 * NWV), 0, stream, p);
+    hipLaunchKernelGGL((attn_prefill_kernel<D, NWV, MW, PRI, PERSIST>), grid, dim3(64 * NWV), 0, stream, p);
     return hipGetLastError();
 }
 
 const FwdVariant* prefill_variants() {
     static const FwdVariant v[] = {
         // one 8-wave workgroup per CU: K/V tiles shared by 256 rows
-        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 0>, 1, 0, 0, 0, &launch_prefill_fix<128, 8, 32>},
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 0>, 1},
         // ablation: raised wave priority around the MFMA phases (measured slower)
-        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 1>, 1, 0, 0, 0, &launch_prefill_fix<128, 8, 32>},
-        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32, 0>, 1, 0, 0, 0, &launch_prefill_fix<64, 8, 32>},
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 1>, 1},
+        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32, 0>, 1},
         // two 4-wave workgroups per CU (independent barriers): the default with a
         // sliding window, an ablation otherwise
-        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0>, 1, 0, 0, 0, &launch_prefill_fix<128, 4, 32>},
-        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0>, 1, 0, 0, 0, &launch_prefill_fix<64, 4, 32>},
+        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0>, 1},
+        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0>, 1},
         // persistent workgroups with per-XCD tile queues
-        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 0, 1>, 1, 1, 0, 0, &launch_prefill_fix<128, 8, 32>},
-        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0, 1>, 1, 2, 0, 0, &launch_prefill_fix<128, 4, 32>},
-        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32, 0, 1>, 1, 1, 0, 0, &launch_prefill_fix<64, 8, 32>},
-        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0, 1>, 1, 2, 0, 0, &launch_prefill_fix<64, 4, 32>},
+        {DT_BF16, 128, 256, 64, 8, 1, PrefillTile<128, 8, 32>::LDS_BYTES, &launch_prefill<128, 8, 32, 0, 1>, 1, 1},
+        {DT_BF16, 128, 128, 64, 4, 1, PrefillTile<128, 4, 32>::LDS_BYTES, &launch_prefill<128, 4, 32, 0, 1>, 1, 2},
+        {DT_BF16, 64, 256, 64, 8, 1, PrefillTile<64, 8, 32>::LDS_BYTES, &launch_prefill<64, 8, 32, 0, 1>, 1, 1},
+        {DT_BF16, 64, 128, 64, 4, 1, PrefillTile<64, 4, 32>::LDS_BYTES, &launch_prefill<64, 4, 32, 0, 1>, 1, 2},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;
