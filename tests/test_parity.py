@@ -95,9 +95,38 @@ def test_verify_page_shapes_fp32(B, H, q_len, kv_len):
                                   (2, 4, 4, 20, 300, 64, False, -1, 0), (1, 4, 1, 5, 77, 128, True, 2, 2),
                                   (1, 2, 2, 32, 129, 64, True, 40, 1)])
 def test_verify_tile_choices_fp32(tile, case, attn_options):
-    # the other tiles the planner can pick for <= 32 query rows per KV head
+    # the general kernel's other tiles for <= 32 query rows per KV head (the
+    # planner's default there is the LDS-copy kernel, switched off here)
+    attn_options("ATTN_F32_DMA", 0)
     attn_options("ATTN_VERIFY_TILE", tile)
     run_case("fp32", *case, seed=4)
+
+
+F32_LDS_CASES = [
+    # dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl, S: the fp32 kernel that copies K/V
+    # into per-wave LDS stages (<= 32 query rows per KV head)
+    ("fp32", 2, 16, 16, 17, 2065, 128, True, -1, 0),   # the verify workload's shape
+    ("fp32", 1, 4, 4, 32, 100, 128, True, -1, 0),      # exactly 32 rows
+    ("fp32", 1, 8, 2, 4, 333, 128, True, -1, 0),       # GQA packed: 16 rows
+    ("fp32", 1, 4, 2, 9, 521, 64, True, 30, 3),        # packed 18 rows, window, d 64
+    ("fp32", 2, 6, 3, 1, 77, 128, False, -1, 2),       # decode, ragged last block
+    ("fp32", 1, 2, 2, 30, 20, 128, True, -1, 1),       # Sq > Sk: fully masked rows
+    ("fp32", 1, 2, 1, 3, 5, 64, False, 1, 1),          # fewer keys than one block
+    ("fp32", 1, 4, 4, 5, 1000, 128, False, -1, 37),    # many splits, empty ones
+    ("fp32", 1, 4, 4, 5, 1000, 64, True, 100, 0),
+    ("fp32", 3, 4, 4, 12, 4100, 128, False, -1, 1),    # one split: many blocks per wave
+]
+
+
+@pytest.mark.parametrize("waves", [8, 4])  # d 128: 8 waves with one stage each; 4 waves with two
+@pytest.mark.parametrize("case", F32_LDS_CASES)
+def test_f32_lds_kernel_shapes(case, waves, attn_options):
+    attn_options("ATTN_F32_DMA", 2)  # decode's row counts too
+    attn_options("ATTN_F32_WAVES", waves)
+    if waves == 4 and case[6] == 64:
+        pytest.skip("d 64 has only the 4-wave form")
+    assert tpa.plan(*case[1:7], case[7], case[8], case[9], "fp32")["block_n"] == 16  # that kernel
+    run_case(*case, seed=8)
 
 
 SMALL = [

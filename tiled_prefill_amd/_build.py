@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_prefill.hip", "attn_mla.hip", "attn_bwd.hip",
+SOURCES = ["attn_fwd.hip", "attn_fwd_f32.hip", "attn_decode.hip", "attn_prefill.hip", "attn_mla.hip", "attn_bwd.hip",
            "attn_scratch.hip", "attn_tools.hip", "attn_api.cpp"]
 HEADERS = ["attn_plan.h", "attn_kernels.h", "attn_device.h"]
 

@@ -65,6 +65,8 @@ const OptionDef kOptionDefs[] = {
     {"ATTN_PREFILL_PERSIST", &Options::prefill_persist, 0},
     {"ATTN_PREFILL_SKIP", &Options::prefill_skip, 0},
     {"ATTN_VERIFY_TILE", &Options::verify_tile, 1},
+    {"ATTN_F32_DMA", &Options::f32_dma, 1},
+    {"ATTN_F32_WAVES", &Options::f32_waves, 8},
     {"ATTN_MIN_CHUNK", &Options::min_chunk, 256},
     {"ATTN_WG_PER_CU", &Options::wg_per_cu, 2},
     {"ATTN_SPLIT_RULE", &Options::split_rule, 0},
@@ -278,11 +280,21 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
                 break;
             }
     }
+    const int head_rows = G > 1 ? p.Sq * G : p.Sq;
+    // fp32 with at most 32 (packed) query rows per KV head (decode, speculative
+    // verify): the kernel that copies K/V into per-wave LDS stages
+    // (ATTN_F32_DMA: 1 = for 17..32 rows, 2 = also for decode's 1..16 rows;
+    // ATTN_F32_WAVES: 8 = one LDS stage per wave where d has that form, 4 = two)
+    if (!var && p.dtype == ATTN_FP32 && head_rows <= 32 && (opt.f32_dma == 2 || (opt.f32_dma == 1 && !decode)))
+        for (const FwdVariant* v = f32_dma_variants(); v->launch; ++v)
+            if (v->d == p.d && (opt.f32_waves == 8 || v->waves_n == 4)) {
+                var = v;
+                break;
+            }
     // general tile kernel: decode tiles (16 rows) for decode, 32-row tiles when a
     // KV head's query rows (packed) are at most 32, else the widest row tile
     // (ATTN_VERIFY_TILE: 0 = widest row tile, 1 = 32-row tile over 2 x 2 waves,
     // 2 = 32-row tile over 2 x 4 waves with 128-key tiles)
-    const int head_rows = G > 1 ? p.Sq * G : p.Sq;
     const int verify_tile = opt.verify_tile;
     const int want_bm = decode ? 16 : (head_rows <= 32 && verify_tile ? 32 : 0);
     const int want_wn = want_bm == 32 ? (verify_tile == 2 ? 4 : 2) : 0;

@@ -29,6 +29,7 @@ const FwdVariant* fwd_variants();
 const FwdVariant* decode_variants();
 const FwdVariant* prefill_variants();
 const FwdVariant* mla_variants();   // values of their own width (d_v != d)
+const FwdVariant* f32_dma_variants();  // fp32, <= 32 query rows per KV head, K/V copied into LDS
 
 // Zeroes the per-XCD tile queue counters of a persistent kernel.
 hipError_t launch_tile_counters_reset(int* counters, hipStream_t stream);
@@ -75,6 +76,8 @@ struct Options {
     int prefill_persist;  // ATTN_PREFILL_PERSIST=1: persistent workgroups over per-XCD queues
     int prefill_skip;     // ATTN_PREFILL_SKIP=n: the n-th later matching prefill variant
     int verify_tile;      // ATTN_VERIFY_TILE: 0 widest row tile, 1 32-row 2x2, 2 32-row 2x4
+    int f32_dma;          // ATTN_F32_DMA: fp32 on the LDS-copy kernel for 17..32 rows per KV head (1), for 1..32 (2)
+    int f32_waves;        // ATTN_F32_WAVES: that kernel's 8-wave form where d has one (8), else 4 waves
     int min_chunk;        // ATTN_MIN_CHUNK: minimum keys per split (256)
     int wg_per_cu;        // ATTN_WG_PER_CU: workgroup target per CU of the split rule (2)
     int split_rule;       // ATTN_SPLIT_RULE: 0 occupancy, 1 [FA-tiling] 5.2, 2 NSPLIT, 3 occupancy first
