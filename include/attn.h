@@ -93,6 +93,8 @@ typedef struct attn_plan_t {
     int lds_bytes;       /* LDS per workgroup                                               */
     int num_cus;         /* compute units the split rule assumed                            */
     int lpt;             /* 1: query blocks launched heaviest first ([FA-tiling] §4.4)      */
+    int work_units;      /* > 0: variable-length decode grid of this many (sequence, split)
+                            units per KV head (grid_x), none for a split a sequence lacks */
     long long visited_blocks;  /* key blocks all tiles visit (fixed-length problems)        */
     size_t workspace_bytes;    /* split partials needed (0 when num_splits == 1)           */
 } attn_plan_t;

@@ -272,6 +272,38 @@ def test_varlen_small():
         assert_parity(o, lse, ro, rl, "bf16", f"varlen S={S}")
 
 
+@pytest.mark.parametrize("units", [1, 0], ids=["unit_grid", "split_grid"])
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, Sq, Sk, d, causal, wl, lengths seed, sum given
+    (5, 8, 2, 1, 700, 128, False, -1, 1, "exact"),
+    (70, 8, 2, 1, 300, 128, False, -1, 2, "exact"),     # more sequences than lanes: two scan steps
+    (70, 8, 2, 1, 300, 64, False, -1, 3, "none"),       # no sum: B x S units
+    (9, 16, 2, 2, 900, 128, True, -1, 4, "exact"),      # two positions x 8 heads per tile, causal
+    (9, 8, 2, 1, 900, 128, False, 200, 5, "exact"),     # window: fewer blocks than the length
+    (12, 8, 2, 1, 600, 128, False, -1, 6, "short"),     # sum understated: workgroups take several units
+])
+def test_varlen_work_units(case, units, attn_options):
+    B, Hq, Hkv, Sq, Sk, d, causal, wl, seed, given = case
+    attn_options("ATTN_VARLEN_UNITS", units)
+    attn_options("ATTN_VARLEN_CHUNK", 128)  # small chunks: many splits per sequence
+    q, k, v = small_case(30 + seed, "bf16", B, Hq, Hkv, Sq, Sk, d)
+    g = torch.Generator().manual_seed(seed)
+    seqlens = torch.randint(0, Sk + 1, (B,), generator=g, dtype=torch.int32)
+    seqlens[0] = 0
+    seqlens[-1] = Sk
+    total = int(seqlens.sum())
+    sum_arg = {"exact": total, "none": -1, "short": max(1, total // 10)}[given]
+    pl = tpa.plan(B, Hq, Hkv, Sq, Sk, d, causal, wl, 0, "bf16", varlen=True, sum_seqlens_k=sum_arg)
+    assert (pl["work_units"] > 0) == bool(units) and pl["num_splits"] > 1
+    if units and given == "exact":
+        assert pl["grid_x"] <= total // (64 * pl["chunk_blocks"]) + B
+    print(f"varlen units={units} {case} plan {pl['grid_x']}x{pl['grid_y']} S={pl['num_splits']}", flush=True)
+    ro, rl = oracle.attn_ref(q, k, v, causal, wl, 1 / math.sqrt(d), seqlens_k=seqlens)
+    o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV), causal=causal,
+                            window_left=wl, sum_seqlens_k=sum_arg)
+    assert_parity(o, lse, ro, rl, "bf16", f"varlen units={units} {case}")
+
+
 @pytest.mark.parametrize("factor,causal,wl,d", [(8.0, True, -1, 128), (4.0, True, -1, 128),
                                                 (8.0, False, -1, 128), (8.0, True, 1000, 128),
                                                 (16.0, False, 300, 64), (2.0, True, -1, 64)])

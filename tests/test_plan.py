@@ -210,3 +210,27 @@ def test_bwd_plan_atomic_form_needs_the_accumulator(attn_options):
     p = tpa.plan_bwd(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, w.dtype)
     assert p["dq_block_m"] == 0
     assert p["workspace_bytes"] >= w.B * w.Sq * w.Hq * (w.d + 2) * 4
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_varlen_work_unit_grid_covers_every_split(seed, attn_options):
+    # The unit grid holds one workgroup per (sequence, split); sequence b has
+    # S_b = min(S, max(1, ceil(blocks_b / chunk))) splits, so with the exact sum
+    # of the key lengths the host's count must reach sum_b S_b, and the fixed
+    # grid (B * S) must be the bound when no sum is given.
+    import numpy as np
+    attn_options("ATTN_VARLEN_CHUNK", 128 * (1 + seed % 3))
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, Sk = int(rng.integers(1, 200)), 32, 8, int(rng.integers(64, 20000))
+    lens = rng.integers(0, Sk + 1, B)
+    total = int(lens.sum())
+    pl = tpa.plan(B, Hq, Hkv, 1, Sk, 128, False, -1, 0, "bf16", varlen=True, sum_seqlens_k=max(total, 1))
+    if pl["num_splits"] == 1:
+        assert pl["work_units"] == 0
+        return
+    cb, S = pl["chunk_blocks"], pl["num_splits"]
+    need = sum(min(S, max(1, -(-(-(-int(n) // 64)) // cb))) for n in lens)
+    assert need <= pl["work_units"] == pl["grid_x"] <= B * S
+    assert pl["grid_y"] == Hkv and pl["grid_z"] == 1
+    pl0 = tpa.plan(B, Hq, Hkv, 1, Sk, 128, False, -1, 0, "bf16", varlen=True, sum_seqlens_k=-1)
+    assert pl0["work_units"] == B * pl0["num_splits"]

@@ -41,7 +41,7 @@ class Plan(ctypes.Structure):
         ("grid_heads", ctypes.c_int), ("num_splits", ctypes.c_int), ("chunk_blocks", ctypes.c_int),
         ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int), ("grid_z", ctypes.c_int),
         ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("num_cus", ctypes.c_int),
-        ("lpt", ctypes.c_int), ("visited_blocks", ctypes.c_longlong),
+        ("lpt", ctypes.c_int), ("work_units", ctypes.c_int), ("visited_blocks", ctypes.c_longlong),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

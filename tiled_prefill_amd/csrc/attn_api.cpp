@@ -71,6 +71,7 @@ const OptionDef kOptionDefs[] = {
     {"ATTN_WG_PER_CU", &Options::wg_per_cu, 2},
     {"ATTN_SPLIT_RULE", &Options::split_rule, 0},
     {"ATTN_VARLEN_CHUNK", &Options::varlen_chunk, 512},
+    {"ATTN_VARLEN_UNITS", &Options::varlen_units, 1},
     {"ATTN_MLA_MIN_CHUNK", &Options::mla_min_chunk, 128},
     {"ATTN_SPLIT_MAJOR", &Options::split_major, -1},
     {"ATTN_COMBINE_COLS", &Options::combine_cols, -1},
@@ -398,6 +399,18 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         q.grid_x = (int)((launch + 7) / 8 * 8);
         q.grid_y = 1;
         q.grid_z = 1;
+    } else if (p.varlen && chunk > 0 && S > 1 && var->kdma && opt.varlen_units) {
+        // variable-length decode over (sequence, split) work units ([FA-tiling]
+        // §4.5): sequence b has S_b = max(1, ceil(len_b / (BN chunk))) or fewer
+        // splits, so sum_b S_b <= sum_seqlens_k / (BN chunk) + B; with no sum
+        // given, B * S
+        const long long per = (long long)BN * chunk;
+        long long units = (long long)p.B * S;
+        if (p.sum_seqlens_k > 0) units = std::min(units, p.sum_seqlens_k / per + p.B);
+        q.work_units = (int)units;
+        q.grid_x = (int)units;
+        q.grid_y = q.grid_heads;
+        q.grid_z = 1;
     } else {
         q.grid_x = q.num_m_blocks;
         q.grid_y = q.grid_heads * S;
@@ -570,6 +583,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.num_splits = pl.num_splits;
     fp.chunk_blocks = pl.chunk_blocks;
     fp.lpt = pl.lpt;
+    fp.work_units = pl.work_units;
     // decode grids: the workgroups of one key range (all grid heads) are
     // dispatched together, so concurrent reads cover whole interleaved KV rows
     fp.split_major = options().split_major >= 0 ? options().split_major : (plan.var->block_m <= 16 ? 1 : 0);

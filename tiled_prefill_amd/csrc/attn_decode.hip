@@ -341,7 +341,7 @@ struct DecodeKdmaTile {
     static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1; }
 };
 
-template <int D, int NW>
+template <int D, int NW, bool UNITS>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdParams p) {
     using C = DecodeKdmaTile<D, NW>;
     constexpr int KB = C::KB, HB = C::HB, NSLAB = C::NSLAB, DT = C::DT;
@@ -354,15 +354,10 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     char* vl = kl + C::HALFB;           // its V half
     char* ql = vl + C::HALFB;           // and its copy of the query rows (K's swizzle)
 
-    // (head, split) of this workgroup: blockIdx.y / y_div by the host's
-    // multiplier (no branch and no integer division before the first copy)
-    const unsigned int gy = blockIdx.y;
-    const unsigned int ty = __umulhi(gy, p.y_mul);
-    const unsigned int qy = (ty + ((gy - ty) >> p.y_s1)) >> p.y_s2;
-    const int ry = (int)(gy - qy * (unsigned int)p.y_div);
-    const int hg = p.split_major ? ry : (int)qy;
-    const int split = p.split_major ? (int)qy : ry;
-    const int b = blockIdx.z;
+    // One (batch b, KV head hg, split) of work. In the work-unit grid, last_of is
+    // the sequence's split count when this is its last split (that unit also
+    // marks the splits the sequence does not use as empty), else 0.
+    auto work = [&](const int b, const int hg, const int split, const int last_of) {
     int Skb = p.Sk;
     if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
     const int G = p.G;
@@ -614,7 +609,12 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
     const size_t row = ((size_t)b * p.Sq + pos) * p.Hq + head;
     if (p.num_splits > 1) {
         const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
-        if (wave == 0 && lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+        if (wave == 0 && lg == 0) {
+            p.lse_part[(size_t)split * rows_total + row] = lse;
+            if constexpr (UNITS)
+                for (int s2 = last_of > 0 ? last_of : p.num_splits; s2 < p.num_splits; ++s2)
+                    p.lse_part[(size_t)s2 * rows_total + row] = -INFINITY;
+        }
         if (any) {
             float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
 #pragma unroll
@@ -629,6 +629,70 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
             wv[0] = pack_bf16x2(om[x][0] * inv, om[x][1] * inv);
             wv[1] = pack_bf16x2(om[x][2] * inv, om[x][3] * inv);
             *reinterpret_cast<u32x2*>(orow + 16 * (wave * DW + x)) = wv;
+        }
+    }
+    };
+
+    if constexpr (!UNITS) {
+        // (head, split) of this workgroup: blockIdx.y / y_div by the host's
+        // multiplier (no branch and no integer division before the first copy)
+        const unsigned int gy = blockIdx.y;
+        const unsigned int ty = __umulhi(gy, p.y_mul);
+        const unsigned int qy = (ty + ((gy - ty) >> p.y_s1)) >> p.y_s2;
+        const int ry = (int)(gy - qy * (unsigned int)p.y_div);
+        const int hg = p.split_major ? ry : (int)qy;
+        const int split = p.split_major ? (int)qy : ry;
+        work((int)blockIdx.z, hg, split, 0);
+    } else {
+        // Work-unit grid for variable key lengths ([FA-tiling] §4.5, §5.3):
+        // sequence b owns S_b consecutive units, one per split, S_b its own split
+        // count, so no workgroup is launched for a split a sequence does not
+        // have. Unit u of KV head blockIdx.y is found by a prefix sum of the
+        // S_b, 64 sequences per step across the wave's lanes. The host sizes the
+        // grid from the sum of the key lengths; should that fall short, the
+        // workgroups also take units u + gridDim.x, ... so every unit runs.
+        const int hg = blockIdx.y;
+        int b = 0, split = 0, sb_u = 0;
+        auto find = [&](const int u) -> int {  // sets (b, split, sb_u); returns the unit count
+            int base = 0;
+            bool found = false;
+            for (int c0 = 0; c0 < p.B; c0 += 64) {
+                const int bb = c0 + lane;
+                int sb = 0;
+                if (bb < p.B) {
+                    const int len = imax(0, imin(p.seqlens_k[bb], p.Sk));
+                    int lo, hi;
+                    n_block_range(p.Sq, len, p.G, p.pack, p.causal, p.window_left, 16, KB, 0, &lo, &hi);
+                    sb = splits_for(imax(0, hi - lo), p.num_splits, p.chunk_blocks);
+                }
+                int incl = sb;  // inclusive prefix sum over the lanes
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    if (lane >= o) incl += y;
+                }
+                if (!found) {
+                    // sequences of this step that end at or before unit u
+                    const int before = __popcll(__builtin_amdgcn_ballot_w64(bb < p.B && base + incl <= u));
+                    if (before < imin(64, p.B - c0)) {
+                        const int excl = before > 0 ? __shfl(incl, before - 1) : 0;
+                        b = __builtin_amdgcn_readfirstlane(c0 + before);
+                        split = __builtin_amdgcn_readfirstlane(u - base - excl);
+                        sb_u = __builtin_amdgcn_readfirstlane(__shfl(sb, before));
+                        found = true;
+                    }
+                }
+                base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+            }
+            return base;
+        };
+        const int total = find((int)blockIdx.x);
+        for (int u = (int)blockIdx.x; u < total; u += (int)gridDim.x) {
+            if (u != (int)blockIdx.x) {
+                __syncthreads();  // the previous unit's LDS reads are done
+                find(u);
+            }
+            work(b, hg, split, split == sb_u - 1 ? sb_u : 0);
         }
     }
 }
@@ -940,7 +1004,12 @@ hipError_t launch_decode(const FwdParams& p, dim3 grid, hipStream_t stream) {
 template <int D, int NW>
 hipError_t launch_decode_kdma(const FwdParams& p, dim3 grid, hipStream_t stream) {
     if (!p.pack && p.G > 1) return hipErrorInvalidValue;  // the kernel takes grid head = KV head
-    hipLaunchKernelGGL((attn_decode_kdma_kernel<D, NW>), grid, dim3(64 * NW), 0, stream, p);
+    if (p.work_units) {  // grid (units, KV heads, 1) over variable key lengths
+        if (!p.seqlens_k || p.chunk_blocks <= 0 || p.num_splits <= 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attn_decode_kdma_kernel<D, NW, true>), grid, dim3(64 * NW), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((attn_decode_kdma_kernel<D, NW, false>), grid, dim3(64 * NW), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -77,6 +77,7 @@ struct Options {
     int prefill_skip;     // ATTN_PREFILL_SKIP=n: the n-th later matching prefill variant
     int verify_tile;      // ATTN_VERIFY_TILE: 0 widest row tile, 1 32-row 2x2, 2 32-row 2x4
     int f32_dma;          // ATTN_F32_DMA: fp32 on the LDS-copy kernel for 17..32 rows per KV head (1), for 1..32 (2)
+    int varlen_units;     // ATTN_VARLEN_UNITS: variable-length decode on the work-unit grid (1)
     int f32_waves;        // ATTN_F32_WAVES: that kernel's 8-wave form where d has one (8), else 4 waves
     int min_chunk;        // ATTN_MIN_CHUNK: minimum keys per split (256)
     int wg_per_cu;        // ATTN_WG_PER_CU: workgroup target per CU of the split rule (2)

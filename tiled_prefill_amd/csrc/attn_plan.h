@@ -139,6 +139,7 @@ struct FwdParams {
     int chunk_blocks;       // > 0: per-sequence split count (variable length)
     int lpt;                // reverse query-block order (heaviest causal blocks first)
     int split_major;        // grid y = split * grid_heads + head (else head * splits + split)
+    int work_units;         // variable-length decode: grid (units, KV heads) over (sequence, split) units
     int* tile_counters;     // persistent kernels: one tile queue counter per XCD, zero at launch
     // Decode tiles of fixed-length problems (seqlens_k null): the key-block
     // range of the single query block and its blocks per split, computed once
