@@ -391,7 +391,8 @@ ABLATIONS = [
     {"ATTN_GENERIC_PREFILL": "1"},          # general tile kernel for bf16 prefill
     {"ATTN_GENERIC_DECODE": "1"},           # general tile kernel for bf16 decode
     {"ATTN_DECODE_WAVES": "8"},             # 8-wave decode workgroups
-    {"ATTN_DECODE_KDMA": "0"},              # decode with K straight into registers
+    {"ATTN_DECODE_KDMA": "0"},              # decode with K straight into registers, 16-row V tiles
+    {"ATTN_DECODE_KDMA": "1"},              # decode with K and V through LDS in 32-key halves
     {"ATTN_SPLIT_RULE": "1"},               # split-count rule of the tiling page
     {"ATTN_SPLIT_RULE": "2"},               # NSPLIT rule of the occupancy blog
     {"ATTN_SPLIT_RULE": "3"},               # occupancy first, below the 256-key chunk
@@ -408,6 +409,38 @@ def test_decode_forced_split_counts(S):
     for seed in (13, 14):
         run_case("bf16", 2, 16, 2, 1, 2100, 128, False, -1, S, seed=seed)
         run_case("bf16", 1, 8, 8, 1, 700, 64, False, 100, S, seed=seed)
+
+
+DECODE_FORM_CASES = [
+    # dtype, B, Hq, Hkv, Sq, Sk, d, causal, wl, S
+    ("bf16", 1, 32, 4, 1, 3000, 128, False, -1, 0),    # ragged last block, planner splits
+    ("bf16", 2, 16, 2, 1, 2100, 128, False, -1, 1),    # one split: 33 blocks, several per wave
+    ("bf16", 2, 16, 2, 1, 2100, 128, False, -1, 37),   # more splits than blocks: empty splits
+    ("bf16", 1, 8, 8, 1, 700, 64, False, 100, 3),      # d 64, window
+    ("bf16", 2, 16, 2, 2, 333, 128, True, -1, 0),      # two positions x 8 heads, causal
+    ("bf16", 1, 8, 1, 1, 5, 128, False, -1, 0),        # fewer keys than one block
+    ("bf16", 1, 32, 8, 1, 64, 128, False, -1, 2),      # exactly one block, split in two
+]
+
+
+@pytest.mark.parametrize("form", [2, 1], ids=["k_in_registers", "halves_through_lds"])
+@pytest.mark.parametrize("case", DECODE_FORM_CASES)
+def test_decode_forms(case, form, attn_options):
+    attn_options("ATTN_DECODE_KDMA", form)
+    run_case(*case, seed=21)
+
+
+@pytest.mark.parametrize("form", [2, 1], ids=["k_in_registers", "halves_through_lds"])
+def test_decode_forms_varlen(form, attn_options):
+    attn_options("ATTN_DECODE_KDMA", form)
+    B, Hq, Hkv, Sk, d = 20, 16, 4, 1500, 128
+    q, k, v = small_case(22, "bf16", B, Hq, Hkv, 1, Sk, d)
+    seqlens = torch.randint(0, Sk + 1, (B,), generator=torch.Generator().manual_seed(22), dtype=torch.int32)
+    seqlens[3] = 0
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, 1 / math.sqrt(d), seqlens_k=seqlens)
+    print(f"decode form {form} varlen", flush=True)
+    o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV), sum_seqlens_k=int(seqlens.sum()))
+    assert_parity(o, lse, ro, rl, "bf16", f"decode form {form} varlen")
 
 
 @pytest.mark.parametrize("env", ABLATIONS, ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))

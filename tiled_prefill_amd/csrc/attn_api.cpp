@@ -253,13 +253,14 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     }
     if (!var && decode && opt.generic_decode == 0) {
         const int want_waves = opt.decode_waves;  // waves per workgroup (4 or 8)
-        // 1: K through LDS in 32-key halves (else the register-K form where no
-        // such variant exists); 0: K straight into registers (ablation)
-        const int want_kdma = opt.decode_kdma ? 1 : 0;
-        for (int pass = 0; pass < 2 && !var; ++pass)
+        // ATTN_DECODE_KDMA: 2 = K in registers and V through LDS in whole blocks,
+        // 1 = K and V through LDS in 32-key halves, 0 = K straight into registers
+        // with 16-row V tiles (ablation); a form with no variant for these waves
+        // and d falls back to the next lower one
+        const int want_kdma = imax(0, imin(2, opt.decode_kdma));
+        for (int kd = want_kdma; kd >= 0 && !var; --kd)
             for (const FwdVariant* v = decode_variants(); v->launch; ++v)
-                if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves &&
-                    v->kdma == (pass == 0 ? want_kdma : 0)) {
+                if (v->dtype == p.dtype && v->d == p.d && v->waves_n == want_waves && v->kdma == kd) {
                     var = v;
                     break;
                 }

@@ -321,6 +321,50 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams 
 // Fixed-length problems take their key range and split share from the host,
 // so nothing is divided before the first copy.
 // ---------------------------------------------------------------------------
+// Work-unit grid for variable key lengths ([FA-tiling] §4.5, §5.3): sequence b
+// owns S_b consecutive units, one per split (S_b its own split count), so no
+// workgroup runs for a split a sequence does not have. Unit u of a KV head is
+// found by a prefix sum of the S_b, 64 sequences per step across the wave's
+// lanes; returns the number of units and sets the unit's sequence, split and
+// that sequence's split count (wave-uniform). The host sizes the grid from the
+// sum of the key lengths; should that fall short, the workgroups also take
+// units u + gridDim.x, ..., so every unit runs.
+__device__ __forceinline__ int decode_find_unit(const FwdParams& p, const int u, const int KB, int* b_out,
+                                                int* split_out, int* sb_out) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    bool found = false;
+    for (int c0 = 0; c0 < p.B; c0 += 64) {
+        const int bb = c0 + lane;
+        int sb = 0;
+        if (bb < p.B) {
+            const int len = imax(0, imin(p.seqlens_k[bb], p.Sk));
+            int lo, hi;
+            n_block_range(p.Sq, len, p.G, p.pack, p.causal, p.window_left, 16, KB, 0, &lo, &hi);
+            sb = splits_for(imax(0, hi - lo), p.num_splits, p.chunk_blocks);
+        }
+        int incl = sb;  // inclusive prefix sum over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (!found) {
+            // sequences of this step that end at or before unit u
+            const int before = __popcll(__builtin_amdgcn_ballot_w64(bb < p.B && base + incl <= u));
+            if (before < imin(64, p.B - c0)) {
+                const int excl = before > 0 ? __shfl(incl, before - 1) : 0;
+                *b_out = __builtin_amdgcn_readfirstlane(c0 + before);
+                *split_out = __builtin_amdgcn_readfirstlane(u - base - excl);
+                *sb_out = __builtin_amdgcn_readfirstlane(__shfl(sb, before));
+                found = true;
+            }
+        }
+        base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    }
+    return base;
+}
+
 template <int D, int NW>
 struct DecodeKdmaTile {
     static constexpr int KB = 64;              // keys per block (the planner's block)
@@ -644,57 +688,323 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
         const int split = p.split_major ? (int)qy : ry;
         work((int)blockIdx.z, hg, split, 0);
     } else {
-        // Work-unit grid for variable key lengths ([FA-tiling] §4.5, §5.3):
-        // sequence b owns S_b consecutive units, one per split, S_b its own split
-        // count, so no workgroup is launched for a split a sequence does not
-        // have. Unit u of KV head blockIdx.y is found by a prefix sum of the
-        // S_b, 64 sequences per step across the wave's lanes. The host sizes the
-        // grid from the sum of the key lengths; should that fall short, the
-        // workgroups also take units u + gridDim.x, ... so every unit runs.
+        // work-unit grid (decode_find_unit)
         const int hg = blockIdx.y;
         int b = 0, split = 0, sb_u = 0;
-        auto find = [&](const int u) -> int {  // sets (b, split, sb_u); returns the unit count
-            int base = 0;
-            bool found = false;
-            for (int c0 = 0; c0 < p.B; c0 += 64) {
-                const int bb = c0 + lane;
-                int sb = 0;
-                if (bb < p.B) {
-                    const int len = imax(0, imin(p.seqlens_k[bb], p.Sk));
-                    int lo, hi;
-                    n_block_range(p.Sq, len, p.G, p.pack, p.causal, p.window_left, 16, KB, 0, &lo, &hi);
-                    sb = splits_for(imax(0, hi - lo), p.num_splits, p.chunk_blocks);
-                }
-                int incl = sb;  // inclusive prefix sum over the lanes
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int y = __shfl_up(incl, o);
-                    if (lane >= o) incl += y;
-                }
-                if (!found) {
-                    // sequences of this step that end at or before unit u
-                    const int before = __popcll(__builtin_amdgcn_ballot_w64(bb < p.B && base + incl <= u));
-                    if (before < imin(64, p.B - c0)) {
-                        const int excl = before > 0 ? __shfl(incl, before - 1) : 0;
-                        b = __builtin_amdgcn_readfirstlane(c0 + before);
-                        split = __builtin_amdgcn_readfirstlane(u - base - excl);
-                        sb_u = __builtin_amdgcn_readfirstlane(__shfl(sb, before));
-                        found = true;
-                    }
-                }
-                base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-            }
-            return base;
-        };
-        const int total = find((int)blockIdx.x);
+        const int total = decode_find_unit(p, (int)blockIdx.x, KB, &b, &split, &sb_u);
         for (int u = (int)blockIdx.x; u < total; u += (int)gridDim.x) {
             if (u != (int)blockIdx.x) {
                 __syncthreads();  // the previous unit's LDS reads are done
-                find(u);
+                decode_find_unit(p, u, KB, &b, &split, &sb_u);
             }
             work(b, hg, split, split == sb_u - 1 ? sb_u : 0);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Decode with K in registers and V through LDS, in whole 64-key blocks. A wave
+// sends the copies of its whole block at once: the query rows and the K block
+// straight into MFMA operand registers (16-byte buffer loads; the K block is 64
+// registers at d = 128), the V block into the wave's 16 KB of LDS (buffer_load
+// ... lds, whole rows). Two 4-wave workgroups on a CU then hold 256 KB of K and
+// V in flight, twice what the half-block pipeline above can (its K and V share
+// LDS), so a split of 256 keys costs one memory round trip instead of two. A
+// wave with more blocks sends the next block's copies once it has read the
+// current one. P.V reads V^T with ds_read_b64_tr_b16 (P as bf16 hi + lo parts);
+// the softmax, the merge of the waves and the epilogue are those of the kernel
+// above.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+struct DecodeKvTile {
+    static constexpr int KB = 64;              // keys per block (the planner's block)
+    static constexpr int NT = KB / 16;         // 16-key subtiles of S^T
+    static constexpr int NSLAB = D / 32;       // 32-d slabs of the QK contraction
+    static constexpr int DT = D / 16;          // 16-wide d tiles of the output
+    static constexpr int CPR = D / 8;          // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;         // bytes per V row in LDS
+    static constexpr int RPI = 1024 / ROWB;    // rows per wave-wide copy
+    static constexpr int NL = KB / RPI;        // copies per V block
+    static constexpr int WAVEB = KB * ROWB;    // one V block per wave
+    static constexpr int RED_BYTES = NW * (DT * 4 * 64 + 2 * 64) * 4;
+    static constexpr int LDS_BYTES = NW * WAVEB > RED_BYTES ? NW * WAVEB : RED_BYTES;
+    static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1; }
+};
+
+template <int D, int NW, bool UNITS>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kv_kernel(FwdParams p) {
+    using C = DecodeKvTile<D, NW>;
+    constexpr int KB = C::KB, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
+    constexpr int CPR = C::CPR, RPI = C::RPI, NL = C::NL, ROWB = C::ROWB;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, lg = lane >> 4;
+    char* vl = smem + wave * C::WAVEB;  // this wave's V block, swizzled rows
+
+    auto work = [&](const int b, const int hg, const int split, const int last_of) {
+    int Skb = p.Sk;
+    if (p.seqlens_k) Skb = imax(0, imin(p.seqlens_k[b], p.Sk));
+    const int G = p.G;
+    const int hkv = hg;  // decode tiles always pack the G heads of a KV head (checked at launch)
+    const int nrows = p.pack ? p.Sq * G : p.Sq;
+    const int delta = Skb - p.Sq;
+
+    // key blocks of this split ([FA-tiling] §3.2, §5.3)
+    int s_lo = 0, s_hi = 0;
+    if (!p.seqlens_k && p.chunk_blocks <= 0) {
+        if (split < p.num_splits) {
+            s_lo = p.dec_lo + split * p.dec_per;
+            s_hi = imin(s_lo + p.dec_per, p.dec_hi);
+        }
+    } else {
+        int n_lo, n_hi;
+        n_block_range(p.Sq, Skb, G, p.pack, p.causal, p.window_left, 16, KB, 0, &n_lo, &n_hi);
+        const int S_b = splits_for(imax(0, n_hi - n_lo), p.num_splits, p.chunk_blocks);
+        if (split < S_b) split_range(n_lo, n_hi, split, S_b, &s_lo, &s_hi);
+    }
+
+    const size_t kv_stride = (size_t)p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+    const bf16_t* kbase = reinterpret_cast<const bf16_t*>(p.k) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    const bf16_t* vbase = reinterpret_cast<const bf16_t*>(p.v) + ((size_t)b * p.Sk * p.Hkv + hkv) * D;
+    // rows at or past Skb lie outside the buffer resources and read as zeros
+    auto block_bytes = [&](int n) { return (uint32_t)imax(0, imin(KB, Skb - n * KB)) * row_bytes; };
+    // V block n: lane l of copy i fills LDS bytes [1024 i + 16 l, +16) = row
+    // RPI i + l / CPR, slot l % CPR, which holds chunk (slot ^ swz_v(row))
+    auto copy_v = [&](int n) {
+        const u32x4 rs = rsrc_words_u(vbase + (size_t)n * KB * kv_stride, block_bytes(n));
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(vl));
+        const int r0 = lane / CPR, slot = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int rr = RPI * i + r0;
+            const uint32_t off = rr * row_bytes + 16 * (slot ^ C::swz_v(rr));
+            dma16_untracked(rs, off, l0 + 1024 * i);
+        }
+    };
+    // K block n into registers: kf[t][c] = K[key 16 t + li][32 c + 8 lg .. + 7]
+    u32x4 kf[NT][NSLAB];
+    auto load_k = [&](int n) {
+        const rsrc_t rk = make_rsrc_u(kbase + (size_t)n * KB * kv_stride, block_bytes(n));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int c = 0; c < NSLAB; ++c) kf[t][c] = buf_load16_nt(rk, (16 * t + li) * row_bytes + 64 * c + 16 * lg);
+    };
+
+    // this lane's query row (column li of every S^T tile); visible keys are
+    // those with 0 <= key - lo <= span (rows that see none: lo above every key)
+    const int r = li;
+    const bool row_ok = r < nrows;
+    const int pos = row_ok ? (p.pack ? r / G : r) : 0;
+    const int head = p.pack ? hkv * G + (row_ok ? r % G : 0) : hg;
+    int row_lo = 0, row_hi = Skb - 1;
+    int wlo = -0x7fffffff, whi = 0x7fffffff;
+    if (row_ok) {
+        if (p.window_left >= 0) row_lo = pos + delta - p.window_left;
+        if (p.causal) row_hi = imin(row_hi, pos + delta);
+        wlo = row_lo;
+        whi = row_hi;
+    }
+    wlo = row16_imax(wlo);
+    whi = row16_imin(whi);
+    const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
+    if (row_hi < row_lo) row_lo = 0x40000000;
+
+    // the first block: query rows (Q^T fragments, lane (i, g) holds Q[row i][32c
+    // + 8g .. +7]; rows the tile does not own read zeros), then V, then K
+    int n = s_lo + wave;
+    u32x4 qf[NSLAB];
+    if (n < s_hi) {
+        const rsrc_t rq = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.q) + (size_t)b * p.Sq * p.Hq * D,
+                                      (uint32_t)p.Sq * p.Hq * D * 2);
+        const uint32_t qoff = row_ok ? (uint32_t)((pos * p.Hq + head) * D) * 2 + 16 * lg : 0x80000000u;
+#pragma unroll
+        for (int c = 0; c < NSLAB; ++c) qf[c] = buf_load16(rq, qoff + 64 * c);
+        copy_v(n);
+        load_k(n);
+    }
+
+    f32x4 oacc[DT];
+#pragma unroll
+    for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
+    constexpr float LAZY = 8.f;
+
+    // blocks of this wave: n = s_lo + wave, +NW, ...
+    for (; n < s_hi; n += NW) {
+        // S^T = K . Q^T over the block's 64 keys (the compiler waits for K)
+        f32x4 sacc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NSLAB; ++c) sacc[t] = mfma_bf16(kf[t][c], qf[c], sacc[t]);
+        }
+
+        const int key0 = n * KB;
+        if (!(key0 >= wlo && key0 + KB - 1 <= whi)) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int base = key0 + 16 * t + 4 * lg - row_lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if ((uint32_t)(base + e) > (uint32_t)row_span) sacc[t][e] = -INFINITY;
+            }
+        }
+
+        // online softmax, reference max moved lazily
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) mx = vmax(vmax(vmax(vmax(mx, sacc[t][0]), sacc[t][1]), sacc[t][2]), sacc[t][3]);
+        mx = xor_max(mx);
+        const bool raise = m_run == -INFINITY ? mx != -INFINITY : (mx - m_run) * sl2 > LAZY;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float alpha = !raise ? 1.f : (m_run == -INFINITY ? 0.f : fast_exp2((m_run - mx) * sl2));
+            if (raise) m_run = mx;
+            l_run *= alpha;
+#pragma unroll
+            for (int w = 0; w < DT; ++w) oacc[w] *= alpha;
+        }
+        const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pv = fast_exp2(fmaf(sacc[t][e], sl2, neg));
+                sacc[t][e] = pv;
+                l_run += pv;
+            }
+
+        // O^T += V^T . P^T with P as bf16 hi + lo parts; the V block was copied
+        // before K, so it has landed (nothing else is in flight here)
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int pp = 0; pp < NT / 2; ++pp) {
+            const u32x2 s0 = split_bf16x2(sacc[2 * pp][0], sacc[2 * pp][1]);
+            const u32x2 s1 = split_bf16x2(sacc[2 * pp][2], sacc[2 * pp][3]);
+            const u32x2 s2 = split_bf16x2(sacc[2 * pp + 1][0], sacc[2 * pp + 1][1]);
+            const u32x2 s3 = split_bf16x2(sacc[2 * pp + 1][2], sacc[2 * pp + 1][3]);
+            const u32x4 ph = {s0[0], s1[0], s2[0], s3[0]};
+            const u32x4 pl = {s0[1], s1[1], s2[1], s3[1]};
+            const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
+            const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+#pragma unroll
+            for (int w = 0; w < DT; ++w) {
+                const int ch = 2 * w + cb;
+                const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vl + ra * ROWB + 16 * (ch ^ C::swz_v(ra)) + hb));
+                const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vl + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
+                const u32x4 vf = {a[0], a[1], c[0], c[1]};
+                oacc[w] = mfma_bf16(vf, ph, oacc[w]);
+                oacc[w] = mfma_bf16(vf, pl, oacc[w]);
+            }
+        }
+        if (n + NW < s_hi) {  // the next block, once this one's V reads are done
+            wait_lgkmcnt0();
+            copy_v(n + NW);
+            load_k(n + NW);
+        }
+    }
+    l_run = xor_sum(l_run);
+
+    // merge the waves' softmax states: every wave merges DT / NW of the d tiles
+    // from all waves and writes that part of the output
+    static_assert(DT % NW == 0, "d tiles split evenly over the waves");
+    constexpr int DW = DT / NW;
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    float* red_o = red;                          // [NW][DT*4][64]
+    float* red_ml = red + NW * DT * 4 * 64;      // [NW][2][64]
+#pragma unroll
+    for (int w = 0; w < DT; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red_o[(wave * DT * 4 + w * 4 + e) * 64 + lane] = oacc[w][e];
+    red_ml[(wave * 2 + 0) * 64 + lane] = m_run;
+    red_ml[(wave * 2 + 1) * 64 + lane] = l_run;
+    __syncthreads();
+    float mw[NW], mstar = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        mw[w] = red_ml[(w * 2 + 0) * 64 + lane];
+        mstar = vmax(mstar, mw[w]);
+    }
+    const float muse = mstar == -INFINITY ? 0.f : mstar;
+    float l = 0.f;
+    f32x4 om[DW];
+#pragma unroll
+    for (int x = 0; x < DW; ++x) om[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float a = fast_exp2((mw[w] - muse) * sl2);
+        l += a * red_ml[(w * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int x = 0; x < DW; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) om[x][e] += a * red_o[(w * DT * 4 + (wave * DW + x) * 4 + e) * 64 + lane];
+    }
+
+    if (!row_ok) return;
+    const bool any = l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const float lse = any ? mstar * p.scale + logf(l) : -INFINITY;
+    const size_t row = ((size_t)b * p.Sq + pos) * p.Hq + head;
+    if (p.num_splits > 1) {
+        const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
+        if (wave == 0 && lg == 0) {
+            p.lse_part[(size_t)split * rows_total + row] = lse;
+            if constexpr (UNITS)
+                for (int s2 = last_of > 0 ? last_of : p.num_splits; s2 < p.num_splits; ++s2)
+                    p.lse_part[(size_t)s2 * rows_total + row] = -INFINITY;
+        }
+        if (any) {
+            float* orow = p.o_part + ((size_t)split * rows_total + row) * D + 4 * lg;
+#pragma unroll
+            for (int x = 0; x < DW; ++x) *reinterpret_cast<f32x4*>(orow + 16 * (wave * DW + x)) = om[x] * inv;
+        }
+    } else {
+        if (wave == 0 && lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + head) * p.Sq + pos] = lse;
+        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * D + 4 * lg;
+#pragma unroll
+        for (int x = 0; x < DW; ++x) {
+            u32x2 wv;
+            wv[0] = pack_bf16x2(om[x][0] * inv, om[x][1] * inv);
+            wv[1] = pack_bf16x2(om[x][2] * inv, om[x][3] * inv);
+            *reinterpret_cast<u32x2*>(orow + 16 * (wave * DW + x)) = wv;
+        }
+    }
+    };
+
+    if constexpr (!UNITS) {
+        const unsigned int gy = blockIdx.y;
+        const unsigned int ty = __umulhi(gy, p.y_mul);
+        const unsigned int qy = (ty + ((gy - ty) >> p.y_s1)) >> p.y_s2;
+        const int ry = (int)(gy - qy * (unsigned int)p.y_div);
+        work((int)blockIdx.z, p.split_major ? ry : (int)qy, p.split_major ? (int)qy : ry, 0);
+    } else {
+        int b = 0, split = 0, sb_u = 0;
+        const int total = decode_find_unit(p, (int)blockIdx.x, KB, &b, &split, &sb_u);
+        for (int u = (int)blockIdx.x; u < total; u += (int)gridDim.x) {
+            if (u != (int)blockIdx.x) {
+                __syncthreads();
+                decode_find_unit(p, u, KB, &b, &split, &sb_u);
+            }
+            work(b, (int)blockIdx.y, split, split == sb_u - 1 ? sb_u : 0);
+        }
+    }
+}
+
+template <int D, int NW>
+hipError_t launch_decode_kv(const FwdParams& p, dim3 grid, hipStream_t stream) {
+    if (!p.pack && p.G > 1) return hipErrorInvalidValue;  // the kernel takes grid head = KV head
+    if (p.work_units) {
+        if (!p.seqlens_k || p.chunk_blocks <= 0 || p.num_splits <= 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attn_decode_kv_kernel<D, NW, true>), grid, dim3(64 * NW), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((attn_decode_kv_kernel<D, NW, false>), grid, dim3(64 * NW), 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1015,6 +1325,9 @@ hipError_t launch_decode_kdma(const FwdParams& p, dim3 grid, hipStream_t stream)
 
 const FwdVariant* decode_variants() {
     static const FwdVariant v[] = {
+        // K in registers, V through LDS, whole 64-key blocks (attn_decode_kv_kernel)
+        {DT_BF16, 128, 16, 64, 1, 4, DecodeKvTile<128, 4>::LDS_BYTES, &launch_decode_kv<128, 4>, 0, 0, 0, 2},
+        {DT_BF16, 64, 16, 64, 1, 4, DecodeKvTile<64, 4>::LDS_BYTES, &launch_decode_kv<64, 4>, 0, 0, 0, 2},
         // K through LDS in 32-key halves (see attn_decode_kdma_kernel)
         {DT_BF16, 128, 16, 64, 1, 4, DecodeKdmaTile<128, 4>::LDS_BYTES, &launch_decode_kdma<128, 4>, 0, 0, 0, 1},
         {DT_BF16, 64, 16, 64, 1, 4, DecodeKdmaTile<64, 4>::LDS_BYTES, &launch_decode_kdma<64, 4>, 0, 0, 0, 1},

@@ -20,7 +20,8 @@ struct FwdVariant {
     int grid_1d;            // 1: one-dimensional XCD-aware grid over all tiles
     int persistent;         // > 0: persistent workgroups (this many per CU) over tile queues
     int dv;                 // value / output width when it differs from d (0: equal to d)
-    int kdma;               // decode kernels: 1 = K through LDS in 32-key halves, 0 = K into registers
+    int kdma;               // decode kernels: 2 = K in registers, V through LDS (whole blocks);
+                            // 1 = K and V through LDS in 32-key halves; 0 = K into registers, 16-row V tiles
 };
 
 // Compiled variants of the general forward kernel and of the split-KV decode
