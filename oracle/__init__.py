@@ -47,7 +47,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_ref.c")
-_LIB_PATH = os.path.join(_HERE, "libattnref.so")
+_LIB_PATH = os.environ.get("ATTNREF_LIB") or os.path.join(_HERE, "libattnref.so")
 _lib = None
 
 
@@ -60,6 +60,18 @@ def build(force: bool = True) -> str:
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized(out_dir: str) -> str:
+    """The same library with host AddressSanitizer + UndefinedBehaviorSanitizer
+    (clang, so that one sanitizer runtime serves it and the HIP library; no
+    OpenMP: the loops run serially), loaded through ATTNREF_LIB."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = os.path.join(rocm, "llvm", "bin", "clang")
+    out = os.path.join(out_dir, "libattnref_asan.so")
+    subprocess.check_call([cc if os.path.exists(cc) else "clang", "-O1", "-g", "-fPIC", "-shared", "-std=c99",
+                           "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-o", out, _SRC, "-lm"])
+    return out
 
 
 def _load():

@@ -45,5 +45,33 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# library (planner, C-ABI and launch code instrumented; the device code is
+# built as usual). Loaded in place of libattn.so through ATTN_LIB, with the
+# sanitizer runtime preloaded (asan_runtime()), by the CPU test suite.
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-g",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+]
+
+
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    out = os.path.join(out_dir, "libattn_asan.so")
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O2"] + SANITIZE_FLAGS
+    cmd = [hipcc()] + flags + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out] + [
+        os.path.join(CSRC, s) for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    return out
+
+
+def asan_runtime() -> str:
+    """The compiler's shared ASan runtime (it carries the UBSan handlers too)."""
+    return subprocess.check_output([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], text=True).strip()
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
