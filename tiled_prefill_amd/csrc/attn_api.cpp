@@ -70,7 +70,7 @@ const OptionDef kOptionDefs[] = {
     {"ATTN_MIN_CHUNK", &Options::min_chunk, 256},
     {"ATTN_WG_PER_CU", &Options::wg_per_cu, 2},
     {"ATTN_SPLIT_RULE", &Options::split_rule, 0},
-    {"ATTN_VARLEN_CHUNK", &Options::varlen_chunk, 512},
+    {"ATTN_VARLEN_CHUNK", &Options::varlen_chunk, 1024},
     {"ATTN_VARLEN_UNITS", &Options::varlen_units, 1},
     {"ATTN_MLA_MIN_CHUNK", &Options::mla_min_chunk, 128},
     {"ATTN_SPLIT_MAJOR", &Options::split_major, -1},
@@ -363,10 +363,11 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
         } else if (rule == 3) {
             S = occupancy_first_rule(t, num_cus, max_blocks, BN, min_chunk, wg_per_cu);
         } else if (p.varlen) {
-            // per-sequence chunk: as many splits as keep >= 512 keys each (fewer
-            // partials for the combine; measured on 16 sequences of 512..16384 keys:
-            // 256-key chunks 154 us, 512 141.6, 768 141.2, 1024 142.3), but enough
-            // to reach the workgroup target when the batch is short
+            // per-sequence chunk: as many splits as keep >= 1024 keys each (fewer
+            // partials for the combine; measured per step on 16 sequences of
+            // 512..16384 keys with the work-unit grid: 512-key chunks 112.0 us,
+            // 1024 108.2, 1536 109.4, 2048 112.4), but enough to reach the
+            // workgroup target when the batch is short
             const long long sum = p.sum_seqlens_k > 0 ? p.sum_seqlens_k : (long long)p.B * p.Sk;
             const long long blocks = (sum + BN - 1) / BN * q.grid_heads * (long long)q.num_m_blocks;
             const long long target = (long long)wg_per_cu * num_cus;

@@ -83,7 +83,7 @@ struct Options {
     int min_chunk;        // ATTN_MIN_CHUNK: minimum keys per split (256)
     int wg_per_cu;        // ATTN_WG_PER_CU: workgroup target per CU of the split rule (2)
     int split_rule;       // ATTN_SPLIT_RULE: 0 occupancy, 1 [FA-tiling] 5.2, 2 NSPLIT, 3 occupancy first
-    int varlen_chunk;     // ATTN_VARLEN_CHUNK: keys per split of variable-length problems (512)
+    int varlen_chunk;     // ATTN_VARLEN_CHUNK: keys per split of variable-length problems (1024)
     int mla_min_chunk;    // ATTN_MLA_MIN_CHUNK: minimum keys per split of the latent kernel (128)
     int split_major;      // ATTN_SPLIT_MAJOR: grid order of split workgroups; -1 = by tile
     int combine_cols;     // ATTN_COMBINE_COLS: -1 by split count, 0/1 force split groups / columns
