@@ -37,7 +37,8 @@ KERNEL_SOURCES = {"attn_decode_kernel": "attn_decode.hip", "attn_decode_kdma_ker
                   "lse_combine_rows_kernel": "attn_decode.hip",
                   "attn_prefill_kernel": "attn_prefill.hip", "attn_fwd_kernel": "attn_fwd.hip",
                   "attn_mla_kernel": "attn_mla.hip", "stream_read_kernel": "attn_tools.hip",
-                  "attn_bwd_dkdv_dma_kernel": "attn_bwd.hip", "attn_bwd_dq_dma_kernel": "attn_bwd.hip"}
+                  "attn_bwd_dkdv_dma_kernel": "attn_bwd.hip", "attn_bwd_dq_dma_kernel": "attn_bwd.hip",
+                  "attn_fwd_f32_dma_kernel": "attn_fwd_f32.hip", "attn_decode_kv_kernel": "attn_decode.hip"}
 
 
 def parse():
@@ -66,12 +67,17 @@ def parse():
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="DIR",
                     help="summarise rocprofv3 --pmc runs (one DIR per pass) into "
                          "profiles/counters_<workload>.md; --rocprof-cmd names each pass's command, '|'-separated")
+    ap.add_argument("--summarize-traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="HBM bytes per launch from a rocprofv3 --pmc FETCH_SIZE pass and a WRITE_SIZE pass "
+                         "(each run with --copy-mb), calibrated on the copies: profiles/hbm_traffic_<workload>.md "
+                         "and profiles/traffic.json")
     return ap.parse_args()
 
 
-# the decode kernel the planner selects (ATTN_DECODE_KDMA=0: the register-K form)
-DECODE_KERNEL = "attn_decode_kernel" if os.environ.get("ATTN_DECODE_KDMA", "").strip() == "0" \
-    else "attn_decode_kdma_kernel"
+# the decode kernel the planner selects (ATTN_DECODE_KDMA: 0 the register-K form with
+# 16-row V tiles, 2 K in registers with whole-block V; default 1, K and V through LDS)
+DECODE_KERNEL = {"0": "attn_decode_kernel", "2": "attn_decode_kv_kernel"}.get(
+    os.environ.get("ATTN_DECODE_KDMA", "").strip(), "attn_decode_kdma_kernel")
 
 
 # headers whose inline device code every kernel source compiles in
@@ -217,6 +223,107 @@ def summarize_counters(args, num_cus=256, num_xcd=8):
         lines += ["", "derived: " + "; ".join(der), ""]
     out = os.path.join(ROOT, "profiles", f"counters_{args.workload}.md")
     open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def algorithmic_bytes(kernel: str, workload: str):
+    """(read, write) bytes one launch of `kernel` needs on `workload` if every
+    input were read and every output written exactly once: forward kernels read
+    Q and the K/V rows that exist (variable lengths: the sum of the key lengths)
+    and write O + lse, or the split partials; the combine reads the partials and
+    writes O + lse; the backward's key-block and query-block kernels read Q, dO,
+    K, V and the two per-row vectors and write dK + dV, or dQ."""
+    from workloads import WORKLOADS, BWD_WORKLOADS, make_inputs
+    import tiled_prefill_amd as tpa
+    w = WORKLOADS.get(workload) or BWD_WORKLOADS.get(workload)
+    if w is None:
+        return None
+    esz = 4 if w.dtype == "fp32" else 2
+    q_bytes = w.B * w.Sq * w.Hq * w.d * esz
+    rows = w.B * w.Sq * w.Hq
+    keys = w.B * w.Sk
+    if getattr(w, "varlen", False):
+        keys = int(make_inputs(w, seed=0)[3].sum())
+    kv_bytes = 2 * keys * w.Hkv * w.d * esz
+    o_bytes = q_bytes + rows * 4
+    if kernel.startswith("attn_bwd_"):
+        reads = 2 * q_bytes + kv_bytes + 2 * rows * 4
+        return reads, (kv_bytes if "dkdv" in kernel else q_bytes)
+    if kernel == "stream_read_kernel":  # the decode leg's reference: K and V bytes, read only
+        return kv_bytes, 0
+    plan = tpa.plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window_left, 0, w.dtype,
+                    varlen=getattr(w, "varlen", False), sum_seqlens_k=keys if getattr(w, "varlen", False) else -1)
+    part = plan["num_splits"] * rows * (w.d + 1) * 4 if plan["num_splits"] > 1 else 0
+    if kernel.startswith("lse_combine"):
+        return part, o_bytes
+    return q_bytes + kv_bytes, part or o_bytes
+
+
+def summarize_traffic(args):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+    summed over the GPU), each scaled by what the same counter reads for the
+    plain copies of --copy-mb MiB that the profiled run made first (the largest
+    copy dispatches of the pass): scale = copied bytes / counter bytes."""
+    import csv
+    import glob
+    import re
+    copy = args.copy_mb << 20
+    if copy <= 0:
+        sys.exit("--summarize-traffic needs --copy-mb (the size of the calibration copies)")
+    per = {}
+    scales = {}
+    for d, counter in zip(args.summarize_traffic, ("FETCH_SIZE", "WRITE_SIZE")):
+        vals, copies = {}, []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = re.sub(r"\(.*\)$", "", r["Kernel_Name"]).replace("void ", "").replace("tpa::", "")
+                v = float(r["Counter_Value"]) * 1024
+                if name.startswith("__amd_rocclr_copyBuffer"):
+                    copies.append(v)
+                else:
+                    vals.setdefault(name, []).append(v)
+        if not copies:
+            sys.exit(f"no copy dispatches in {d}: run the pass with --copy-mb")
+        big = [v for v in copies if v > 0.9 * max(copies)]
+        scales[counter] = copy / (sum(big) / len(big))
+        for name, v in vals.items():
+            per.setdefault(name, {})[counter] = (len(v), sum(v) / len(v) * scales[counter])
+    cmds = [c.strip() for c in args.rocprof_cmd.split("|") if c.strip()]
+    lines = [f"# HBM traffic per launch: {args.title or args.workload}", "",
+             "commands (from the repository root on one MI355X, TMPDIR=/tmp; one pass per counter), then this summary:",
+             ""] + [f"    {c}" for c in cmds] + [
+             f"    python3 bench.py --summarize-traffic {' '.join(args.summarize_traffic)} --workload {args.workload} "
+             f"--copy-mb {args.copy_mb}", "",
+             f"Each pass first copies a {args.copy_mb} MiB buffer three times; a counter's scale is the copied bytes "
+             f"over what it reads for those copies (FETCH_SIZE {scales['FETCH_SIZE']:.4f}, "
+             f"WRITE_SIZE {scales['WRITE_SIZE']:.4f}). Bytes are per launch, averaged over the kernel's dispatches; "
+             "algorithmic bytes read every input and write every output once.", "",
+             "| kernel | dispatches | fetched MB | written MB | algorithmic read MB | algorithmic write MB | fetch / algorithmic read |",
+             "|---|---|---|---|---|---|---|"]
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {}
+    for name, c in sorted(per.items(), key=lambda kv: -kv[1].get("FETCH_SIZE", (0, 0))[1]):
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c or name.startswith("at::"):
+            continue  # (torch's own kernels: input fills and copies)
+        fb, wb = c["FETCH_SIZE"][1], c["WRITE_SIZE"][1]
+        base = name.split("<")[0]
+        alg = algorithmic_bytes(base, args.workload) if base in KERNEL_SOURCES else None
+        ratio = f"{fb / alg[0]:.2f}" if alg and alg[0] else "-"
+        lines.append(f"| {name} | {c['FETCH_SIZE'][0]} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | "
+                     f"{alg[0] / 1e6 if alg else float('nan'):.2f} | {alg[1] / 1e6 if alg else float('nan'):.2f} | {ratio} |")
+        if base in KERNEL_SOURCES:
+            rec[f"{base}:{args.workload}"] = {
+                "kernel": name, "source": KERNEL_SOURCES[base], "source_sha": source_hash(base),
+                "bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
+                "fetch_scale": round(scales["FETCH_SIZE"], 4), "write_scale": round(scales["WRITE_SIZE"], 4),
+                "algorithmic_read_bytes": alg[0] if alg else None, "algorithmic_write_bytes": alg[1] if alg else None}
+    out = os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
     print(out)
 
 
@@ -427,6 +534,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(args)
         return
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(every workload fits one MI355X); run with --gpus 1", file=sys.stderr)
@@ -440,19 +550,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     tpa.load()
-    if args.suite:
-        run_suite(args)
-        return
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    out = {}
-    if args.copy_mb > 0:
+    if args.copy_mb > 0:  # plain copies of known size, to calibrate HBM byte counters
         src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.suite:
+        run_suite(args)
+        return
+    out = {}
 
     # ------------------------------------------------------------------ decode
     w = WORKLOADS["gqa_decode_bf16"]
@@ -651,7 +761,7 @@ def main():
     }
     if dec:
         line["pct_of_hbm_peak"] = round(100 * dec["value"] / HBM_PEAK_GBS, 2)
-        line["roofline"] = {"bound": "hbm", "kernel": DECODE_KERNEL + "<128, 4>",
+        line["roofline"] = {"bound": "hbm", "kernel": DECODE_KERNEL + "<128, 4, false>",
                             "achieved": round(dec["achieved"], 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4),
                             "traffic": dec["traffic"],
