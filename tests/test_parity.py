@@ -678,3 +678,46 @@ def test_persistent_several_tiles_per_workgroup(B, Hq, Hkv, S, wl, attn_options)
                                  True, wl, scale)
         assert_parity(o[b:b + 1, i:i + 1], lse[b:b + 1, :, i:i + 1], ro, rl, "bf16",
                       f"persistent row {b},{i}")
+
+
+# ---------------------------------------------------------------------------
+# the largest sizes the planner takes on one call
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [0, 256])
+def test_decode_256k_keys(S):
+    # 262,144 keys: the planner's 128 splits give 2048 keys per split (eight blocks
+    # per wave, the longest decode pipelines); 256 is the split cap
+    B, Hq, Hkv, Sk, d = 1, 32, 4, 262144, 128
+    pl = tpa.plan(B, Hq, Hkv, 1, Sk, d, False, -1, S, "bf16")
+    assert pl["num_splits"] == (S or 128)
+    run_case("bf16", B, Hq, Hkv, 1, Sk, d, False, -1, S, seed=41)
+
+
+def test_varlen_200_sequences():
+    # more sequences than two 64-lane scan steps of the work-unit search, many short
+    B, Hq, Hkv, Sk, d = 200, 8, 2, 2500, 128
+    q, k, v = small_case(42, "bf16", B, Hq, Hkv, 1, Sk, d)
+    g = torch.Generator().manual_seed(42)
+    seqlens = torch.randint(0, Sk + 1, (B,), generator=g, dtype=torch.int32)
+    seqlens[::17] = 0
+    seqlens[5] = Sk
+    pl = tpa.plan(B, Hq, Hkv, 1, Sk, d, False, -1, 0, "bf16", varlen=True, sum_seqlens_k=int(seqlens.sum()))
+    print(f"varlen 200 sequences plan {pl['grid_x']} units x {pl['grid_y']}, S={pl['num_splits']}", flush=True)
+    ro, rl = oracle.attn_ref(q, k, v, False, -1, 1 / math.sqrt(d), seqlens_k=seqlens)
+    o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV), sum_seqlens_k=int(seqlens.sum()))
+    assert_parity(o, lse, ro, rl, "bf16", "varlen 200 sequences")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_causal_prefill_32k_sampled(d):
+    # 32,768 positions: 128 query blocks per head, the longest key ranges
+    B, H, S = 1, 4, 32768
+    q, k, v = small_case(43, "bf16", B, H, H, S, S, d, std=0.5)
+    scale = 1.0 / math.sqrt(d)
+    print(f"causal prefill 32k d={d}", flush=True)
+    o, lse = tpa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    for i in (0, 255, 256, 16383, 16384, 32511, S - 1):
+        ro, rl = oracle.attn_ref(q[:, i:i + 1], k[:, :i + 1], v[:, :i + 1], True, -1, scale)
+        assert_parity(o[:, i:i + 1], lse[:, :, i:i + 1], ro, rl, "bf16", f"32k row {i} d={d}")
