@@ -133,7 +133,7 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float
  * d_v == d behaves as attn_fwd; otherwise only bf16 with d = 576, d_v = 512
  * is built (ATTN_EUNSUPPORTED else). The query heads of a KV head are always
  * packed into the row dimension ([FA-tiling] §6.3); num_splits <= 0 splits as far
- * as one workgroup per CU allows (the kernel holds one per CU), with at least 128
+ * as one workgroup per CU allows (the kernel holds one per CU), with at least 64
  * keys per split (the fp32 split partials are d_v wide). Other arguments as
  * attn_fwd. */
 int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -472,17 +472,28 @@ def run_latent(B, Hq, Sq, Sk, causal=True, wl=-1, S=0, seed=0):
     assert_parity(o, lse, ro, rl, "bf16", f"latent {B},{Hq},{Sq},{Sk} c={causal} wl={wl} S={S}")
 
 
+# the latent kernel's two forms: 4 waves (all 512 output columns each), 8 waves
+# (a row block's two waves split the output columns)
+MLA_WAVES = pytest.mark.parametrize("mla_waves", [4, 8], ids=["w4", "w8"])
+
+
+@MLA_WAVES
 @pytest.mark.parametrize("shape", LATENT_SHAPES, ids=lambda s: "B%d_H%d_q%d_kv%d" % s)
-def test_latent_verify_shapes(shape):
+def test_latent_verify_shapes(shape, mla_waves, attn_options):
+    attn_options("ATTN_MLA_WAVES", mla_waves)
     run_latent(*shape)
 
 
+@MLA_WAVES
 @pytest.mark.parametrize("S", [1, 2, 3, 7])
-def test_latent_split_sweep(S):
+def test_latent_split_sweep(S, mla_waves, attn_options):
+    attn_options("ATTN_MLA_WAVES", mla_waves)
     run_latent(2, 16, 17, 2065, S=S, seed=1)
 
 
-def test_latent_noncausal_window_and_ragged():
+@MLA_WAVES
+def test_latent_noncausal_window_and_ragged(mla_waves, attn_options):
+    attn_options("ATTN_MLA_WAVES", mla_waves)
     run_latent(1, 8, 5, 77, causal=False, seed=2)           # ragged last key tile
     run_latent(1, 8, 12, 300, causal=True, wl=50, seed=3)   # sliding window
     run_latent(1, 3, 30, 20, causal=True, seed=4)           # Sq > Sk: fully masked rows
@@ -598,8 +609,10 @@ def test_decode_and_verify_values_beyond_fp16_range():
         _assert_scaled_parity(o, lse, q, k, v, False, -1, scale, f"decode S={S}")
 
 
+@MLA_WAVES
 @pytest.mark.parametrize("rows", ["all", "tail"])
-def test_latent_values_beyond_fp16_range(rows):
+def test_latent_values_beyond_fp16_range(rows, mla_waves, attn_options):
+    attn_options("ATTN_MLA_WAVES", mla_waves)
     B, Hq, Sq, Sk = 2, 16, 17, 2065
     q, k, v = latent_case(5, B, Hq, Sq, Sk)
     vf = v.float()

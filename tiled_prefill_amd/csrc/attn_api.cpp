@@ -72,7 +72,8 @@ const OptionDef kOptionDefs[] = {
     {"ATTN_SPLIT_RULE", &Options::split_rule, 0},
     {"ATTN_VARLEN_CHUNK", &Options::varlen_chunk, 1024},
     {"ATTN_VARLEN_UNITS", &Options::varlen_units, 1},
-    {"ATTN_MLA_MIN_CHUNK", &Options::mla_min_chunk, 128},
+    {"ATTN_MLA_MIN_CHUNK", &Options::mla_min_chunk, 64},
+    {"ATTN_MLA_WAVES", &Options::mla_waves, 8},
     {"ATTN_SPLIT_MAJOR", &Options::split_major, -1},
     {"ATTN_COMBINE_COLS", &Options::combine_cols, -1},
     {"ATTN_COMBINE_ROWS", &Options::combine_rows, 1},
@@ -244,8 +245,11 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     const int dv = p.dv > 0 ? p.dv : p.d;
     const FwdVariant* var = nullptr;
     if (dv != p.d) {  // values of their own width: the latent-attention kernel
+        // (ATTN_MLA_WAVES: 4 = each wave owns all output columns of its rows,
+        // 8 = two waves per row block split the output columns)
+        const int want_wn = opt.mla_waves == 8 ? 2 : 1;
         for (const FwdVariant* v = mla_variants(); v->launch; ++v)
-            if (v->dtype == p.dtype && v->d == p.d && v->dv == dv) {
+            if (v->dtype == p.dtype && v->d == p.d && v->dv == dv && v->waves_n == want_wn) {
                 var = v;
                 break;
             }
@@ -381,7 +385,9 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
             // far as one wave of workgroups allows (tiles * S <= CUs; a second,
             // partial wave costs more than the splits save: 65,536 keys, 5 query
             // blocks, 51 splits 161 us vs 64 splits 236 us) and every split keeps
-            // a minimum chunk of 128 keys.
+            // a minimum chunk of 64 keys (the 8-wave form on 2 x 16 heads over 2065
+            // keys: 64-key chunks, 25 splits, 29.7 us per call; 128-key, 16 splits,
+            // 32.4 us).
             const int mc = imax(1, ceil_div(opt.mla_min_chunk, BN));
             S = imin(imax(1, num_cus / t), imax(1, max_blocks / mc));
         } else {

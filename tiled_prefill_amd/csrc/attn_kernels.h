@@ -79,12 +79,13 @@ struct Options {
     int verify_tile;      // ATTN_VERIFY_TILE: 0 widest row tile, 1 32-row 2x2, 2 32-row 2x4
     int f32_dma;          // ATTN_F32_DMA: fp32 on the LDS-copy kernel for 17..32 rows per KV head (1), for 1..32 (2)
     int varlen_units;     // ATTN_VARLEN_UNITS: variable-length decode on the work-unit grid (1)
+    int mla_waves;        // ATTN_MLA_WAVES: latent kernel with 4 waves (all output columns each) or 8
     int f32_waves;        // ATTN_F32_WAVES: that kernel's 8-wave form where d has one (8), else 4 waves
     int min_chunk;        // ATTN_MIN_CHUNK: minimum keys per split (256)
     int wg_per_cu;        // ATTN_WG_PER_CU: workgroup target per CU of the split rule (2)
     int split_rule;       // ATTN_SPLIT_RULE: 0 occupancy, 1 [FA-tiling] 5.2, 2 NSPLIT, 3 occupancy first
     int varlen_chunk;     // ATTN_VARLEN_CHUNK: keys per split of variable-length problems (1024)
-    int mla_min_chunk;    // ATTN_MLA_MIN_CHUNK: minimum keys per split of the latent kernel (128)
+    int mla_min_chunk;    // ATTN_MLA_MIN_CHUNK: minimum keys per split of the latent kernel (64)
     int split_major;      // ATTN_SPLIT_MAJOR: grid order of split workgroups; -1 = by tile
     int combine_cols;     // ATTN_COMBINE_COLS: -1 by split count, 0/1 force split groups / columns
     int combine_rows;     // ATTN_COMBINE_ROWS: 1 row-parallel combine for 512-wide rows

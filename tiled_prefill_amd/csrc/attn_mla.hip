@@ -11,11 +11,15 @@
 //
 // All G = Hq / Hkv query heads of a KV head are packed into the row dimension
 // ([FA-tiling] §6.3: packed row r is query position r / G, head hkv G + r % G),
-// so every K/V tile is read once for all of them. One workgroup: 4 waves x 16
-// packed rows, 32-key tiles, double-buffered in LDS (K 36 KB by DMA, V 32 KB
-// through registers; 136 KB, one workgroup per CU, one wave per SIMD, up to
-// 512 VGPRs: the 576-wide Q^T fragments take 72, the 512-wide O^T accumulators
-// 128). S^T = K Q^T on 16x16x32 bf16 MFMA, online softmax with a lazy
+// so every K/V tile is read once for all of them. One workgroup: 64 packed rows
+// in 4 blocks of 16, 32-key tiles, double-buffered in LDS (K 36 KB by DMA, V 32
+// KB through registers; 136 KB, one workgroup per CU). Two forms: 4 waves, one
+// per row block, each holding the 576-wide Q^T fragments (72 registers) and all
+// 512 output columns (128 accumulators), one wave per SIMD; or 8 waves, the two
+// waves of a row block each computing the block's scores and half of its output
+// columns (64 accumulators, no AGPRs), two waves per SIMD to hide each other's
+// LDS and memory latency -- the QK product runs twice, and the kernel still wins
+// (the latency, not the matrix core, bounds it). S^T = K Q^T on 16x16x32 bf16 MFMA, online softmax with a lazy
 // reference max, O^T += V^T P^T on 16x16x32 bf16 MFMA with V as stored and P
 // as two bf16 parts (P ~= hi + lo to about 16 bits: one bf16 rounding of P
 // would cost up to 2^-9 per term, and fp16 operands would not hold V beyond
@@ -32,9 +36,12 @@
 
 namespace tpa {
 
-template <int DK, int DV>
+template <int DK, int DV, int SV = 1>
 struct MlaTile {
-    static constexpr int NWV = 4, MW = 16, BM = NWV * MW, BN = 32, NTHR = 64 * NWV;
+    // SV = 1: 4 waves, each owning 16 packed rows and all DV output columns;
+    // SV = 2: 8 waves, wave w owning rows 16 (w % 4) .. +15 and half w / 4 of the
+    // output columns (the QK product is computed by both waves of a row block)
+    static constexpr int SV_ = SV, RWV = 4, NWV = RWV * SV, MW = 16, BM = RWV * MW, BN = 32, NTHR = 64 * NWV;
     static constexpr int NSLAB = DK / 32;  // QK contraction slabs
     static constexpr int NT = BN / 16;     // 16-key sub-tiles
     static constexpr int DT = DV / 16;     // 16-wide output d tiles
@@ -44,8 +51,10 @@ struct MlaTile {
     static constexpr int KTILEB = BN * KROWB, VTILEB = BN * VROWB, STAGEB = KTILEB + VTILEB;
     static constexpr int LDS_BYTES = 2 * STAGEB;
     static constexpr int KDMA = KTILEB / 1024;        // wave-wide K DMAs per tile
+    static constexpr int KDMA_PER_WAVE = (KDMA + NWV - 1) / NWV;
     static constexpr int VCH = BN * VCPR / NTHR;      // V chunks per thread per tile
-    static_assert(DK % 32 == 0 && DV % 16 == 0 && KTILEB % 1024 == 0 && KDMA % NWV == 0, "tile shape");
+    static constexpr int DTW = DT / SV;               // output d tiles per wave
+    static_assert(DK % 32 == 0 && DV % (16 * SV) == 0 && KTILEB % 1024 == 0, "tile shape");
     static_assert(BN * VCPR % NTHR == 0, "V tile must split evenly over the threads");
     // LDS chunk swizzles. K rows are 72 chunks: the XOR touches only the low 3
     // bits of the chunk index (the row stays whole); with rows an odd multiple of
@@ -57,15 +66,16 @@ struct MlaTile {
     static __device__ __forceinline__ int vslot(int c, int r) { return c ^ ((r & 7) << 1); }
 };
 
-template <int DK, int DV>
-__global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
-    using C = MlaTile<DK, DV>;
-    constexpr int BN = C::BN, BM = C::BM, NT = C::NT, NSLAB = C::NSLAB, DT = C::DT;
+template <int DK, int DV, int SV>
+__global__ void __launch_bounds__(256 * SV, 1) attn_mla_kernel(FwdParams p) {
+    using C = MlaTile<DK, DV, SV>;
+    constexpr int BN = C::BN, BM = C::BM, NT = C::NT, NSLAB = C::NSLAB, DTW = C::DTW;
     constexpr int KROWB = C::KROWB, VROWB = C::VROWB, KTILEB = C::KTILEB, STAGEB = C::STAGEB;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rw = wave % C::RWV, vh = wave / C::RWV;  // row block, output-column part
     const int li = lane & 15, lg = lane >> 4;
 
     // ---- tile coordinates: XCD-aware one-dimensional grid, heaviest query block first
@@ -97,7 +107,7 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
     const bool has_work = s_hi > s_lo;
 
     // ---- this lane's query row (query column li of the wave's 16) and its keys
-    const int r = m_block * BM + wave * 16 + li;
+    const int r = m_block * BM + rw * 16 + li;
     const bool row_ok = r < nrows;
     const int row_pos = row_ok ? (p.pack ? r / G : r) : 0;
     const int row_head = p.pack ? hkv * G + (row_ok ? r % G : 0) : hg;
@@ -125,9 +135,9 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
         }
     }
 
-    f32x4 oacc[DT], lacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 oacc[DTW], lacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < DT; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < DTW; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0
     const float sl2 = p.scale_log2;
@@ -145,8 +155,9 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
         const rsrc_t rk = make_rsrc(kbase + (size_t)n * BN * k_stride, tile_rows(n) * k_row_bytes);
         char* dst = smem + stage * STAGEB;
 #pragma unroll
-        for (int j = 0; j < C::KDMA / C::NWV; ++j) {
+        for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
             const int i = wave + C::NWV * j;
+            if (C::KDMA % C::NWV != 0 && i >= C::KDMA) break;
             const int f = 64 * i + lane;
             const int rr = f / C::KCPR, slot = f % C::KCPR;
             const uint32_t voff = rr * k_row_bytes + 16 * C::kslot(slot, rr);
@@ -231,7 +242,7 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
             m_run = mx;
             lacc *= alpha;
 #pragma unroll
-            for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
+            for (int u = 0; u < DTW; ++u) oacc[u] *= alpha;
         }
         const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
 #pragma unroll
@@ -253,8 +264,8 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
         const int ra = 4 * lg + (li >> 2), rb = ra + 16;
         const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
 #pragma unroll
-        for (int u = 0; u < DT; ++u) {
-            const int ch = 2 * u + cb;
+        for (int u = 0; u < DTW; ++u) {
+            const int ch = 2 * (vh * DTW + u) + cb;
             const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + ra * VROWB + 16 * C::vslot(ch, ra) + hb));
             const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * VROWB + 16 * C::vslot(ch, rb) + hb));
             const u32x4 vf = {a[0], a[1], c[0], c[1]};
@@ -277,19 +288,20 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
     const float inv = any ? 1.f / l : 0.f;
     const float lse = any ? m_run * p.scale + logf(l) : -INFINITY;
     const size_t row = ((size_t)b * p.Sq + row_pos) * p.Hq + row_head;
+    const int c0 = 16 * DTW * vh;  // this wave's first output column
     if (S > 1) {
         const size_t rows_total = (size_t)p.B * p.Sq * p.Hq;
-        if (lg == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
+        if (lg == 0 && vh == 0) p.lse_part[(size_t)split * rows_total + row] = lse;
         if (any) {
-            float* orow = p.o_part + ((size_t)split * rows_total + row) * DV + 4 * lg;
+            float* orow = p.o_part + ((size_t)split * rows_total + row) * DV + c0 + 4 * lg;
 #pragma unroll
-            for (int u = 0; u < DT; ++u) *reinterpret_cast<f32x4*>(orow + 16 * u) = oacc[u] * inv;
+            for (int u = 0; u < DTW; ++u) *reinterpret_cast<f32x4*>(orow + 16 * u) = oacc[u] * inv;
         }
     } else {
-        if (lg == 0 && p.lse) p.lse[((size_t)b * p.Hq + row_head) * p.Sq + row_pos] = lse;
-        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * DV + 4 * lg;
+        if (lg == 0 && vh == 0 && p.lse) p.lse[((size_t)b * p.Hq + row_head) * p.Sq + row_pos] = lse;
+        bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + row * DV + c0 + 4 * lg;
 #pragma unroll
-        for (int u = 0; u < DT; ++u) {
+        for (int u = 0; u < DTW; ++u) {
             u32x2 w;
             w[0] = pack_bf16x2(oacc[u][0] * inv, oacc[u][1] * inv);
             w[1] = pack_bf16x2(oacc[u][2] * inv, oacc[u][3] * inv);
@@ -298,16 +310,18 @@ __global__ void __launch_bounds__(256, 1) attn_mla_kernel(FwdParams p) {
     }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int SV>
 hipError_t launch_mla(const FwdParams& p, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_mla_kernel<DK, DV>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_mla_kernel<DK, DV, SV>), grid, dim3(256 * SV), 0, stream, p);
     return hipGetLastError();
 }
 
 const FwdVariant* mla_variants() {
     static const FwdVariant v[] = {
         // d = 576, d_v = 512 (latent attention); block_n 32, 4 waves x 16 packed rows
-        {DT_BF16, 576, 64, 32, 4, 1, MlaTile<576, 512>::LDS_BYTES, &launch_mla<576, 512>, 1, 0, 512},
+        {DT_BF16, 576, 64, 32, 4, 1, MlaTile<576, 512>::LDS_BYTES, &launch_mla<576, 512, 1>, 1, 0, 512},
+        // the same rows over 8 waves, each pair of waves splitting the 512 output columns
+        {DT_BF16, 576, 64, 32, 4, 2, MlaTile<576, 512, 2>::LDS_BYTES, &launch_mla<576, 512, 2>, 1, 0, 512},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;
