@@ -66,7 +66,7 @@ const OptionDef kOptionDefs[] = {
     {"ATTN_PREFILL_SKIP", &Options::prefill_skip, 0},
     {"ATTN_VERIFY_TILE", &Options::verify_tile, 1},
     {"ATTN_F32_DMA", &Options::f32_dma, 1},
-    {"ATTN_F32_WAVES", &Options::f32_waves, 8},
+    {"ATTN_F32_WAVES", &Options::f32_waves, 4},
     {"ATTN_MIN_CHUNK", &Options::min_chunk, 256},
     {"ATTN_WG_PER_CU", &Options::wg_per_cu, 2},
     {"ATTN_SPLIT_RULE", &Options::split_rule, 0},
@@ -290,13 +290,14 @@ int make_plan(const Problem& p, int num_cus, Plan* out) {
     // fp32 with at most 32 (packed) query rows per KV head (decode, speculative
     // verify): the kernel that copies K/V into per-wave LDS stages
     // (ATTN_F32_DMA: 1 = for 17..32 rows, 2 = also for decode's 1..16 rows;
-    // ATTN_F32_WAVES: 8 = one LDS stage per wave where d has that form, 4 = two)
+    // ATTN_F32_WAVES: waves per workgroup, 4 or 8 where d has that form)
     if (!var && p.dtype == ATTN_FP32 && head_rows <= 32 && (opt.f32_dma == 2 || (opt.f32_dma == 1 && !decode)))
-        for (const FwdVariant* v = f32_dma_variants(); v->launch; ++v)
-            if (v->d == p.d && (opt.f32_waves == 8 || v->waves_n == 4)) {
-                var = v;
-                break;
-            }
+        for (int pass = 0; pass < 2 && !var; ++pass)
+            for (const FwdVariant* v = f32_dma_variants(); v->launch; ++v)
+                if (v->d == p.d && (pass == 1 || v->waves_n == opt.f32_waves)) {
+                    var = v;
+                    break;
+                }
     // general tile kernel: decode tiles (16 rows) for decode, 32-row tiles when a
     // KV head's query rows (packed) are at most 32, else the widest row tile
     // (ATTN_VERIFY_TILE: 0 = widest row tile, 1 = 32-row tile over 2 x 2 waves,

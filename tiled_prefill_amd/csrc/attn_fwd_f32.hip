@@ -8,14 +8,16 @@
 //                for Blackwell's 188 SMs" (the verify workload: 17 query rows
 //                per head over a 2065-key prefix)
 //
-// One workgroup of 4 waves owns up to 32 (packed) query rows of one (batch,
-// grid head, split). Its key range is cut into 16-key blocks and the waves
-// take them in turn (wave w: blocks w, w + 4, ...), each wave with its own
-// online-softmax state for all 32 rows and its own two LDS stages: K and V of a
+// One workgroup of NW waves (4 or 8) owns up to 32 (packed) query rows of one
+// (batch, grid head, split). Its key range is cut into 16-key blocks and the
+// waves take them in turn (wave w: blocks w, w + NW, ...), each wave with its
+// own online-softmax state for all 32 rows and its own LDS stage: K and V of a
 // block stream straight into LDS by buffer_load ... lds (two or four whole rows
-// per instruction, no registers), the next block's copy in flight while the
-// current one is computed, so no workgroup barrier stands in the loop. The
-// four states are merged through LDS at the end.
+// per instruction, no registers), and the stage is refilled in two parts -- K
+// with the wave's next block once the QK product has read it, V once P.V has --
+// so the next block's copy overlaps the current block's softmax and P.V, and no
+// workgroup barrier stands in the loop. The states are merged through LDS at
+// the end. Four waves take 80 KB of LDS at d = 128, so two workgroups fit a CU.
 //
 // Products on the fp32 16x16x4 MFMA, transposed so that the query rows sit on
 // the N axis:
@@ -39,10 +41,7 @@ namespace tpa {
 
 template <int D, int NW_ = 4>
 struct F32DmaTile {
-    // NW_ waves; 4: two LDS stages per wave (the next block's copy in flight while
-    // one is computed); 8: one stage per wave, refilled in two parts (K after the
-    // QK product, V after P.V), two waves per SIMD
-    static constexpr int NW = NW_, NTHR = 64 * NW, STAGES = NW_ == 4 ? 2 : 1;
+    static constexpr int NW = NW_, NTHR = 64 * NW;
     static constexpr int BM = 32, NQ = 2;      // query rows per workgroup, 16-row column blocks
     static constexpr int KB = 16;              // keys per block (one wave's unit of work)
     static constexpr int ROWB = 4 * D;         // bytes per K / V row
@@ -51,7 +50,7 @@ struct F32DmaTile {
     static constexpr int NL = KB / RPI;        // copies per block (K or V)
     static constexpr int BLKB = KB * ROWB;     // bytes of one K (or V) block
     static constexpr int STAGEB = 2 * BLKB;    // K + V
-    static constexpr int WAVEB = STAGES * STAGEB;
+    static constexpr int WAVEB = STAGEB;
     static constexpr int QB = BM * ROWB;       // the workgroup's query rows
     static constexpr int NQL = QB / 1024 / NW; // query-row copies per wave
     static constexpr int DL = D / 4, QV = DL / 4;  // d per lane group, 16-byte vectors of it
@@ -66,16 +65,15 @@ struct F32DmaTile {
 };
 
 template <int D, int NW_>
-__global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams p) {
+__global__ void __launch_bounds__(64 * NW_, NW_ == 4 ? 2 : 1) attn_fwd_f32_dma_kernel(FwdParams p) {
     using C = F32DmaTile<D, NW_>;
-    constexpr bool ONE = C::STAGES == 1;
     constexpr int BM = C::BM, NQ = C::NQ, KB = C::KB, ROWB = C::ROWB, CPR = C::CPR, RPI = C::RPI;
     constexpr int NL = C::NL, QV = C::QV, DT = C::DT, NW = C::NW;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
-    char* wbuf = smem + wave * C::WAVEB;     // this wave's two stages (K then V each)
+    char* wbuf = smem + wave * C::WAVEB;     // this wave's stage (K then V)
     char* qs = smem + NW * C::WAVEB;         // the workgroup's query rows (K's swizzle)
 
     // ---- tile: (query block, grid head x split, batch); heaviest query block first
@@ -105,10 +103,10 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
     // copy i of a block fills LDS bytes [1024 i + 16 l, +16) for lane l: key row
     // RPI i + l / CPR, slot l % CPR, which holds chunk slot ^ swz(row); rows at
     // or past Skb lie outside the buffer resource and read as zeros
-    auto copy_part = [&](int n, int stage, const bool is_v) {
+    auto copy_part = [&](int n, const bool is_v) {
         const uint32_t valid = (uint32_t)imax(0, imin(KB, Skb - n * KB));
         const u32x4 rs = rsrc_words_u((is_v ? vbase : kbase) + (size_t)n * KB * kv_stride, valid * row_bytes);
-        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(wbuf + stage * C::STAGEB + (is_v ? C::BLKB : 0)));
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(wbuf + (is_v ? C::BLKB : 0)));
         const int r0 = lane / CPR, slot = lane % CPR;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
@@ -117,15 +115,15 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
             dma16_untracked(rs, rr * row_bytes + 16 * (slot ^ sw), l0 + 1024 * i);
         }
     };
-    auto copy_block = [&](int n, int stage) {
-        copy_part(n, stage, false);
-        copy_part(n, stage, true);
+    auto copy_block = [&](int n) {
+        copy_part(n, false);
+        copy_part(n, true);
     };
 
     // this wave's blocks: n = s_lo + wave + NW j
     int n = s_lo + wave;
-    const bool first = n < s_hi, second = !ONE && n + NW < s_hi;
-    if (first) copy_block(n, 0);
+    const bool first = n < s_hi;
+    if (first) copy_block(n);
     // the query rows: wave w copies rows [BM w / NW, BM (w + 1) / NW); row r of the
     // tile is packed row m_block BM + r; rows the tile does not own read zeros
     {
@@ -145,7 +143,6 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
             dma16_untracked(rq, off, l0 + 1024 * ci);
         }
     }
-    if (second) copy_block(n + NW, 1);
 
     // ---- this lane's query rows and their visible key intervals
     int row_pos[NQ], row_head[NQ], row_lo[NQ], row_span[NQ];
@@ -174,8 +171,7 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
     whi = row16_imin(whi);
 
     // the query rows have landed (and block n, copied before them) in every wave
-    if (second) wait_vmcnt<2 * NL>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();
     __syncthreads();
     // Q^T fragments: lane (i, g) holds Q[row 16 q + i][g D/4 + 4 c .. + 3]
     f32x4 qf[NQ][QV];
@@ -199,13 +195,10 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
     const float sl2 = p.scale_log2;
     constexpr float LAZY = 8.f;  // the reference max moves only when a score exceeds it by 2^8
 
-    int stage = 0;
     for (; n < s_hi; n += NW) {
-        const bool next = n + NW < s_hi;        // two stages: in flight behind this block
-        if constexpr (ONE) wait_vmcnt<NL>();    // this block's K (its V may still stream)
-        else if (next) wait_vmcnt<2 * NL>();
-        else wait_vmcnt<0>();
-        const char* kt = wbuf + stage * C::STAGEB;
+        const bool next = n + NW < s_hi;  // the wave has a further block
+        wait_vmcnt<NL>();                 // this block's K (its V may still stream)
+        const char* kt = wbuf;
         const char* vt = kt + C::BLKB;
 
         // S^T = K . Q^T over this block's 16 keys
@@ -221,11 +214,9 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sacc[q] = mfma_f32(kv[e], qf[q][c][e], sacc[q]);
         }
-        if constexpr (ONE) {  // one stage: refill K with the wave's next block once read
-            if (next) {
-                wait_lgkmcnt0();
-                copy_part(n + NW, 0, false);
-            }
+        if (next) {  // refill K with the wave's next block once read
+            wait_lgkmcnt0();
+            copy_part(n + NW, false);
         }
 
         // mask the keys a row cannot see (only blocks that cut a row's interval)
@@ -263,10 +254,8 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
         }
 
         // O^T += V^T . P^T: MFMA e contracts keys 4 g + e over the lane groups g
-        if constexpr (ONE) {  // this block's V (behind it only the next K, if any)
-            if (next) wait_vmcnt<NL>();
-            else wait_vmcnt<0>();
-        }
+        if (next) wait_vmcnt<NL>();  // this block's V (behind it only the next K, if any)
+        else wait_vmcnt<0>();
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
             float vf[4];
@@ -282,23 +271,15 @@ __global__ void __launch_bounds__(64 * NW_, 1) attn_fwd_f32_dma_kernel(FwdParams
                 for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f32(vf[e], sacc[q][e], oacc[u][q]);
         }
 
-        if constexpr (ONE) {  // refill V with the next block once read
-            if (next) {
-                wait_lgkmcnt0();
-                copy_part(n + NW, 0, true);
-            }
-        } else {  // refill this stage with the block after next once its reads are done
-            if (n + 2 * NW < s_hi) {
-                wait_lgkmcnt0();
-                copy_block(n + 2 * NW, stage);
-            }
-            stage ^= 1;
+        if (next) {  // refill V with the next block once read
+            wait_lgkmcnt0();
+            copy_part(n + NW, true);
         }
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) l_run[q] = xor_sum(l_run[q]);
 
-    // ---- merge the four waves' states; wave w merges and writes the d tiles
+    // ---- merge the waves' states; wave w merges and writes the d tiles
     // [w DT / NW, (w + 1) DT / NW) of every row
     constexpr int DW = DT / NW, OV = DT * 4;
     __syncthreads();
@@ -368,11 +349,11 @@ hipError_t launch_fwd_f32_dma(const FwdParams& p, dim3 grid, hipStream_t stream)
 
 const FwdVariant* f32_dma_variants() {
     static const FwdVariant v[] = {
-        // 32 query rows, 16-key blocks taken by the waves in turn: 8 waves with one
-        // LDS stage each (d = 128), or 4 with two
-        {DT_FP32, 128, 32, 16, 1, 8, F32DmaTile<128, 8>::LDS_BYTES, &launch_fwd_f32_dma<128, 8>, 0},
+        // 32 query rows, 16-key blocks taken by the waves in turn, one LDS stage per
+        // wave: 4 waves (two workgroups per CU fit), or 8 (one per CU, d = 128)
         {DT_FP32, 128, 32, 16, 1, 4, F32DmaTile<128, 4>::LDS_BYTES, &launch_fwd_f32_dma<128, 4>, 0},
         {DT_FP32, 64, 32, 16, 1, 4, F32DmaTile<64, 4>::LDS_BYTES, &launch_fwd_f32_dma<64, 4>, 0},
+        {DT_FP32, 128, 32, 16, 1, 8, F32DmaTile<128, 8>::LDS_BYTES, &launch_fwd_f32_dma<128, 8>, 0},
         {0, 0, 0, 0, 0, 0, 0, nullptr, 0},
     };
     return v;

@@ -80,7 +80,7 @@ struct Options {
     int f32_dma;          // ATTN_F32_DMA: fp32 on the LDS-copy kernel for 17..32 rows per KV head (1), for 1..32 (2)
     int varlen_units;     // ATTN_VARLEN_UNITS: variable-length decode on the work-unit grid (1)
     int mla_waves;        // ATTN_MLA_WAVES: latent kernel with 4 waves (all output columns each) or 8
-    int f32_waves;        // ATTN_F32_WAVES: that kernel's 8-wave form where d has one (8), else 4 waves
+    int f32_waves;        // ATTN_F32_WAVES: that kernel's waves per workgroup (4; 8 where d has that form)
     int min_chunk;        // ATTN_MIN_CHUNK: minimum keys per split (256)
     int wg_per_cu;        // ATTN_WG_PER_CU: workgroup target per CU of the split rule (2)
     int split_rule;       // ATTN_SPLIT_RULE: 0 occupancy, 1 [FA-tiling] 5.2, 2 NSPLIT, 3 occupancy first
