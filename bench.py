@@ -233,8 +233,17 @@ def algorithmic_bytes(kernel: str, workload: str):
     and write O + lse, or the split partials; the combine reads the partials and
     writes O + lse; the backward's key-block and query-block kernels read Q, dO,
     K, V and the two per-row vectors and write dK + dV, or dQ."""
-    from workloads import WORKLOADS, BWD_WORKLOADS, make_inputs
+    from workloads import WORKLOADS, BWD_WORKLOADS, LATENT_WORKLOADS, make_inputs
     import tiled_prefill_amd as tpa
+    if workload in LATENT_WORKLOADS:  # keys 576 wide, values 512, one shared KV head
+        B, Hq, Sq, Sk = LATENT_WORKLOADS[workload]
+        rows = B * Sq * Hq
+        plan = tpa.plan_dv(B, Hq, 1, Sq, Sk, 576, 512, True, -1, 0, "bf16")
+        part = plan["num_splits"] * rows * (512 + 1) * 4 if plan["num_splits"] > 1 else 0
+        o_bytes = rows * 512 * 2 + rows * 4
+        if kernel.startswith("lse_combine"):
+            return part, o_bytes
+        return rows * 576 * 2 + B * Sk * (576 + 512) * 2, part or o_bytes
     w = WORKLOADS.get(workload) or BWD_WORKLOADS.get(workload)
     if w is None:
         return None
