@@ -193,6 +193,17 @@ __device__ __forceinline__ void dma16_untracked(u32x4 rs, uint32_t voff, uint32_
         : "v"(voff), "s"(rs), "{m0}"(lds)
         : "memory");
 }
+// The same copy without the non-temporal hint, for tiles that other workgroups
+// read again soon from L2 (the prefill's K tiles are shared by a head's query
+// blocks).
+__device__ __forceinline__ void dma16_untracked_cached(u32x4 rs, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rs), "{m0}"(lds)
+        : "memory");
+}
 // s_waitcnt written as a compiler memory barrier (no load or store moves across
 // it), for the copies above that the compiler does not track
 template <int N>
