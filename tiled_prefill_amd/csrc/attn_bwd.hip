@@ -1107,39 +1107,42 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
 
     const uint32_t row_bytes = (uint32_t)((size_t)p.Hq * D * 2);
     // DMA of query block it into stage st: Q and dO rows (KDMA_PER_WAVE per wave
-    // each), then lse2 and D (one 4-byte-per-lane DMA each, waves 0 and 1)
+    // each), then lse2 and D (one 4-byte-per-lane DMA each, waves 0 and 1).
+    // Issued untracked: the compiler's own tracking cannot tell the two stages
+    // apart and waited for the next block's copies early in every block; the one
+    // vmcnt(0) wait before the block's barrier orders them before their reads.
     auto load_block = [&](int it, int st) {
         const int g = it / nm, m = m_lo + it % nm;
         const int hq = hkv * G + g;
         const int valid = imin(BM, Sq - m * BM);
         const size_t row0 = ((size_t)b * Sq + m * BM) * p.Hq + hq;
-        const rsrc_t rq = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.q) + row0 * D, (uint32_t)valid * row_bytes);
-        const rsrc_t rg = make_rsrc_u(reinterpret_cast<const bf16_t*>(p.dout) + row0 * D, (uint32_t)valid * row_bytes);
-        char* dq_ = smem + st * STAGEB;
-        char* dg_ = dq_ + TILEB;
+        const u32x4 rq = rsrc_words_u(reinterpret_cast<const bf16_t*>(p.q) + row0 * D, (uint32_t)valid * row_bytes);
+        const u32x4 rg = rsrc_words_u(reinterpret_cast<const bf16_t*>(p.dout) + row0 * D, (uint32_t)valid * row_bytes);
+        const uint32_t lq = __builtin_amdgcn_readfirstlane(lds_addr(smem + st * STAGEB));
+        const uint32_t lg_ = lq + TILEB;
 #pragma unroll
         for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
             const int i = wave * C::KDMA_PER_WAVE + j;
             const int rr = C::KROWS * i + lane / CPR;
             const uint32_t voff = rr * row_bytes + 16 * ((lane % CPR) ^ C::swz(rr));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rq, (__attribute__((address_space(3))) void*)(dq_ + 1024 * i), 16, voff, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rg, (__attribute__((address_space(3))) void*)(dg_ + 1024 * i), 16, voff, 0, 0, 0);
+            dma16_untracked_cached(rq, voff, lq + 1024 * i);
+            dma16_untracked_cached(rg, voff, lg_ + 1024 * i);
         }
         if (wave < 2) {
             const float* src = (wave == 0 ? p.lse2 : p.dsum) + ((size_t)b * p.Hq + hq) * Sq + m * BM;
-            const rsrc_t rl = make_rsrc_u(src, (uint32_t)valid * 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rl, (__attribute__((address_space(3))) void*)(dg_ + TILEB + wave * BM * 4), 4,
-                4 * lane, 0, 0, 0);
+            const u32x4 rl = rsrc_words_u(src, (uint32_t)valid * 4);
+            dma4_untracked_cached(rl, 4 * lane, lg_ + TILEB + wave * BM * 4);
         }
     };
 
     if (total > 0) {
         load_block(0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        wait_vmcnt<0>();
     }
+    // (the compiler's own record: the K and V register loads above have landed,
+    // so it places no wait for them inside the loop, where the hardware count
+    // would include the next block's copies)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 
     const float sl2 = p.scale_log2;
@@ -1234,7 +1237,7 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next block has landed
+        wait_vmcnt<0>();  // the next block has landed
         __syncthreads();
         st ^= 1;
     }

@@ -204,6 +204,16 @@ __device__ __forceinline__ void dma16_untracked_cached(u32x4 rs, uint32_t voff, 
         : "v"(voff), "s"(rs), "{m0}"(lds)
         : "memory");
 }
+// 4 bytes per lane (buffer_load_dword ... lds): lane l writes LDS bytes
+// [lds + 4 l, +4).
+__device__ __forceinline__ void dma4_untracked_cached(u32x4 rs, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dword %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rs), "{m0}"(lds)
+        : "memory");
+}
 // s_waitcnt written as a compiler memory barrier (no load or store moves across
 // it), for the copies above that the compiler does not track
 template <int N>

@@ -151,9 +151,12 @@ __global__ void __launch_bounds__(256 * SV, 1) attn_mla_kernel(FwdParams p) {
     auto tile_rows = [&](int n) { return (uint32_t)imin(BN, Skb - n * BN); };
     // K DMA i fills LDS bytes [1024 i, 1024 i + 1024): flat chunk f = 64 i + lane is
     // row f / KCPR, slot f % KCPR, which holds the row's chunk kslot(slot, row)
+    // (issued untracked: the compiler's tracking cannot tell the stages apart and
+    // waited for the next tile's copy before the current tile's P.V reads; the
+    // vmcnt(0) wait before the tile's barrier orders the copy before its reads)
     auto load_k = [&](int n, int stage) {
-        const rsrc_t rk = make_rsrc(kbase + (size_t)n * BN * k_stride, tile_rows(n) * k_row_bytes);
-        char* dst = smem + stage * STAGEB;
+        const u32x4 rk = rsrc_words_u(kbase + (size_t)n * BN * k_stride, tile_rows(n) * k_row_bytes);
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(smem + stage * STAGEB));
 #pragma unroll
         for (int j = 0; j < C::KDMA_PER_WAVE; ++j) {
             const int i = wave + C::NWV * j;
@@ -161,8 +164,7 @@ __global__ void __launch_bounds__(256 * SV, 1) attn_mla_kernel(FwdParams p) {
             const int f = 64 * i + lane;
             const int rr = f / C::KCPR, slot = f % C::KCPR;
             const uint32_t voff = rr * k_row_bytes + 16 * C::kslot(slot, rr);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, voff, 0, 0, 0);
+            dma16_untracked_cached(rk, voff, l0 + 1024 * i);
         }
     };
     u32x4 vst[C::VCH];
@@ -188,7 +190,7 @@ __global__ void __launch_bounds__(256 * SV, 1) attn_mla_kernel(FwdParams p) {
         load_k(s_hi - 1, 0);
         load_v(s_hi - 1);
         store_v(0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the K DMAs have landed
+        wait_vmcnt<0>();  // the K copies have landed
     }
     __syncthreads();
 
@@ -275,7 +277,7 @@ __global__ void __launch_bounds__(256 * SV, 1) attn_mla_kernel(FwdParams p) {
 
         if (more) {
             store_v(stage ^ 1);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K DMAs landed
+            wait_vmcnt<0>();  // this wave's K copies landed
         }
         __syncthreads();
         stage ^= 1;
