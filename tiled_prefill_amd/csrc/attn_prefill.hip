@@ -4,11 +4,12 @@
 //   [FA-tiling]  "分块策略与调度" (FlashAttention tiling strategy and scheduling)
 //
 // One workgroup of NWV waves owns BM = NWV * MW query rows of one (batch, query
-// head[, split]) and walks its key-block range ([FA-tiling] §3) from the last
-// block to the first. Per 64-key tile:
+// head[, split]) and walks its key-block range ([FA-tiling] §3) from the first
+// block to the last, so the query blocks of a head, which run together on one
+// XCD, move over its K/V tiles in step and share them in L2. Per 64-key tile:
 //   * K (bf16) streams from global memory straight into LDS (buffer_load ...
 //     lds), V is loaded into registers, converted to fp16 and written to LDS;
-//     both double-buffered, so tile n-1 loads while tile n computes, with one
+//     both double-buffered, so tile n+1 loads while tile n computes, with one
 //     workgroup barrier per tile;
 //   * S^T = K Q^T on 16x16x32 bf16 MFMA (Q^T stays in registers);
 //   * online softmax in fp32 (row max over the 4 lanes of a query column with
@@ -28,8 +29,9 @@
 //
 // Grid: one dimension over all tiles. Workgroups are dealt round-robin to the 8
 // XCDs, so tile t is placed on XCD (t / per_xcd): the query blocks of one head
-// share one XCD's L2 and its K/V are fetched from HBM about once. Within a head
-// the query blocks run heaviest first ([FA-tiling] §4.4).
+// share one XCD's L2 (HBM fetch 1.9x the algorithmic bytes on the causal
+// 8192-position prefill; 4.6x when the keys were walked downward). Within a
+// head the query blocks run heaviest first ([FA-tiling] §4.4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -252,8 +254,8 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     };
 
     if (has_work) {
-        load_k(s_hi - 1, 0);
-        load_v(s_hi - 1);
+        load_k(s_lo, 0);
+        load_v(s_lo);
         store_v(0);
         wait_vmcnt<0>();  // the K copies have landed
     }
@@ -373,11 +375,11 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     bool steady = false;  // every row of the wave has a finite reference max
     bool redo = false;    // this tile runs again with the exact max
     int stage = 0;
-    for (int n = s_hi - 1; n >= s_lo;) {
-        const bool more = n > s_lo;
-        if (more && !redo) {  // prefetch the next (lower) tile into the other stage
-            load_k(n - 1, stage ^ 1);
-            if constexpr (!VB) load_v(n - 1);
+    for (int n = s_lo; n < s_hi;) {
+        const bool more = n + 1 < s_hi;
+        if (more && !redo) {  // prefetch the next (higher) tile into the other stage
+            load_k(n + 1, stage ^ 1);
+            if constexpr (!VB) load_v(n + 1);
         }
         const char* kt = smem + stage * STAGEB;
         const char* vt = kt + TILEB;
@@ -456,13 +458,13 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
             // (the bf16 form, which runs only when a V element is beyond fp16's
             // range, loads V here rather than ahead, so its registers are not
             // live across the tile and the kernel needs no more of them)
-            if constexpr (VB) load_v(n - 1);
+            if constexpr (VB) load_v(n + 1);
             store_v(stage ^ 1);
             wait_vmcnt<0>();  // this wave's K copies landed
         }
         __syncthreads();
         stage ^= 1;
-        --n;
+        ++n;
     }
 
     // ---- epilogue. fp16 form: finite inputs give finite accumulators unless a V
