@@ -160,6 +160,40 @@ def test_small_shapes(case):
     run_case(*case, seed=3)
 
 
+def _random_cases(n, seed):
+    """n forward problems from a fixed generator, spanning every kernel family
+    (decode tiles, the fp32 verify kernel, prefill tiles, the general kernel):
+    GQA groups of 1..8 heads (3 included), ragged query and key counts (more
+    queries than keys too), both masks and windows, automatic and forced split
+    counts; each small enough for the oracle to take well under a second."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = "bf16" if rng.random() < 0.65 else "fp32"
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        B = int(rng.integers(1, 4))
+        kind = rng.random()
+        Sq = 1 if kind < 0.25 else (int(rng.integers(2, 33)) if kind < 0.5 else int(rng.integers(33, 600)))
+        Sk = int(rng.integers(1, 1500))
+        causal = bool(rng.random() < 0.6)
+        wl = -1 if rng.random() < 0.6 else int(rng.integers(0, Sk + 1))
+        S = 0 if rng.random() < 0.6 else int(rng.integers(1, 10))
+        if B * Hkv * G * Sq * Sk * d > 1e8:
+            continue
+        cases.append((dtype, B, Hkv * G, Hkv, Sq, Sk, d, causal, wl, S))
+    return cases
+
+
+RANDOM = _random_cases(96, 20261203)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=lambda c: "%s_B%d_H%d-%d_q%d_k%d_d%d_c%d_w%d_S%d" % c)
+def test_random_shapes(case):
+    run_case(*case, seed=7)
+
+
 def test_empty_keys_give_masked_rows():
     for dtype in ("fp32", "bf16"):
         q, k, v = small_case(4, dtype, 1, 4, 2, 3, 0, 64)
@@ -270,6 +304,46 @@ def test_varlen_small():
         o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV), num_splits=S,
                                 sum_seqlens_k=int(seqlens.sum()))
         assert_parity(o, lse, ro, rl, "bf16", f"varlen S={S}")
+
+
+def _random_varlen(n, seed):
+    """variable-length decode batches from a fixed generator: 2..24 sequences,
+    1 or 2 query positions, GQA groups of 1..8 heads, both head dims, both masks
+    and windows, automatic and forced split counts"""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        B = int(rng.integers(2, 25))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Sq = int(rng.choice([1, 2]))
+        Sk = int(rng.integers(64, 4000))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.random() < 0.5)
+        wl = -1 if rng.random() < 0.7 else int(rng.integers(0, Sk + 1))
+        S = 0 if rng.random() < 0.7 else int(rng.integers(1, 17))
+        if B * Hkv * G * Sq * Sk * d > 1e8:
+            continue
+        cases.append((B, Hkv * G, Hkv, Sq, Sk, d, causal, wl, S, int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_varlen(12, 5077),
+                         ids=lambda c: "B%d_H%d-%d_q%d_k%d_d%d_c%d_w%d_S%d_%d" % c)
+def test_varlen_random_batches(case):
+    B, Hq, Hkv, Sq, Sk, d, causal, wl, S, lseed = case
+    q, k, v = small_case(lseed % 1000, "bf16", B, Hq, Hkv, Sq, Sk, d)
+    g = torch.Generator().manual_seed(lseed)
+    seqlens = torch.randint(0, Sk + 1, (B,), generator=g, dtype=torch.int32)
+    seqlens[0] = Sk
+    seqlens[B // 2] = 0
+    print(f"varlen random {case} lengths {seqlens.tolist()}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = tpa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), seqlens.to(DEV), causal=causal,
+                            window_left=wl, scale=scale, num_splits=S, sum_seqlens_k=int(seqlens.sum()))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_ref(q, k, v, causal, wl, scale, seqlens_k=seqlens)
+    assert_parity(o, lse, ro, rl, "bf16", f"varlen random {case}")
 
 
 @pytest.mark.parametrize("units", [1, 0], ids=["unit_grid", "split_grid"])
@@ -497,6 +571,33 @@ def test_latent_noncausal_window_and_ragged(mla_waves, attn_options):
     run_latent(1, 8, 5, 77, causal=False, seed=2)           # ragged last key tile
     run_latent(1, 8, 12, 300, causal=True, wl=50, seed=3)   # sliding window
     run_latent(1, 3, 30, 20, causal=True, seed=4)           # Sq > Sk: fully masked rows
+
+
+def _random_latent(n, seed):
+    """latent-width problems (keys 576, values 512, one KV head) from a fixed
+    generator: 1..16 heads, 1..40 query positions, ragged key counts, both masks
+    and windows, automatic and forced split counts"""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        B = int(rng.integers(1, 3))
+        Hq = int(rng.integers(1, 17))
+        Sq = int(rng.integers(1, 41))
+        Sk = int(rng.integers(1, 3000))
+        causal = bool(rng.random() < 0.7)
+        wl = -1 if rng.random() < 0.7 else int(rng.integers(0, Sk + 1))
+        S = 0 if rng.random() < 0.6 else int(rng.integers(1, 9))
+        if B * Hq * Sq * Sk > 4e5:
+            continue
+        cases.append((B, Hq, Sq, Sk, causal, wl, S))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_latent(16, 7031),
+                         ids=lambda c: "B%d_H%d_q%d_k%d_c%d_w%d_S%d" % c)
+def test_latent_random_shapes(case):
+    B, Hq, Sq, Sk, causal, wl, S = case
+    run_latent(B, Hq, Sq, Sk, causal=causal, wl=wl, S=S, seed=9)
 
 
 def test_latent_long_prefix_sampled():
