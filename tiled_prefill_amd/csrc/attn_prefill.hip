@@ -177,10 +177,14 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     // all-ones A operand turns a PV-shaped MFMA into sum_j P[j][i] for every lane
     // of query column i, which also keeps l consistent with the fp16-rounded P.
     f32x4 oacc[DT][NQ];
-    float m_run[NQ], l_run[NQ];
+    // m_run: the reference max of each row; negm = -m_run * scale * log2(e), the
+    // exponent offset of P, kept beside it (0 while the row has no reference) so
+    // a steady tile does not recompute it
+    float m_run[NQ], l_run[NQ], negm[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         m_run[q] = -INFINITY;
+        negm[q] = 0.f;
         l_run[q] = 0.f;
 #pragma unroll
         for (int u = 0; u < DT; ++u) oacc[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -325,6 +329,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
                 if (!raise[q]) continue;
                 const float alpha = m_run[q] == -INFINITY ? 0.f : fast_exp2((m_run[q] - mxs[q]) * sl2);
                 m_run[q] = mxs[q];
+                negm[q] = -mxs[q] * sl2;
                 l_run[q] *= alpha;
 #pragma unroll
                 for (int u = 0; u < DT; ++u) oacc[u][q] *= alpha;
@@ -339,7 +344,7 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
     auto exps = [&]() {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const float neg = m_run[q] == -INFINITY ? 0.f : -m_run[q] * sl2;
+            const float neg = negm[q];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
