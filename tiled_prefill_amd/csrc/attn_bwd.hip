@@ -929,7 +929,10 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
         // per 32-key half of the tile: S^T = K Q^T and dP^T = V dO^T (lane group lg
         // contracts d in [lg DL, (lg+1) DL)), then P^T, dS^T and dQ^T += K^T dS^T
         const int key0 = n * BN;
-        const bool full = key0 >= wlo && key0 + BN - 1 <= whi;
+        // every row of the wave sees the whole tile (wave-uniform, so the masked
+        // path below is one scalar branch per half tile, not a divergent branch
+        // per element)
+        const bool full = __builtin_amdgcn_ballot_w64(!(key0 >= wlo && key0 + BN - 1 <= whi)) == 0;
 #pragma unroll
         for (int pp = 0; pp < NT / 2; ++pp) {
             f32x4 sacc[2][NQW], pacc[2][NQW];
@@ -955,17 +958,24 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dq_dma_kernel(BwdParams p) 
                     }
                 }
             }
+            if (!full) {  // -inf on the scores a row cannot see (P = 0 there)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int qq = 0; qq < NQW; ++qq)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = key0 + 16 * (2 * pp + h) + 4 * lg + r;
+                            if ((key < row_lo[qq]) | (key > row_hi[qq])) sacc[h][qq][r] = -INFINITY;
+                        }
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int qq = 0; qq < NQW; ++qq)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float pv = fast_exp2(fmaf(sacc[h][qq][r], sl2, -l2[qq]));
-                        if (!full) {
-                            const int key = key0 + 16 * (2 * pp + h) + 4 * lg + r;
-                            pv = (key < row_lo[qq] || key > row_hi[qq]) ? 0.f : pv;
-                        }
+                        const float pv = fast_exp2(fmaf(sacc[h][qq][r], sl2, -l2[qq]));
                         if constexpr (ROWSUM) dacc[qq] += pv * pacc[h][qq][r];
                         else pacc[h][qq][r] = pv * (pacc[h][qq][r] - dsum[qq]);
                     }
@@ -1162,8 +1172,11 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
         const int kk0 = key0 + kw0;
         const int row0 = m * BM;
         const int row1 = imin(row0 + BM, Sq) - 1;
-        const bool full = kk0 + NKW <= Sk && (!p.causal || kk0 + NKW - 1 <= row0 + delta) &&
-                          (p.window_left < 0 || kk0 >= row1 + delta - p.window_left);
+        // every (row, key) pair of the wave's block is visible (wave-uniform, so the
+        // masked path below is one scalar branch per half block)
+        const bool full = __builtin_amdgcn_readfirstlane(
+                              (kk0 + NKW <= Sk) & (!p.causal | (kk0 + NKW - 1 <= row0 + delta)) &
+                              ((p.window_left < 0) | (kk0 >= row1 + delta - p.window_left))) != 0;
 #pragma unroll
         for (int pp = 0; pp < BM / 32; ++pp) {
             f32x4 sacc[2][NT], pacc[2][NT];
@@ -1188,6 +1201,21 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
                         pacc[h][t] = mfma_bf16(ga, vf[t][c], pacc[h][t]);
                     }
                 }
+            if (!full) {  // -inf on the pairs that are not visible (P = 0 there)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int key = kk0 + 16 * t + li;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int pos = row0 + 16 * (2 * pp + h) + 4 * lg + r;
+                            const bool vis = (key < Sk) & (!p.causal | (key <= pos + delta)) &
+                                             ((p.window_left < 0) | (key >= pos + delta - p.window_left));
+                            if (!vis) sacc[h][t][r] = -INFINITY;
+                        }
+                    }
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int qb = 2 * pp + h;
@@ -1195,16 +1223,9 @@ __global__ void __launch_bounds__(256, OCC) attn_bwd_dkdv_dma_kernel(BwdParams p
                 const f32x4 dsv = *reinterpret_cast<const f32x4*>(lds_dsum + 16 * qb + 4 * lg);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int key = kk0 + 16 * t + li;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float pv = fast_exp2(fmaf(sacc[h][t][r], sl2, -lv[r]));
-                        if (!full) {
-                            const int pos = row0 + 16 * qb + 4 * lg + r;
-                            const bool vis = key < Sk && (!p.causal || key <= pos + delta) &&
-                                             (p.window_left < 0 || key >= pos + delta - p.window_left);
-                            pv = vis ? pv : 0.f;
-                        }
+                        const float pv = fast_exp2(fmaf(sacc[h][t][r], sl2, -lv[r]));
                         sacc[h][t][r] = pv;
                         pacc[h][t][r] = pv * (pacc[h][t][r] - dsv[r]);
                     }
