@@ -161,6 +161,11 @@ int attn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int
                     int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
                     attn_plan_t* out);
 
+/* attn_plan_fwd under its shorter name: the same arguments, checks and plan. */
+int attn_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+              int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
+              attn_plan_t* out);
+
 /* Backward pass: gradients of L = <dout, o> for o = attention(q, k, v) with the
  * mask of attn_fwd ([FA-tiling] §3.4: one workgroup per key block, looping
  * over the query blocks that see it -- get_m_block_min_max -- and the query

@@ -18,7 +18,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("attn_fwd", "attn_fwd_varlen", "attn_plan_fwd", "attn_workspace_bytes",
+    for required in ("attn_fwd", "attn_fwd_varlen", "attn_plan", "attn_plan_fwd", "attn_workspace_bytes",
                      "attn_set_workspace", "attn_lse_combine", "attn_last_error",
                      "attn_set_option", "attn_get_option"):
         assert required in names
@@ -194,3 +194,17 @@ def test_stream_read_rejects_bad_buffers():
     assert lib.attn_stream_read(FAKE + 4, 1024, 0, FAKE, None) == -1   # misaligned
     assert lib.attn_stream_read(FAKE, 1 << 34, 4, FAKE, None) == -1    # > 2 GiB per workgroup
     assert lib.attn_stream_read(FAKE, 0, 0, FAKE, None) == 0           # nothing to read
+
+
+def test_attn_plan_is_attn_plan_fwd():
+    lib = tpa.load()
+    for args in [(1, 32, 4, 1, 32768, 128, 0, -1, 0, tpa.BF16, 0, -1, 256),
+                 (1, 32, 32, 8192, 8192, 128, 1, -1, 0, tpa.BF16, 0, -1, 256),
+                 (16, 32, 8, 1, 16384, 128, 0, -1, 0, tpa.BF16, 1, 135000, 256),
+                 (2, 16, 16, 17, 2065, 128, 1, -1, 0, tpa.FP32, 0, -1, 256),
+                 (1, 4, 3, 8, 8, 64, 0, -1, 0, tpa.BF16, 0, -1, 256)]:  # Hq % Hkv != 0
+        a, b = tpa.Plan(), tpa.Plan()
+        ra = lib.attn_plan(*args, ctypes.byref(a))
+        rb = lib.attn_plan_fwd(*args, ctypes.byref(b))
+        assert ra == rb
+        assert bytes(a) == bytes(b)

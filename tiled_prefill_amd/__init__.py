@@ -84,6 +84,8 @@ def load():
     lib.attn_fwd_varlen.restype = i
     lib.attn_plan_fwd.argtypes = [i, i, i, i, i, i, i, i, i, i, i, ll, i, ctypes.POINTER(Plan)]
     lib.attn_plan_fwd.restype = i
+    lib.attn_plan.argtypes = lib.attn_plan_fwd.argtypes
+    lib.attn_plan.restype = i
     lib.attn_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_fwd_dv.restype = i
     lib.attn_plan_fwd_dv.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, ctypes.POINTER(Plan)]

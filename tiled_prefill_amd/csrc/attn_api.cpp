@@ -857,6 +857,13 @@ int attn_plan_fwd(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int
     return ATTN_OK;
 }
 
+int attn_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+              int num_splits, int dtype, int varlen, long long sum_seqlens_k, int num_cus,
+              attn_plan_t* out) {
+    return attn_plan_fwd(B, Hq, Hkv, Sq, Sk, d, causal, window_left, num_splits, dtype, varlen,
+                         sum_seqlens_k, num_cus, out);
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
                int Sk, int d, int causal, int window_left, float scale, int dtype, void* stream) {
