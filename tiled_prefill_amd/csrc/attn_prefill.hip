@@ -147,8 +147,21 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
         row_hi[q] = hi;
         row_ok[q] = ok;
     }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
+    // The 16 lanes of a lane group hold all of the wave's rows, so these
+    // reductions give wave-wide values: [wlo, whi], the keys every row sees
+    // (a tile inside it needs no mask), and [ulo, uhi], the keys some row
+    // sees (a tile outside it is skipped by the whole wave).
+    int ulo = 0x7fffffff, uhi = -1;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        if (row_ok[q] && row_hi[q] >= row_lo[q]) {
+            ulo = imin(ulo, row_lo[q]);
+            uhi = imax(uhi, row_hi[q]);
+        }
+    wlo = __builtin_amdgcn_readfirstlane(row16_imax(wlo));
+    whi = __builtin_amdgcn_readfirstlane(row16_imin(whi));
+    ulo = __builtin_amdgcn_readfirstlane(row16_imin(ulo));
+    uhi = __builtin_amdgcn_readfirstlane(row16_imax(uhi));
     int row_span[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -390,75 +403,79 @@ __global__ void __launch_bounds__(64 * NWV, MW > 32 ? 1 : 8 / NWV) attn_prefill_
         const char* vt = kt + TILEB;
         const int key0 = n * BN;
 
-        // online softmax: exact max until steady, then the bounded fast form; a
-        // steady tile whose row sums show an fp16 overflow runs again, exactly.
-        // (The bf16 form always takes the exact max.)
-        scores(kt, key0);
-        if (VB || !steady || redo) exact_max();
-        exps();
-        if (!VB && steady && !redo) {
-            bool bad = false;
+        // a tile no row of the wave can see is skipped by the wave (the copies and the
+        // barrier still run)
+        if (key0 <= uhi && key0 + BN - 1 >= ulo) {
+            // online softmax: exact max until steady, then the bounded fast form; a
+            // steady tile whose row sums show an fp16 overflow runs again, exactly.
+            // (The bf16 form always takes the exact max.)
+            scores(kt, key0);
+            if (VB || !steady || redo) exact_max();
+            exps();
+            if (!VB && steady && !redo) {
+                bool bad = false;
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) bad |= !(tsum[q][0] <= P_MAX);
-            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-                redo = true;
-                continue;
-            }
-        }
-        redo = false;
-        if (!VB && !steady) {
-            bool open = false;
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) open |= m_run[q] == -INFINITY;
-            steady = __builtin_amdgcn_ballot_w64(open) == 0;
-        }
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) l_run[q] += tsum[q][0];
-
-        // O^T += V^T . P^T (fp16)
-        if (PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int pp = 0; pp < NT / 2; ++pp) {
-            const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
-            const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
-            auto v_frag = [&](const int u) {
-                const int ch = 2 * u + cb;
-                const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + ra * ROWB + 16 * (ch ^ C::swz_v(ra)) + hb));
-                const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
-                return u32x4{a[0], a[1], c[0], c[1]};
-            };
-            if constexpr (!VB) {
-#pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    const u32x4 vf = v_frag(u);
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f16(vf, pf[pp][q], oacc[u][q]);
-                }
-            } else {
-                // bf16 form: P of this key half as hi + lo parts
-                u32x4 ph[NQ], plo[NQ];
-#pragma unroll
-                for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const f32x4& src = sacc[2 * pp + (w >> 1)][q];
-                        const u32x2 hl = split_bf16x2(src[2 * (w & 1)], src[2 * (w & 1) + 1]);
-                        ph[q][w] = hl[0];
-                        plo[q][w] = hl[1];
-                    }
-#pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    const u32x4 vf = v_frag(u);
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) {
-                        oacc[u][q] = mfma_bf16(vf, ph[q], oacc[u][q]);
-                        oacc[u][q] = mfma_bf16(vf, plo[q], oacc[u][q]);
-                    }
+                for (int q = 0; q < NQ; ++q) bad |= !(tsum[q][0] <= P_MAX);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                    redo = true;
+                    continue;
                 }
             }
-        }
+            redo = false;
+            if (!VB && !steady) {
+                bool open = false;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) open |= m_run[q] == -INFINITY;
+                steady = __builtin_amdgcn_ballot_w64(open) == 0;
+            }
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) l_run[q] += tsum[q][0];
 
-        if (PRIO) __builtin_amdgcn_s_setprio(0);
+            // O^T += V^T . P^T (fp16)
+            if (PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int pp = 0; pp < NT / 2; ++pp) {
+                const int ra = 32 * pp + 4 * lg + (li >> 2), rb = ra + 16;
+                const int cb = (li & 3) >> 1, hb = 8 * (li & 1);
+                auto v_frag = [&](const int u) {
+                    const int ch = 2 * u + cb;
+                    const u32x2 a = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + ra * ROWB + 16 * (ch ^ C::swz_v(ra)) + hb));
+                    const u32x2 c = lds_read_tr16(reinterpret_cast<const bf16_t*>(vt + rb * ROWB + 16 * (ch ^ C::swz_v(rb)) + hb));
+                    return u32x4{a[0], a[1], c[0], c[1]};
+                };
+                if constexpr (!VB) {
+#pragma unroll
+                    for (int u = 0; u < DT; ++u) {
+                        const u32x4 vf = v_frag(u);
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q) oacc[u][q] = mfma_f16(vf, pf[pp][q], oacc[u][q]);
+                    }
+                } else {
+                    // bf16 form: P of this key half as hi + lo parts
+                    u32x4 ph[NQ], plo[NQ];
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const f32x4& src = sacc[2 * pp + (w >> 1)][q];
+                            const u32x2 hl = split_bf16x2(src[2 * (w & 1)], src[2 * (w & 1) + 1]);
+                            ph[q][w] = hl[0];
+                            plo[q][w] = hl[1];
+                        }
+#pragma unroll
+                    for (int u = 0; u < DT; ++u) {
+                        const u32x4 vf = v_frag(u);
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q) {
+                            oacc[u][q] = mfma_bf16(vf, ph[q], oacc[u][q]);
+                            oacc[u][q] = mfma_bf16(vf, plo[q], oacc[u][q]);
+                        }
+                    }
+                }
+            }
+
+            if (PRIO) __builtin_amdgcn_s_setprio(0);
+        }
         if (more) {
             // (the bf16 form, which runs only when a V element is beyond fp16's
             // range, loads V here rather than ahead, so its registers are not
