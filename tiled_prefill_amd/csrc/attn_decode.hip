@@ -89,8 +89,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kernel(FwdParams 
         wlo = row_lo;
         whi = row_hi;
     }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
+    // (the 16 lanes of a group hold all of the wave's rows: wave-wide bounds)
+    wlo = __builtin_amdgcn_readfirstlane(row16_imax(wlo));
+    whi = __builtin_amdgcn_readfirstlane(row16_imin(whi));
 
     // Q^T fragments: lane (i, g) holds Q[row i][32c + 8g .. +7]
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(p.q);
@@ -490,8 +491,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kdma_kernel(FwdPa
         wlo = row_lo;
         whi = row_hi;
     }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
+    // (the 16 lanes of a group hold all of the wave's rows: wave-wide bounds)
+    wlo = __builtin_amdgcn_readfirstlane(row16_imax(wlo));
+    whi = __builtin_amdgcn_readfirstlane(row16_imin(whi));
     const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
     if (row_hi < row_lo) row_lo = 0x40000000;
 
@@ -807,8 +809,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) attn_decode_kv_kernel(FwdPara
         wlo = row_lo;
         whi = row_hi;
     }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
+    // (the 16 lanes of a group hold all of the wave's rows: wave-wide bounds)
+    wlo = __builtin_amdgcn_readfirstlane(row16_imax(wlo));
+    whi = __builtin_amdgcn_readfirstlane(row16_imin(whi));
     const int row_span = row_hi < row_lo ? 0 : row_hi - row_lo;
     if (row_hi < row_lo) row_lo = 0x40000000;
 

@@ -167,8 +167,9 @@ __global__ void __launch_bounds__(64 * NW_, NW_ == 4 ? 2 : 1) attn_fwd_f32_dma_k
         row_span[q] = hi < lo ? 0 : hi - lo;
         row_lo[q] = hi < lo ? 0x40000000 : lo;
     }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
+    // (the 16 lanes of a group hold all of the wave's rows: wave-wide bounds)
+    wlo = __builtin_amdgcn_readfirstlane(row16_imax(wlo));
+    whi = __builtin_amdgcn_readfirstlane(row16_imin(whi));
 
     // the query rows have landed (and block n, copied before them) in every wave
     wait_vmcnt<0>();

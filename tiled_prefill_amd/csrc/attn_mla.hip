@@ -119,8 +119,9 @@ __global__ void __launch_bounds__(256 * SV, 1) attn_mla_kernel(FwdParams p) {
         wlo = row_lo;
         whi = row_hi;
     }
-    wlo = row16_imax(wlo);
-    whi = row16_imin(whi);
+    // (the 16 lanes of a group hold all of the wave's rows: wave-wide bounds)
+    wlo = __builtin_amdgcn_readfirstlane(row16_imax(wlo));
+    whi = __builtin_amdgcn_readfirstlane(row16_imin(whi));
 
     // ---- Q^T fragments: lane (i, g) holds Q[row i][32 s + 8 g .. +7]
     u32x4 qf[NSLAB];
